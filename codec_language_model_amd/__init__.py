@@ -1,0 +1,228 @@
+"""codec_language_model_amd - one batched decode step of a codec-language-model
+TTS generator on AMD Instinct MI355X (gfx950).
+
+The computation lives in libclm.so (hand-written HIP kernels behind the C ABI
+in include/clm.h).  This module only marshals torch tensors into that ABI:
+it checks device, dtype, shape and contiguity, passes data pointers and torch's
+current HIP stream, and raises ClmError on a non-zero status.  torch provides
+device memory and streams; no step of the computation runs here.
+
+Calls (names follow the C ABI):
+  kv_cache_append, decode_attention, codebook_head, sample_or_argmax,
+  spec_verify, decode_attention_workspace_size
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import math
+
+from . import _lib
+from ._lib import CLM_BF16, CLM_F32, STATUS
+
+__all__ = [
+    "ClmError", "load", "kv_cache_append", "decode_attention", "decode_attention_workspace_size",
+    "codebook_head", "sample_or_argmax", "spec_verify", "Workspace",
+]
+
+
+class ClmError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        super().__init__(f"{call} returned {status} ({STATUS.get(status, 'unknown')})")
+        self.status = status
+
+
+def load():
+    return _lib.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(call: str, status: int):
+    if status != 0:
+        raise ClmError(call, status)
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return CLM_BF16
+    if t.dtype == torch.float32:
+        return CLM_F32
+    raise TypeError(f"unsupported element type {t.dtype} (bfloat16 or float32)")
+
+
+def _cuda(name, t, dtype=None, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return C.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+class Workspace:
+    """Zero-initialised device workspace for decode_attention, cached per
+    device.  The attention kernel leaves its counters zero after each call, so
+    a workspace can be reused by calls ordered on one stream."""
+
+    _cache = {}
+
+    @classmethod
+    def get(cls, nbytes: int, device):
+        torch = _torch()
+        key = torch.device(device).index or 0
+        buf = cls._cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 256) + 256, dtype=torch.uint8, device=device)
+            cls._cache[key] = buf
+        off = (-buf.data_ptr()) % 256
+        return buf[off:]
+
+
+def kv_cache_append(k_new, v_new, k_cache, v_cache, block_table, len_before, block_size=16):
+    """k_new, v_new [B,T,H_kv,D]; k_cache [nb,H_kv,bs,D]; v_cache [nb,H_kv,D,bs];
+    block_table [B,max_blocks] int32; len_before [B] int32.  In place."""
+    torch = _torch()
+    lib = load()
+    _cuda("k_new", k_new, ndim=4)
+    _cuda("v_new", v_new, k_new.dtype, 4)
+    _cuda("k_cache", k_cache, k_new.dtype, 4)
+    _cuda("v_cache", v_cache, k_new.dtype, 4)
+    _cuda("block_table", block_table, torch.int32, 2)
+    _cuda("len_before", len_before, torch.int32, 1)
+    B, T, H, D = k_new.shape
+    nb = k_cache.shape[0]
+    if tuple(v_new.shape) != (B, T, H, D) or tuple(k_cache.shape) != (nb, H, block_size, D) \
+            or tuple(v_cache.shape) != (nb, H, D, block_size):
+        raise ValueError("kv_cache_append: shape mismatch")
+    if block_table.shape[0] != B or len_before.shape[0] != B:
+        raise ValueError("kv_cache_append: batch mismatch")
+    _check("clm_kv_cache_append", lib.clm_kv_cache_append(
+        _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        block_table.shape[1], _ptr(len_before), B, T, H, D, block_size, nb, _dt(k_new), _stream()))
+
+
+def decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len) -> int:
+    return int(load().clm_decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len))
+
+
+def decode_attention(q, k_cache, v_cache, block_table, kv_len, max_kv_len, scale=None,
+                     out=None, workspace=None, block_size=16):
+    """q [B,Kq,H_q,D]; cache as for kv_cache_append; kv_len [B] int32 (keys
+    seen by the last query, after this step's append).  Returns o [B,Kq,H_q,D]."""
+    torch = _torch()
+    lib = load()
+    _cuda("q", q, ndim=4)
+    _cuda("k_cache", k_cache, q.dtype, 4)
+    _cuda("v_cache", v_cache, q.dtype, 4)
+    _cuda("block_table", block_table, torch.int32, 2)
+    _cuda("kv_len", kv_len, torch.int32, 1)
+    B, Kq, H_q, D = q.shape
+    nb, H_kv = k_cache.shape[0], k_cache.shape[1]
+    if tuple(k_cache.shape) != (nb, H_kv, block_size, D) or tuple(v_cache.shape) != (nb, H_kv, D, block_size):
+        raise ValueError("decode_attention: cache shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _cuda("out", out, q.dtype, 4)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len)
+    if need == 0:
+        raise ClmError("clm_decode_attention_workspace_size", -1)
+    if workspace is None:
+        workspace = Workspace.get(need, q.device)
+    _check("clm_decode_attention", lib.clm_decode_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(kv_len),
+        int(max_kv_len), _ptr(out), B, Kq, H_q, H_kv, D, block_size, nb, C.c_float(scale), _dt(q),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def codebook_head(h, W, head_id=None, out=None):
+    """h [M,d]; W a [G,V,d] tensor or a list of G [V,d] tensors; head_id [M]
+    int32 (required when G > 1).  Returns logits [M,V] float32."""
+    torch = _torch()
+    lib = load()
+    _cuda("h", h, ndim=2)
+    Ws = [W[g] for g in range(W.shape[0])] if isinstance(W, torch.Tensor) and W.dim() == 3 else list(W)
+    for i, w in enumerate(Ws):
+        _cuda(f"W[{i}]", w, h.dtype, 2)
+    G = len(Ws)
+    V, d = Ws[0].shape
+    M = h.shape[0]
+    if h.shape[1] != d or any(tuple(w.shape) != (V, d) for w in Ws):
+        raise ValueError("codebook_head: shape mismatch")
+    if head_id is not None:
+        _cuda("head_id", head_id, torch.int32, 1)
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.float32, device=h.device)
+    else:
+        _cuda("out", out, torch.float32, 2)
+    arr = (C.c_void_p * G)(*[w.data_ptr() for w in Ws])
+    _check("clm_codebook_head", lib.clm_codebook_head(
+        _ptr(h), arr, G, _ptr(head_id), _ptr(out), M, d, V, _dt(h), _stream()))
+    return out
+
+
+def sample_or_argmax(logits, temperature=None, uniforms=None, vocab_valid=None, out=None):
+    """logits [M,V] float32 (rows may be padded: ld = stride); temperature,
+    uniforms [M] float32; vocab_valid [M] int32.  Returns tokens [M] int32."""
+    torch = _torch()
+    lib = load()
+    if logits.dim() != 2 or logits.dtype != torch.float32 or not logits.is_cuda or logits.stride(1) != 1:
+        raise ValueError("logits must be a 2-D float32 GPU tensor with unit column stride")
+    M, V = logits.shape
+    for name, t, dt in (("temperature", temperature, torch.float32), ("uniforms", uniforms, torch.float32),
+                        ("vocab_valid", vocab_valid, torch.int32)):
+        if t is not None:
+            _cuda(name, t, dt, 1)
+    if out is None:
+        out = torch.empty(M, dtype=torch.int32, device=logits.device)
+    _check("clm_sample_or_argmax", lib.clm_sample_or_argmax(
+        _ptr(logits), M, V, logits.stride(0), _ptr(temperature), _ptr(uniforms), _ptr(vocab_valid),
+        _ptr(out), _stream()))
+    return out
+
+
+def spec_verify(target_logits, draft_probs, draft_tokens, u_accept, u_resample, temperature,
+                out_tokens=None, num_emitted=None):
+    """target_logits, draft_probs [B,K,V] float32; draft_tokens [B,K] int32;
+    u_accept [B,K], u_resample [B] float32.  Returns (out_tokens [B,K] int32
+    padded with -1, num_emitted [B] int32)."""
+    torch = _torch()
+    lib = load()
+    _cuda("target_logits", target_logits, torch.float32, 3)
+    _cuda("draft_probs", draft_probs, torch.float32, 3)
+    _cuda("draft_tokens", draft_tokens, torch.int32, 2)
+    _cuda("u_accept", u_accept, torch.float32, 2)
+    _cuda("u_resample", u_resample, torch.float32, 1)
+    B, K, V = target_logits.shape
+    if tuple(draft_probs.shape) != (B, K, V) or tuple(draft_tokens.shape) != (B, K):
+        raise ValueError("spec_verify: shape mismatch")
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K), dtype=torch.int32, device=target_logits.device)
+    if num_emitted is None:
+        num_emitted = torch.empty(B, dtype=torch.int32, device=target_logits.device)
+    _check("clm_spec_verify", lib.clm_spec_verify(
+        _ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resample),
+        C.c_float(temperature), B, K, V, _ptr(out_tokens), _ptr(num_emitted), _stream()))
+    return out_tokens, num_emitted

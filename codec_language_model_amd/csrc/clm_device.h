@@ -1,0 +1,90 @@
+// Device-side helpers shared by the clm kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace clm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Finite stand-in for -inf as an initial running max: exp2(kNegBig - m) is 0
+// for any real score m, and exp2(kNegBig - kNegBig) = 1 multiplies zeros.
+constexpr float kNegBig = -1.0e30f;
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// ---- bf16 <-> f32 -----------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---- DPP cross-lane moves within 16-lane rows --------------------------------
+// Controls: quad_perm [1,0,3,2] = 0xB1 (xor 1), [2,3,0,1] = 0x4E (xor 2),
+// row_half_mirror = 0x141 (lane i <-> 7-i in each half row),
+// row_mirror = 0x140 (lane i <-> 15-i in each row).  For sums and maxima these
+// act as butterflies: after the four steps every lane of a row holds the
+// row-wide result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+template <int LANES>  // 4, 8 or 16 consecutive lanes
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16, "group width");
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  if (LANES >= 8) x += dpp_f<0x141>(x);
+  if (LANES >= 16) x += dpp_f<0x140>(x);
+  return x;
+}
+
+// ---- whole-wave reductions (ds_bpermute based shuffles) ------------------------
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele, fixed order).
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+}  // namespace clm

@@ -1,0 +1,90 @@
+// Internal host-side interface between the C ABI (abi.cpp) and the kernel
+// translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace clm {
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const int32_t* len_before;
+  int max_blocks, B, T_new, H_kv, D, block_size, num_blocks;
+  bool bf16;
+};
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
+
+struct AttnPlan {
+  int split;        // tokens per work item (multiple of 64)
+  int max_splits;   // ceil(max_kv_len / split)
+  int nr;           // query rows per KV head = G * Kq
+  int nr_tmpl;      // compiled row capacity (>= nr)
+  size_t counters_bytes, ml_offset, acc_offset, total_bytes;
+};
+// Deterministic function of the sizes; the workspace query and the call use it.
+bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_len, AttnPlan* p);
+
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* kv_len;
+  void* o;
+  void* workspace;
+  int max_blocks, max_kv_len, B, Kq, H_q, H_kv, D, block_size, num_blocks;
+  float scale;
+  bool bf16;
+};
+hipError_t launch_decode_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+
+struct HeadArgs {
+  const void* h;
+  const void* W[8];
+  int G;
+  const int32_t* head_id;
+  float* logits;
+  int M, d, V;
+  bool bf16;
+};
+hipError_t launch_codebook_head(const HeadArgs& a, hipStream_t s);
+
+struct SampleArgs {
+  const float* logits;
+  int M, V, ld;
+  const float* temperature;
+  const float* uniforms;
+  const int32_t* vocab_valid;
+  int32_t* tokens;
+};
+hipError_t launch_sample_or_argmax(const SampleArgs& a, hipStream_t s);
+
+struct VerifyArgs {
+  const float* target_logits;
+  const float* draft_probs;
+  const int32_t* draft_tokens;
+  const float* u_accept;
+  const float* u_resample;
+  float temperature;
+  int B, K, V;
+  int32_t* out_tokens;
+  int32_t* num_emitted;
+};
+hipError_t launch_spec_verify(const VerifyArgs& a, hipStream_t s);
+
+// Checked mode: validators write the number of bad entries into *bad_count
+// (device int, zeroed by the caller).
+hipError_t launch_check_lengths(const int32_t* len, int n, int lo, int hi, int* bad, hipStream_t s);
+hipError_t launch_check_block_table(const int32_t* bt, const int32_t* len, int B, int max_blocks,
+                                    int len_add, int block_size, int num_blocks, int* bad,
+                                    hipStream_t s);
+hipError_t launch_check_ints(const int32_t* x, int n, int lo, int hi, int* bad, hipStream_t s);
+hipError_t launch_check_uniforms(const float* u, int n, int* bad, hipStream_t s);
+
+}  // namespace clm

@@ -1,0 +1,218 @@
+/*
+ * clm.h - C ABI of libclm.so: one batched autoregressive decode step of a
+ * codec-language-model text-to-speech generator, as hand-written HIP kernels
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The step (TTS Serving, in depth, "Token generation under a frame budget":
+ * after a prefill, the generator runs one decode step per audio frame and each
+ * step reads the KV cache; continuous batching over a paged cache):
+ *
+ *   clm_kv_cache_append    write the step's new K/V rows into the paged cache
+ *   clm_decode_attention   single- or K-query GQA attention over each stream's
+ *                          ragged cache (split-KV flash decoding)
+ *   clm_codebook_head      codebook logit projection, optionally grouped by
+ *                          stage (one weight matrix per stage)
+ *   clm_sample_or_argmax   greedy argmax or temperature sampling per row
+ *   clm_spec_verify        speculative accept/reject of K drafted tokens
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers.  Every array argument is DEVICE memory owned by the caller, except
+ *   where a comment says "host".  The library keeps no per-call state, never
+ *   allocates in these calls and never frees caller memory.
+ * Asynchrony.  A call validates its host-visible arguments, enqueues its
+ *   kernels on `stream` (NULL = the null stream) and returns.  It never
+ *   synchronises and never reads device memory on the host, so a fixed-shape
+ *   step can be captured in a HIP graph.  The one exception is checked mode
+ *   (environment variable CLM_CHECK=1, read once at load): each call then first
+ *   runs a validator over its device-resident indices (lengths, block ids,
+ *   head ids, tokens, uniforms), synchronises, and returns
+ *   CLM_ERR_DEVICE_DATA without launching anything if one is out of range.
+ * Errors.  A call returns CLM_OK or a negative clm_status.  Host-visible
+ *   arguments are checked before any HIP call: a call that returns an error
+ *   other than CLM_ERR_HIP has enqueued nothing.  Device-resident values are
+ *   trusted outside checked mode; kernels still clamp every block-table entry,
+ *   length and head id they read into range, so bad device data gives wrong
+ *   numbers, not out-of-bounds memory accesses.
+ * Element types.  q, K, V, o, h and W share one element type per call
+ *   (clm_dtype).  Logits, probabilities, temperatures and uniforms are always
+ *   float32; tokens, lengths and indices are int32.
+ * Layouts are row-major (C order) with the shapes given; "[a, b]" means b is
+ *   contiguous.
+ */
+#ifndef CLM_H
+#define CLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { CLM_F32 = 0, CLM_BF16 = 1 } clm_dtype;
+
+typedef enum {
+  CLM_OK = 0,
+  CLM_ERR_INVALID_ARG = -1,  /* null pointer, non-positive or inconsistent size   */
+  CLM_ERR_UNSUPPORTED = -2,  /* valid but not implemented (D, dtype, group size)  */
+  CLM_ERR_CAPACITY = -3,     /* append would overflow a stream's block-table row  */
+  CLM_ERR_WORKSPACE = -4,    /* workspace missing or smaller than required        */
+  CLM_ERR_HIP = -5,          /* a HIP runtime call failed (launch, query)         */
+  CLM_ERR_DEVICE_DATA = -6   /* checked mode found an out-of-range device value   */
+} clm_status;
+
+/* Human-readable name of a clm_status value (static string). */
+const char* clm_status_string(int status);
+
+/* ABI version: major*10000 + minor*100 + patch. */
+int clm_version(void);
+
+/* --------------------------------------------------------------------------
+ * KV cache layout (paged).  Optimizing Streaming Text-to-Speech Models for
+ * Sub-50 Millisecond Latency, "Dynamic Token-Level Batching": the cache is a
+ * static pool of fixed-size blocks (16 tokens there) that streams take from a
+ * global free list and give back when done; the free list is the caller's.
+ *
+ *   k_cache [num_blocks, H_kv, block_size, D]   one key row per token slot
+ *   v_cache [num_blocks, H_kv, D, block_size]   values TRANSPOSED inside a block
+ *   block_table [B, max_blocks] int32            stream b's logical block p
+ *                                                (token positions
+ *                                                [p*block_size, (p+1)*block_size))
+ *                                                lives in pool block
+ *                                                block_table[b*max_blocks + p]
+ * Values are stored transposed so that the attention kernels read, for one
+ * head dimension, consecutive tokens as one contiguous run (the operand
+ * layout the matrix cores and the dot-product loop want for P.V).
+ * block_size must be a multiple of 16 in [16, 256].
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Append T_new new rows per stream at positions len_before[b] .. len_before[b]+T_new-1.
+ *   k_new, v_new  [B, T_new, H_kv, D]      rows to write (element type dt)
+ *   k_cache, v_cache                       pool, layout above; updated in place
+ *   block_table   [B, max_blocks]          must map every written position
+ *   len_before    [B] int32                tokens already in each stream
+ * Every other cache slot is left untouched; the result is bit-exact copies.
+ * Errors: INVALID_ARG (null, B/T_new/H_kv/D/max_blocks/num_blocks < 1),
+ *   UNSUPPORTED (D not 64 or 128, block_size not a multiple of 16 in
+ *   [16,256], unknown dt), CAPACITY (T_new > max_blocks*block_size).
+ * Rows whose position falls outside the block table, or whose block id is
+ * outside [0, num_blocks), are skipped (checked mode reports them).
+ */
+int clm_kv_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                        const int32_t* block_table, int max_blocks, const int32_t* len_before,
+                        int B, int T_new, int H_kv, int D, int block_size, int num_blocks,
+                        clm_dtype dt, hipStream_t stream);
+
+/*
+ * Bytes of workspace clm_decode_attention needs for these sizes (0 on a size
+ * error).  max_kv_len bounds kv_len[b] for every stream of the call.
+ */
+size_t clm_decode_attention_workspace_size(int B, int Kq, int H_q, int H_kv, int D,
+                                           int max_kv_len);
+
+/*
+ * Decode attention, one step, all streams.  For stream b, query j in [0,Kq)
+ * and query head h (H_q heads, H_kv KV heads, group G = H_q/H_kv):
+ *     n   = kv_len[b] - (Kq-1-j)          keys visible to query j (a causal
+ *                                         block of Kq queries: the last query
+ *                                         sees every key, including the rows
+ *                                         appended this step)
+ *     kvh = h / G                         consecutive query heads share a KV head
+ *     o[b,j,h,:] = softmax(scale * q[b,j,h,:] . K[0:n,kvh,:]) . V[0:n,kvh,:]
+ * (Speculative Decoding for Acoustic Tokens: one target pass scores the K
+ * drafted positions, i.e. Kq = K queries with causal visibility.)
+ *   q          [B, Kq, H_q, D]        queries (already position-rotated)
+ *   k_cache, v_cache, block_table     paged cache, layout above
+ *   kv_len     [B] int32              visible keys of the last query, >= Kq,
+ *                                     <= max_kv_len
+ *   max_kv_len                        host bound on kv_len (sizes the split plan)
+ *   o          [B, Kq, H_q, D]        output, element type dt
+ *   scale                             score scale (1/sqrt(D) for standard attention)
+ *   workspace  >= clm_decode_attention_workspace_size(...) bytes, 256-byte
+ *              aligned.  Its first B*H_kv*4 bytes are completion counters that
+ *              MUST be zero before the first call that uses this workspace;
+ *              every call leaves them zero again.  Calls that share one
+ *              workspace must be ordered on one stream.
+ * Arithmetic: fp32 dot products, exponentials, online softmax and
+ * accumulation; o rounded to dt once.  Results do not depend on the order in
+ * which workgroups finish (splits are merged in a fixed order).
+ * Errors: INVALID_ARG (null, sizes < 1, H_q % H_kv != 0, max_kv_len < Kq,
+ *   scale not finite), UNSUPPORTED (D not 64/128, G*Kq > 16, B > 4096,
+ *   block_size as for append, unknown dt), WORKSPACE (too small or misaligned).
+ */
+int clm_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, int max_blocks, const int32_t* kv_len,
+                         int max_kv_len, void* o, int B, int Kq, int H_q, int H_kv, int D,
+                         int block_size, int num_blocks, float scale, clm_dtype dt,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Codebook logit projection (TontaubeV1, audio head paragraph: each stage owns
+ * a head that maps the transformer state onto that stage's codebook; codec
+ * paragraph: 16,384 semantic / 4,096 acoustic entries).  No bias.
+ *     logits[r, v] = sum_k h[r, k] * W_{g(r)}[v, k],   g(r) = head_id[r] (or 0)
+ *   h        [M, d]                   head input (element type dt)
+ *   W        host array of G device pointers, each [V, d] (element type dt)
+ *   head_id  [M] int32 in [0, G), or NULL when G == 1
+ *   logits   [M, V] float32           output
+ * Each W_g is streamed from memory once per call for up to 64 rows of its
+ * group (more rows: once per 64-row chunk).  Arithmetic: products of dt
+ * values accumulated in fp32.
+ * Errors: INVALID_ARG (null, sizes < 1, G > 8, head_id NULL with G > 1),
+ *   UNSUPPORTED (d % 64 != 0, M > 65536, unknown dt).
+ */
+int clm_codebook_head(const void* h, const void* const* W, int G, const int32_t* head_id,
+                      float* logits, int M, int d, int V, clm_dtype dt, hipStream_t stream);
+
+/*
+ * One token per row (TontaubeV1 decodes later stages greedily; Section 3.3
+ * masks logits outside the stage's target vocabulary at sampling time).
+ *   logits       [M, ld] float32, first V columns used (ld >= V)
+ *   temperature  [M] float32 >= 0, or NULL (every row greedy)
+ *   uniforms     [M] float32 in [0, 1); required when temperature != NULL
+ *   vocab_valid  [M] int32 in [1, V], or NULL: columns >= vocab_valid[r] are excluded
+ *   tokens       [M] int32 output
+ * T = 0: the lowest index of the largest logit.
+ * T > 0: z = logit / T (fp32 division), e_i = exp(z_i - max z),
+ *        token = min{ i : u*S < e_0 + ... + e_i } with S = sum e  (inverse CDF
+ *        in ascending index order); if rounding leaves no such i, the last
+ *        index with e_i > 0.
+ * Errors: INVALID_ARG (null logits/tokens, M/V < 1, ld < V, uniforms NULL with
+ *   temperature set), UNSUPPORTED (V > 1<<20).
+ */
+int clm_sample_or_argmax(const float* logits, int M, int V, int ld, const float* temperature,
+                         const float* uniforms, const int32_t* vocab_valid, int32_t* tokens,
+                         hipStream_t stream);
+
+/*
+ * Speculative verification (Speculative Decoding for Acoustic Tokens).  For
+ * each stream independently, i = 0..K-1:
+ *     p = softmax(target_logits[b,i,:] / T)   (T = 0: one-hot at the argmax)
+ *     x = draft_tokens[b,i],  q = draft_probs[b,i,x]
+ *     accept iff q > 0 and u_accept[b,i] < p[x] / q   -> emit x, continue
+ *     else emit the inverse-CDF draw (ascending index order) at u_resample[b]
+ *          from max(p - draft_probs[b,i,:], 0) (from p if that is all zero)
+ *          and stop.
+ * No bonus token follows K accepts.
+ *   target_logits [B, K, V] float32,  draft_probs [B, K, V] float32
+ *   draft_tokens  [B, K] int32 in [0, V)
+ *   u_accept      [B, K] float32 in [0,1),  u_resample [B] float32 in [0,1)
+ *   temperature   host float >= 0
+ *   out_tokens    [B, K] int32 output: emitted tokens, then -1 padding
+ *   num_emitted   [B] int32 output in [1, K]
+ * Errors: INVALID_ARG (null, sizes < 1, temperature < 0 or not finite),
+ *   UNSUPPORTED (K > 16, V > 1<<20).
+ */
+int clm_spec_verify(const float* target_logits, const float* draft_probs,
+                    const int32_t* draft_tokens, const float* u_accept, const float* u_resample,
+                    float temperature, int B, int K, int V, int32_t* out_tokens,
+                    int32_t* num_emitted, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CLM_H */

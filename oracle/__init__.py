@@ -21,6 +21,8 @@ with explicit loops over streams, heads and queries:
 * ``sampling``  - greedy argmax and temperature sampling with a supplied
                   uniform; masking of logits outside the target vocabulary
                   (TontaubeV1 Section 3.3).
+* ``step``      - the chained step: append, attention, o in the step's
+                  element type, head, token choice or verification.
 * ``verify``    - speculative accept/reject with residual resampling
                   ("Speculative Decoding for Acoustic Tokens", Optimizing
                   Streaming Text-to-Speech Models ...).
@@ -35,10 +37,11 @@ from .head import codebook_head
 from .kv import gather_logical, kv_cache_append
 from .sampling import argmax_token, inverse_cdf, sample_or_argmax, sample_token
 from .verify import spec_verify, spec_verify_stream, target_probs
+from .step import decode_step, round_to_bf16
 
 __all__ = [
     "attend", "attention_weights", "decode_attention", "codebook_head",
     "gather_logical", "kv_cache_append", "argmax_token", "inverse_cdf",
     "sample_or_argmax", "sample_token", "spec_verify", "spec_verify_stream",
-    "target_probs",
+    "target_probs", "decode_step", "round_to_bf16",
 ]

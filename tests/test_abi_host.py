@@ -1,0 +1,147 @@
+"""Host-side checks of libclm.so that need no GPU: it loads, exports every
+function include/clm.h declares, and rejects bad arguments before any HIP call
+(so these calls never touch a device)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import codec_language_model_amd as clm
+from codec_language_model_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "clm.h")
+
+INVALID, UNSUPPORTED, CAPACITY, WORKSPACE = -1, -2, -3, -4
+P = C.c_void_p(0x100000)          # a non-null, 256-byte aligned stand-in; never dereferenced
+N = C.c_void_p(0)
+S = C.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(clm_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return clm.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks {n}"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_status_strings_and_version(lib):
+    for code, name in _lib.STATUS.items():
+        assert lib.clm_status_string(code).decode() == name
+    assert lib.clm_status_string(42).decode() == "CLM_ERR_UNKNOWN"
+    assert lib.clm_version() >= 100
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = _lib._lib
+    _lib._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="no CPU fallback"):
+            _lib.load(str(tmp_path / "libclm.so"))
+    finally:
+        _lib._lib = saved
+
+
+def append(lib, **kw):
+    a = dict(k_new=P, v_new=P, k_cache=P, v_cache=P, bt=P, max_blocks=8, lb=P, B=2, T=1, H=8, D=128,
+             bs=16, nb=100, dt=1)
+    a.update(kw)
+    return lib.clm_kv_cache_append(a["k_new"], a["v_new"], a["k_cache"], a["v_cache"], a["bt"],
+                                   a["max_blocks"], a["lb"], a["B"], a["T"], a["H"], a["D"], a["bs"],
+                                   a["nb"], a["dt"], S)
+
+
+def test_append_argument_errors(lib):
+    assert append(lib, k_new=N) == INVALID
+    assert append(lib, B=0) == INVALID
+    assert append(lib, T=0) == INVALID
+    assert append(lib, k_cache=C.c_void_p(0x100008)) == INVALID     # not 16-byte aligned
+    assert append(lib, D=96) == UNSUPPORTED
+    assert append(lib, bs=24) == UNSUPPORTED
+    assert append(lib, bs=512) == UNSUPPORTED
+    assert append(lib, dt=7) == UNSUPPORTED
+    assert append(lib, T=129, max_blocks=8, bs=16) == CAPACITY
+
+
+def attn(lib, ws_bytes=None, **kw):
+    a = dict(q=P, k=P, v=P, bt=P, max_blocks=64, kv_len=P, max_kv_len=1000, o=P, B=4, Kq=1, Hq=16, Hk=8,
+             D=128, bs=16, nb=300, scale=0.088, dt=1, ws=P)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.clm_decode_attention_workspace_size(a["B"], a["Kq"], a["Hq"], a["Hk"], a["D"],
+                                                           a["max_kv_len"]) - 1
+    return lib.clm_decode_attention(a["q"], a["k"], a["v"], a["bt"], a["max_blocks"], a["kv_len"],
+                                    a["max_kv_len"], a["o"], a["B"], a["Kq"], a["Hq"], a["Hk"], a["D"],
+                                    a["bs"], a["nb"], C.c_float(a["scale"]), a["dt"], a["ws"], ws_bytes, S)
+
+
+def test_attention_argument_errors(lib):
+    assert attn(lib, q=N) == INVALID
+    assert attn(lib, Hq=12, Hk=8) == INVALID
+    assert attn(lib, max_kv_len=0) == INVALID
+    assert attn(lib, Kq=6, max_kv_len=5) == INVALID
+    assert attn(lib, scale=float("inf")) == INVALID
+    assert attn(lib, D=80) == UNSUPPORTED
+    assert attn(lib, Hq=34, Hk=2) == UNSUPPORTED          # 17 query heads per KV head
+    assert attn(lib, Kq=6, Hq=32, Hk=8) == UNSUPPORTED    # 4 * 6 = 24 rows per KV head
+    assert attn(lib, B=5000) == UNSUPPORTED
+    assert attn(lib) == WORKSPACE                          # one byte short
+    assert attn(lib, ws=N, ws_bytes=1 << 30) == WORKSPACE
+    assert attn(lib, ws=C.c_void_p(0x100010), ws_bytes=1 << 30) == WORKSPACE  # misaligned
+
+
+def test_workspace_size_query(lib):
+    f = lib.clm_decode_attention_workspace_size
+    assert f(0, 1, 16, 8, 128, 100) == 0
+    assert f(4, 1, 16, 8, 96, 100) == 0
+    assert f(4, 6, 16, 8, 128, 5) == 0
+    small = f(16, 1, 16, 8, 128, 1500)
+    big = f(256, 1, 16, 8, 128, 8192)
+    assert 0 < small < big
+    # counters + (m, l) + accumulators for every (stream, KV head, split, row)
+    assert big >= 256 * 8 * 4 + 256 * 8 * 16 * 2 * 130 * 4
+
+
+def test_head_sampler_verify_argument_errors(lib):
+    Ws = (C.c_void_p * 3)(0x100000, 0x200000, 0x300000)
+    assert lib.clm_codebook_head(P, Ws, 3, N, P, 64, 2048, 4096, 1, S) == INVALID   # G > 1 needs head_id
+    assert lib.clm_codebook_head(P, Ws, 9, P, P, 64, 2048, 4096, 1, S) == INVALID
+    assert lib.clm_codebook_head(P, Ws, 1, N, P, 0, 2048, 4096, 1, S) == INVALID
+    assert lib.clm_codebook_head(P, Ws, 1, N, P, 4, 2000, 4096, 1, S) == UNSUPPORTED
+    assert lib.clm_codebook_head(N, Ws, 1, N, P, 4, 2048, 4096, 1, S) == INVALID
+    assert lib.clm_sample_or_argmax(P, 4, 100, 99, N, N, N, P, S) == INVALID       # ld < V
+    assert lib.clm_sample_or_argmax(P, 4, 100, 100, P, N, N, P, S) == INVALID      # T without u
+    assert lib.clm_sample_or_argmax(P, 4, (1 << 20) + 1, (1 << 20) + 1, N, N, N, P, S) == UNSUPPORTED
+    assert lib.clm_spec_verify(P, P, P, P, P, C.c_float(-0.1), 4, 6, 4096, P, P, S) == INVALID
+    assert lib.clm_spec_verify(P, P, P, P, P, C.c_float(float("nan")), 4, 6, 4096, P, P, S) == INVALID
+    assert lib.clm_spec_verify(P, P, P, P, P, C.c_float(0.7), 4, 17, 4096, P, P, S) == UNSUPPORTED
+    assert lib.clm_spec_verify(P, N, P, P, P, C.c_float(0.7), 4, 6, 4096, P, P, S) == INVALID
+
+
+def test_oracle_bf16_rounding_pins():
+    import numpy as np
+    import oracle
+    # ties go to even: 1 + 2^-8 is halfway between 1 and 1 + 2^-7
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -2.5, 0.0, 65504.0],
+                 np.float32)
+    want = np.array([1.0, 1.0, 1 + 2 ** -6, 1 + 2 ** -7, -2.5, 0.0, 65536.0], np.float32)
+    np.testing.assert_array_equal(oracle.round_to_bf16(x), want)
+    import torch
+    y = np.random.default_rng(0).standard_normal(10000).astype(np.float32) * 100
+    np.testing.assert_array_equal(oracle.round_to_bf16(y),
+                                  torch.from_numpy(y).to(torch.bfloat16).to(torch.float32).numpy())

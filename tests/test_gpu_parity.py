@@ -1,0 +1,302 @@
+"""GPU parity: each C-ABI call, and the chained step, against the oracle.
+
+All inputs come from synth (seeded); every expected value comes from oracle/.
+Sizes: the five workloads at full size except the 256-stream one, which runs
+with its first 24 streams here and at full size (sampled streams checked) in
+test_full_size_high_concurrency.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import (bf16_tensor_to_f32, check_argmax, check_close, check_sampled, check_verify,
+                    to_torch)
+
+pytestmark = pytest.mark.gpu
+
+SMALL_B = {1: None, 2: None, 3: None, 4: None, 5: 24}
+_CACHE = {}
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-case] {request.node.nodeid}", file=sys.stderr, flush=True)
+    yield
+
+
+def inputs(cfg_index, B=None):
+    key = (cfg_index, B)
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = synth.make_inputs(cfg_index, B=B)
+    return _CACHE[key]
+
+
+class Dev:
+    """The step's arrays on the GPU."""
+
+    def __init__(self, x, include_new):
+        import torch
+        bf = x.cfg.dtype == "bf16"
+        self.bf = bf
+        kp, vp = x.build_pool(include_new=include_new)
+        self.k_pool_host, self.v_pool_host = kp, vp
+        self.k_cache = to_torch(kp, bf16=bf)
+        self.v_cache = to_torch(vp, bf16=bf)
+        self.block_table = to_torch(x.block_table)
+        self.kv_len = to_torch(x.kv_len)
+        self.len_before = to_torch(x.len_before)
+        self.k_new = to_torch(x.k_new, bf16=bf)
+        self.v_new = to_torch(x.v_new, bf16=bf)
+        self.q = to_torch(x.q, bf16=bf)
+        self.W = to_torch(x.W, bf16=bf)
+        self.head_id = to_torch(x.head_id) if x.cfg.G > 1 else None
+        self.max_kv_len = int(x.kv_len.max())
+        torch.cuda.synchronize()
+
+
+def logical(x):
+    return [x.logical_k(b) for b in range(x.cfg.B)], [x.logical_v(b) for b in range(x.cfg.B)]
+
+
+def as_bits(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_kv_append_bit_exact(clm_gpu, cfg):
+    x = inputs(cfg, SMALL_B[cfg])
+    d = Dev(x, include_new=False)
+    clm_gpu.kv_cache_append(d.k_new, d.v_new, d.k_cache, d.v_cache, d.block_table, d.len_before,
+                            block_size=x.cfg.block_size)
+    rk, rv = oracle.kv_cache_append(d.k_pool_host, d.v_pool_host, x.block_table, x.len_before,
+                                    x.k_new, x.v_new, x.cfg.block_size)
+    gk, gv = as_bits(d.k_cache), as_bits(d.v_cache)
+    dt = np.int16 if d.bf else np.uint32
+    np.testing.assert_array_equal(gk, rk.view(dt))
+    np.testing.assert_array_equal(gv, rv.view(dt))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_decode_attention_parity(clm_gpu, cfg):
+    x = inputs(cfg, SMALL_B[cfg])
+    d = Dev(x, include_new=True)
+    scale = 1.0 / math.sqrt(x.cfg.D)
+    o = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len,
+                                 scale=scale)
+    keys, vals = logical(x)
+    ref = oracle.decode_attention(x.f32(x.q), keys, vals, x.kv_len, scale, x.cfg.H_kv)
+    err = check_close(bf16_tensor_to_f32(o), ref, f"attention c{cfg}")
+    print(f"attention c{cfg}: max abs err {err:.3g}")
+    # run-to-run determinism
+    o2 = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len,
+                                  scale=scale)
+    assert np.array_equal(as_bits(o), as_bits(o2))
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_decode_attention_split_plan_and_batch_order(clm_gpu, cfg):
+    """A larger max_kv_len bound changes the split plan; permuting streams
+    must not change any stream's output bits."""
+    import torch
+    x = inputs(cfg, SMALL_B[cfg])
+    d = Dev(x, include_new=True)
+    scale = 1.0 / math.sqrt(x.cfg.D)
+    o = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len, scale=scale)
+    cap = d.block_table.shape[1] * x.cfg.block_size
+    o_big = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, cap, scale=scale)
+    check_close(bf16_tensor_to_f32(o_big), bf16_tensor_to_f32(o), f"split plan c{cfg}", atol=1e-2, rtol=1e-2)
+    perm = torch.randperm(x.cfg.B, generator=torch.Generator().manual_seed(7)).to(d.q.device)
+    o_p = clm_gpu.decode_attention(d.q[perm].contiguous(), d.k_cache, d.v_cache, d.block_table[perm].contiguous(),
+                                   d.kv_len[perm].contiguous(), d.max_kv_len, scale=scale)
+    assert np.array_equal(as_bits(o_p), as_bits(o[perm].contiguous()))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_codebook_head_isolated(clm_gpu, cfg):
+    x = inputs(cfg, SMALL_B[cfg])
+    bf = x.cfg.dtype == "bf16"
+    h = x.h_iso()
+    W = to_torch(x.W, bf16=bf)
+    hid = to_torch(x.head_id) if x.cfg.G > 1 else None
+    logits = clm_gpu.codebook_head(to_torch(h, bf16=bf), W, hid)
+    ref = oracle.codebook_head(x.f32(h), x.f32(x.W), x.head_id)
+    err = check_close(logits.cpu().numpy(), ref, f"head c{cfg}")
+    tok = clm_gpu.sample_or_argmax(logits)
+    ex = check_argmax(tok.cpu().numpy(), ref.astype(np.float32), f"head argmax c{cfg}")
+    print(f"head c{cfg}: max abs err {err:.3g}, argmax exempt {ex}/{x.cfg.M}")
+
+
+def test_codebook_head_ragged_rows(clm_gpu):
+    """Row counts that are not multiples of 16 or 64, a vocabulary that is not
+    a multiple of 64, and several row chunks per head."""
+    rng = np.random.default_rng(5)
+    for M, V, G in [(1, 4096, 1), (17, 1000, 1), (70, 4096, 3), (130, 4160, 2)]:
+        d = 256
+        h = synth.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32))
+        W = synth.f32_to_bf16_bits((rng.standard_normal((G, V, d)) * 0.05).astype(np.float32))
+        hid = rng.integers(0, G, size=M).astype(np.int32)
+        logits = clm_gpu.codebook_head(to_torch(h, bf16=True), to_torch(W, bf16=True),
+                                       to_torch(hid) if G > 1 else None)
+        ref = oracle.codebook_head(synth.bf16_bits_to_f32(h), synth.bf16_bits_to_f32(W), hid)
+        check_close(logits.cpu().numpy(), ref, f"head M={M} V={V} G={G}")
+
+
+@pytest.mark.parametrize("cfg,scale", [(2, 1.0), (2, 4.0), (5, 1.0), (3, 1.0)])
+def test_sampler_isolated(clm_gpu, cfg, scale):
+    import torch
+    x = inputs(cfg, SMALL_B[cfg])
+    logits = x.logits_iso(scale)
+    u = x.uniforms()
+    lt = to_torch(logits)
+    M = x.cfg.M
+    temp = np.full(M, 0.7, np.float32)
+    tok = clm_gpu.sample_or_argmax(lt, to_torch(temp), to_torch(u)).cpu().numpy()
+    ex = check_sampled(tok, logits, temp, u, f"sample c{cfg} x{scale}")
+    greedy = clm_gpu.sample_or_argmax(lt).cpu().numpy()
+    ex2 = check_argmax(greedy, logits, f"argmax c{cfg}")
+    # per-row mix of greedy and sampled rows, with a vocabulary mask
+    temp_mix = np.where(np.arange(M) % 2 == 0, 0.0, 0.7).astype(np.float32)
+    vv = np.where(np.arange(M) % 3 == 0, x.cfg.V // 2 + 1, x.cfg.V).astype(np.int32)
+    mix = clm_gpu.sample_or_argmax(lt, to_torch(temp_mix), to_torch(u), to_torch(vv)).cpu().numpy()
+    for r in range(M):
+        if temp_mix[r] == 0:
+            check_argmax(mix[r:r + 1], logits[r:r + 1], "mix argmax", vocab_valid=vv[r:r + 1])
+        else:
+            check_sampled(mix[r:r + 1], logits[r:r + 1], temp_mix[r:r + 1], u[r:r + 1], "mix sample",
+                          vocab_valid=vv[r:r + 1])
+    print(f"sampler c{cfg} x{scale}: exempt sampled {ex}/{M}, argmax {ex2}/{M}")
+    del torch
+
+
+def test_sampler_closed_forms(clm_gpu):
+    """Equal logits give floor(u*V); a one-hot row gives its hot index; u = 0
+    gives the first positive-probability token; padded rows (ld > V)."""
+    V = 1000
+    u = np.array([(k + 0.5) / 10 for k in range(10)], np.float32)
+    logits = np.zeros((10, V), np.float32)
+    tok = clm_gpu.sample_or_argmax(to_torch(logits), to_torch(np.full(10, 0.7, np.float32)), to_torch(u)).cpu().numpy()
+    assert tok.tolist() == [int(ui * V) for ui in u]
+    hot = np.full((4, 1024 + 8), -3.0, np.float32)
+    for r in range(4):
+        hot[r, 100 * r + 7] = 60.0
+    lt = to_torch(hot)[:, :1024]   # padded rows
+    t = clm_gpu.sample_or_argmax(lt, to_torch(np.full(4, 1.0, np.float32)),
+                                 to_torch(np.array([0.0, 0.3, 0.7, 0.999], np.float32))).cpu().numpy()
+    assert t.tolist() == [7, 107, 207, 307]
+    y = np.full((1, 4096), -1e30, np.float32)
+    y[0, 3000:] = 0.0
+    t0 = clm_gpu.sample_or_argmax(to_torch(y), to_torch(np.ones(1, np.float32)), to_torch(np.zeros(1, np.float32)))
+    assert int(t0.cpu()[0]) == 3000
+
+
+def _spec_inputs_torch(s):
+    return (to_torch(s["draft_probs"]), to_torch(s["draft_tokens"]), to_torch(s["u_accept"]),
+            to_torch(s["u_resample"]))
+
+
+@pytest.mark.parametrize("T", [0.7, 0.0])
+def test_spec_verify_isolated(clm_gpu, T):
+    x = inputs(4)
+    s = x.spec_inputs()
+    tl = s["target_logits_iso"]
+    dp, dtok, ua, ur = _spec_inputs_torch(s)
+    toks, num = clm_gpu.spec_verify(to_torch(tl), dp, dtok, ua, ur, T)
+    ex = check_verify(toks.cpu().numpy(), num.cpu().numpy(), tl, s["draft_probs"], s["draft_tokens"],
+                      s["u_accept"], s["u_resample"], T, f"verify T={T}")
+    print(f"verify T={T}: exempt {ex}/{x.cfg.B}, mean emitted {num.float().mean().item():.3f}")
+
+
+def test_spec_verify_accepts_when_draft_equals_target(clm_gpu):
+    x = inputs(4)
+    s = x.spec_inputs()
+    tl = s["target_logits_iso"]
+    T = 0.7
+    q = np.stack([[oracle.target_probs(tl[b, i], T) for i in range(x.cfg.Kq)] for b in range(x.cfg.B)])
+    ua = (s["u_accept"] * np.float32(0.999)).astype(np.float32)
+    toks, num = clm_gpu.spec_verify(to_torch(tl), to_torch(q.astype(np.float32)), to_torch(s["draft_tokens"]),
+                                    to_torch(ua), to_torch(s["u_resample"]), T)
+    # GPU and oracle normalisers may differ in the last bit, so p[x]/q can be
+    # just under 1; u < 0.999 keeps every decision an accept.
+    assert (num.cpu().numpy() == x.cfg.Kq).all()
+    assert np.array_equal(toks.cpu().numpy(), s["draft_tokens"])
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_chained_step(clm_gpu, cfg):
+    """append -> attention -> head -> sample/argmax/verify on the GPU, against
+    the oracle's chained step."""
+    import torch
+    x = inputs(cfg, SMALL_B[cfg])
+    c = x.cfg
+    d = Dev(x, include_new=False)
+    scale = 1.0 / math.sqrt(c.D)
+    clm_gpu.kv_cache_append(d.k_new, d.v_new, d.k_cache, d.v_cache, d.block_table, d.len_before,
+                            block_size=c.block_size)
+    o = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len, scale=scale)
+    h = o.view(c.M, c.d_model)
+    logits = clm_gpu.codebook_head(h, d.W, d.head_id)
+    keys, vals = logical(x)
+    spec = x.spec_inputs() if c.mode == "spec" else None
+    temp = np.full(c.M, c.temperature, np.float32) if c.mode == "sample" else None
+    u = x.uniforms() if c.mode == "sample" else None
+    ref = oracle.decode_step(x.f32(x.q), keys, vals, x.kv_len, scale, c.H_kv, x.f32(x.W), x.head_id,
+                             c.dtype == "bf16", mode=c.mode,
+                             temperature=(c.temperature if c.mode == "spec" else temp), uniforms=u, spec=spec)
+    check_close(bf16_tensor_to_f32(o), ref["o"], f"chained attention c{cfg}")
+    check_close(logits.cpu().numpy(), ref["logits"], f"chained logits c{cfg}")
+    if c.mode == "spec":
+        dp, dtok, ua, ur = _spec_inputs_torch(spec)
+        toks, num = clm_gpu.spec_verify(logits.view(c.B, c.Kq, c.V), dp, dtok, ua, ur, c.temperature)
+        ex = check_verify(toks.cpu().numpy(), num.cpu().numpy(), ref["logits"].reshape(c.B, c.Kq, c.V),
+                          spec["draft_probs"], spec["draft_tokens"], spec["u_accept"], spec["u_resample"],
+                          c.temperature, f"chained verify c{cfg}")
+    elif c.mode == "sample":
+        tok = clm_gpu.sample_or_argmax(logits, to_torch(temp), to_torch(u)).cpu().numpy()
+        ex = check_sampled(tok, ref["logits"], temp, u, f"chained sample c{cfg}")
+    else:
+        tok = clm_gpu.sample_or_argmax(logits).cpu().numpy()
+        ex = check_argmax(tok, ref["logits"], f"chained argmax c{cfg}")
+    print(f"chained c{cfg}: exempt {ex}")
+    del torch
+
+
+def test_full_size_high_concurrency(clm_gpu):
+    """256 streams, log-uniform KV lengths 64..8192, head 2048->16384, greedy:
+    the launch configuration the benchmark times; sampled streams (shortest,
+    longest and a spread between) checked against the oracle."""
+    x = synth.make_inputs(5)
+    c = x.cfg
+    d = Dev(x, include_new=False)
+    scale = 1.0 / math.sqrt(c.D)
+    clm_gpu.kv_cache_append(d.k_new, d.v_new, d.k_cache, d.v_cache, d.block_table, d.len_before)
+    o = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len, scale=scale)
+    logits = clm_gpu.codebook_head(o.view(c.M, c.d_model), d.W)
+    tok = clm_gpu.sample_or_argmax(logits).cpu().numpy()
+    order = np.argsort(x.kv_len)
+    streams = sorted(set([int(order[0]), int(order[-1])] + [int(order[i]) for i in np.linspace(0, c.B - 1, 10).astype(int)]))
+    keys = {b: x.logical_k(b) for b in streams}
+    vals = {b: x.logical_v(b) for b in streams}
+    ref = oracle.decode_step(x.f32(x.q), keys, vals, x.kv_len, scale, c.H_kv, x.f32(x.W), None, True,
+                             streams=streams)
+    o_np = bf16_tensor_to_f32(o)
+    lg = logits.cpu().numpy()
+    for b in streams:
+        check_close(o_np[b], ref["o"][b], f"full-size attention stream {b} (kv_len {x.kv_len[b]})")
+        check_close(lg[b], ref["logits"][b], f"full-size logits stream {b}")
+        check_argmax(tok[b:b + 1], ref["logits"][b:b + 1], f"full-size argmax stream {b}")
+    # append at full size: each sampled stream's new row sits where the
+    # block table puts position len_before[b]
+    kc, vc = d.k_cache, d.v_cache
+    for b in streams:
+        pos = int(x.len_before[b])
+        blk = int(x.block_table[b, pos // c.block_size])
+        slot = pos % c.block_size
+        np.testing.assert_array_equal(as_bits(kc[blk, :, slot, :].contiguous()), x.k_new[b, 0].view(np.int16))
+        np.testing.assert_array_equal(as_bits(vc[blk, :, :, slot].contiguous()), x.v_new[b, 0].view(np.int16))
