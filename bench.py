@@ -1,0 +1,292 @@
+"""Benchmark: one batched codec-LM decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
+                    [--no-cpu-baseline] [--copy-calibration]
+
+A step is the whole hot path over one batch: kv_cache_append ->
+decode_attention -> codebook_head -> sample_or_argmax (spec_verify for the
+speculative workload), all through the C ABI, inputs resident in HBM.  The
+default workload is 256 streams with log-uniform KV lengths in [64, 8192],
+16 query / 8 KV heads of width 128, bf16 cache, a 2048 -> 16384 head and
+greedy decoding: the one that fills the GPU and exposes the attention
+roofline.
+
+Prints ONE JSON line: value = stream-steps/s (streams x query tokens per
+second), the attention kernel's roofline (algorithmic K/V/q/o bytes per
+launch over its HIP-event-timed duration, against 8 TB/s), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "codec decode steps/s (streams×tokens) and % HBM roofline of KV attention"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_c5_traffic.txt")
+ATTN_SRC = os.path.join(ROOT, "codec_language_model_amd", "csrc", "attention.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-streams", type=int, default=0,
+                    help="streams in the oracle's timed sample (0 = the whole batch)")
+    ap.add_argument("--cpu-reps", type=int, default=3, help="oracle repetitions timed")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
+    return ap.parse_args()
+
+
+def attention_bytes(cfg, kv_len):
+    """Algorithmic bytes of one decode_attention launch: every visible K and V
+    row once (2 * H_kv * D * elem bytes per token), q read once, o written once."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    kv = int(kv_len.astype("int64").sum()) * 2 * cfg.H_kv * cfg.D * e
+    qo = 2 * cfg.B * cfg.Kq * cfg.H_q * cfg.D * e
+    return kv + qo
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per attention launch measured by rocprofv3 PMC counters, if
+    the record was taken on the current attention source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("attention_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, n_streams, reps=1):
+    """The oracle, as it stands, on n_streams streams spread over the length
+    distribution (all of them when n_streams is 0 or >= B): attention, head
+    and token choice per stream, repeated reps times."""
+    import numpy as np
+
+    import oracle
+    c = x.cfg
+    if n_streams <= 0 or n_streams > c.B:
+        n_streams = c.B
+    order = np.argsort(x.kv_len)
+    streams = sorted(set(int(order[i]) for i in np.linspace(0, c.B - 1, n_streams).astype(int)))
+    keys = {b: x.logical_k(b) for b in streams}
+    vals = {b: x.logical_v(b) for b in streams}
+    q = x.f32(x.q)
+    W = x.f32(x.W)
+    scale = 1.0 / math.sqrt(c.D)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.decode_step(q, keys, vals, x.kv_len, scale, c.H_kv, W, x.head_id if c.G > 1 else None,
+                           c.dtype == "bf16", streams=streams)
+    dt = time.perf_counter() - t0
+    threads = os.cpu_count()
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas = [i["num_threads"] for i in info if i.get("user_api") == "blas"]
+        if blas:
+            threads = max(blas)
+    except Exception:
+        pass
+    rows = len(streams) * c.Kq * reps
+    what = "the whole batch" if len(streams) == c.B else \
+        f"{len(streams)} of {c.B} streams (spread over the KV-length order)"
+    return {"value": round(rows / dt, 3), "unit": "stream-steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}, {int(sum(x.kv_len[b] for b in streams))} cached tokens, full head, "
+                      f"{reps} repetitions: {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: the decode step shards by stream with no exchange, "
+              f"and multi-GPU runs are not part of this build (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import codec_language_model_amd as clm
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    clm.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = synth.get_config(args.workload)
+    t_gen = time.perf_counter()
+    x = synth.make_inputs(cfg)
+    c = x.cfg
+    bf = c.dtype == "bf16"
+    kp, vp = x.build_pool(include_new=False)
+    log(f"[bench] {c.workload}: inputs drawn in {time.perf_counter() - t_gen:.1f} s "
+        f"(sum kv_len {int(x.kv_len.sum())}, pool {kp.nbytes * 2 / 2**30:.2f} GiB)")
+
+    def dev_t(a, bf16):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
+        return t.to(dev)
+
+    k_cache, v_cache = dev_t(kp, bf), dev_t(vp, bf)
+    del kp, vp
+    bt, kv_len, len_before = dev_t(x.block_table, False), dev_t(x.kv_len, False), dev_t(x.len_before, False)
+    k_new, v_new, q = dev_t(x.k_new, bf), dev_t(x.v_new, bf), dev_t(x.q, bf)
+    W = dev_t(x.W, bf)
+    head_id = dev_t(x.head_id, False) if c.G > 1 else None
+    max_kv = int(x.kv_len.max())
+    scale = 1.0 / math.sqrt(c.D)
+    o = torch.empty_like(q)
+    logits = torch.empty((c.M, c.V), dtype=torch.float32, device=dev)
+    tokens = torch.empty(c.M, dtype=torch.int32, device=dev)
+    ws = clm.Workspace.get(clm.decode_attention_workspace_size(c.B, c.Kq, c.H_q, c.H_kv, c.D, max_kv), dev)
+    temp = uni = None
+    if c.mode == "sample":
+        temp = torch.full((c.M,), c.temperature, dtype=torch.float32, device=dev)
+        uni = dev_t(x.uniforms(), False)
+    spec = None
+    if c.mode == "spec":
+        s = x.spec_inputs()
+        spec = tuple(dev_t(s[k], False) for k in ("draft_probs", "draft_tokens", "u_accept", "u_resample"))
+        out_tok = torch.empty((c.B, c.Kq), dtype=torch.int32, device=dev)
+        num_em = torch.empty(c.B, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    def step(timed):
+        if timed:
+            ev[0].record()
+        clm.kv_cache_append(k_new, v_new, k_cache, v_cache, bt, len_before, block_size=c.block_size)
+        if timed:
+            ev[1].record()
+        clm.decode_attention(q, k_cache, v_cache, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
+        if timed:
+            ev[2].record()
+        clm.codebook_head(o.view(c.M, c.d_model), W, head_id, out=logits)
+        if timed:
+            ev[3].record()
+        if spec is not None:
+            clm.spec_verify(logits.view(c.B, c.Kq, c.V), *spec, c.temperature, out_tokens=out_tok,
+                            num_emitted=num_em)
+        else:
+            clm.sample_or_argmax(logits, temp, uni, out=tokens)
+        if timed:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    # whole-step throughput: K steps, no per-call events inside
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-call durations: the same K steps again, with events between calls
+    per = np.zeros(4)
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        per += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    per_us = per / args.steps * 1e3
+
+    ms_per_step = wall / args.steps * 1e3
+    value = c.B * c.Kq / (wall / args.steps)
+    attn_s = per_us[1] * 1e-6
+    attn_bytes = attention_bytes(c, x.kv_len)
+    achieved = attn_bytes / attn_s / 1e9
+    traffic = traffic_for_current_kernel()
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; per call (us): append {per_us[0]:.1f}, "
+        f"attention {per_us[1]:.1f}, head {per_us[2]:.1f}, token {per_us[3]:.1f}; attention "
+        f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 5 x 1 GiB device-to-device copies done")
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        cpu = cpu_baseline(x, args.cpu_streams, args.cpu_reps)
+        log(f"[bench] cpu oracle: {cpu['value']:.2f} {cpu['unit']} ({cpu['sample']})")
+
+    head_flops = 2.0 * c.M * c.d_model * c.V
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "stream-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic (seeded N(0,1) q/K/V, N(0,0.02) head weights; no dataset or checkpoint)",
+        "config": {
+            "workload": c.workload,
+            "streams": c.B, "queries_per_stream": c.Kq, "q_heads": c.H_q, "kv_heads": c.H_kv,
+            "head_dim": c.D, "kv_len": "x".join(str(a) for a in c.kv_len_dist), "block_size": c.block_size,
+            "d_model": c.d_model, "codebook": c.V, "heads": c.G, "decoding": c.mode,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode_attention",
+            "algorithmic_bytes_per_launch": attn_bytes,
+        },
+        "per_call_us": {"kv_cache_append": round(per_us[0], 2), "decode_attention": round(per_us[1], 2),
+                        "codebook_head": round(per_us[2], 2),
+                        ("spec_verify" if spec is not None else "sample_or_argmax"): round(per_us[3], 2)},
+        "codebook_head_tflops": round(head_flops / (per_us[2] * 1e-6) / 1e12, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -34,6 +34,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxB = 4096;
+constexpr long kMaxCounters = 65536;  // completion counters: one per (stream, KV head)
 
 template <int BYTES> struct VecT;
 template <> struct VecT<4> { using type = uint32_t; };
@@ -435,7 +436,11 @@ bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_l
   p->split = (int)split;
   p->max_splits = (int)((max_kv_len + split - 1) / split);
   const size_t slots = (size_t)B * H_kv * p->max_splits * p->nr_tmpl;
-  p->counters_bytes = align256((size_t)B * H_kv * sizeof(int));
+  // The counter area has one fixed size, whatever B and H_kv are, so a
+  // workspace reused by calls of other shapes never finds partial results
+  // where it expects zeroed counters.
+  if ((long)B * H_kv > kMaxCounters) return false;
+  p->counters_bytes = (size_t)kMaxCounters * sizeof(int);
   p->ml_offset = p->counters_bytes;
   p->acc_offset = p->ml_offset + align256(slots * 2 * sizeof(float));
   p->total_bytes = p->acc_offset + align256(slots * (size_t)D * sizeof(float));

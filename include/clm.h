@@ -110,6 +110,8 @@ int clm_kv_cache_append(const void* k_new, const void* v_new, void* k_cache, voi
  * Bytes of workspace clm_decode_attention needs for these sizes (0 on a size
  * error).  max_kv_len bounds kv_len[b] for every stream of the call.
  */
+#define CLM_ATTN_COUNTER_BYTES (65536 * 4)
+
 size_t clm_decode_attention_workspace_size(int B, int Kq, int H_q, int H_kv, int D,
                                            int max_kv_len);
 
@@ -132,16 +134,19 @@ size_t clm_decode_attention_workspace_size(int B, int Kq, int H_q, int H_kv, int
  *   o          [B, Kq, H_q, D]        output, element type dt
  *   scale                             score scale (1/sqrt(D) for standard attention)
  *   workspace  >= clm_decode_attention_workspace_size(...) bytes, 256-byte
- *              aligned.  Its first B*H_kv*4 bytes are completion counters that
- *              MUST be zero before the first call that uses this workspace;
- *              every call leaves them zero again.  Calls that share one
- *              workspace must be ordered on one stream.
+ *              aligned.  Its first CLM_ATTN_COUNTER_BYTES bytes hold completion
+ *              counters; they MUST be zero before the first call that uses
+ *              this workspace, and every call leaves them zero again and
+ *              writes nothing else there, so one workspace can serve calls of
+ *              any shape.  Calls that share a workspace must be ordered on
+ *              one stream.
  * Arithmetic: fp32 dot products, exponentials, online softmax and
  * accumulation; o rounded to dt once.  Results do not depend on the order in
  * which workgroups finish (splits are merged in a fixed order).
  * Errors: INVALID_ARG (null, sizes < 1, H_q % H_kv != 0, max_kv_len < Kq,
  *   scale not finite), UNSUPPORTED (D not 64/128, G*Kq > 16, B > 4096,
- *   block_size as for append, unknown dt), WORKSPACE (too small or misaligned).
+ *   B*H_kv > 65536, block_size as for append, unknown dt), WORKSPACE (too
+ *   small or misaligned).
  */
 int clm_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_table, int max_blocks, const int32_t* kv_len,
@@ -161,8 +166,9 @@ int clm_decode_attention(const void* q, const void* k_cache, const void* v_cache
  * Each W_g is streamed from memory once per call for up to 64 rows of its
  * group (more rows: once per 64-row chunk).  Arithmetic: products of dt
  * values accumulated in fp32.
- * Errors: INVALID_ARG (null, sizes < 1, G > 8, head_id NULL with G > 1),
- *   UNSUPPORTED (d % 64 != 0, M > 65536, unknown dt).
+ * Errors: INVALID_ARG (null, sizes < 1, G > 8, head_id NULL with G > 1,
+ *   h or a W not 16-byte aligned), UNSUPPORTED (bf16 with d % 128 != 0, f32
+ *   with d % 4 != 0, M > 65536, unknown dt).
  */
 int clm_codebook_head(const void* h, const void* const* W, int G, const int32_t* head_id,
                       float* logits, int M, int d, int V, clm_dtype dt, hipStream_t stream);

@@ -102,20 +102,43 @@ def test_decode_attention_parity(clm_gpu, cfg):
 
 @pytest.mark.parametrize("cfg", [2, 5])
 def test_decode_attention_split_plan_and_batch_order(clm_gpu, cfg):
-    """A larger max_kv_len bound changes the split plan; permuting streams
-    must not change any stream's output bits."""
+    """A looser max_kv_len bound changes the split plan (longer splits, more
+    of them per stream); permuting streams must not change any stream's
+    output bits."""
     import torch
     x = inputs(cfg, SMALL_B[cfg])
     d = Dev(x, include_new=True)
     scale = 1.0 / math.sqrt(x.cfg.D)
     o = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len, scale=scale)
-    cap = d.block_table.shape[1] * x.cfg.block_size
-    o_big = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, cap, scale=scale)
+    loose = 8 * d.max_kv_len
+    assert clm_gpu.decode_attention_workspace_size(x.cfg.B, 1, 16, 8, 128, loose) != \
+        clm_gpu.decode_attention_workspace_size(x.cfg.B, 1, 16, 8, 128, d.max_kv_len)
+    o_big = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, loose, scale=scale)
     check_close(bf16_tensor_to_f32(o_big), bf16_tensor_to_f32(o), f"split plan c{cfg}", atol=1e-2, rtol=1e-2)
     perm = torch.randperm(x.cfg.B, generator=torch.Generator().manual_seed(7)).to(d.q.device)
     o_p = clm_gpu.decode_attention(d.q[perm].contiguous(), d.k_cache, d.v_cache, d.block_table[perm].contiguous(),
                                    d.kv_len[perm].contiguous(), d.max_kv_len, scale=scale)
     assert np.array_equal(as_bits(o_p), as_bits(o[perm].contiguous()))
+
+
+def test_decode_attention_workspace_reuse_across_shapes(clm_gpu):
+    """One workspace serves calls of different batch sizes in turn: each call
+    must find its completion counters zero (regression: the counter area used
+    to grow with B * H_kv and overlap an earlier call's partial results)."""
+    import torch
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    outs = {}
+    for cfg, B in [(5, 24), (2, None), (5, 24), (3, None), (5, 24)]:
+        x = inputs(cfg, B)
+        d = Dev(x, include_new=True)
+        o = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len,
+                                     workspace=ws)
+        if cfg == 5:
+            if 5 in outs:
+                assert np.array_equal(as_bits(o), outs[5])
+            else:
+                outs[5] = as_bits(o)
+    assert int(ws[:65536 * 4].count_nonzero()) == 0
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
