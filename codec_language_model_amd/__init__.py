@@ -79,9 +79,9 @@ def _stream():
 
 
 class Workspace:
-    """Zero-initialised device workspace for decode_attention, cached per
-    device.  The attention kernel leaves its counters zero after each call, so
-    a workspace can be reused by calls ordered on one stream."""
+    """Device scratch for decode_attention's per-split partial results, cached
+    per device and grown on demand; calls that share it must be ordered on one
+    stream (torch's current stream is used for every call)."""
 
     _cache = {}
 
@@ -91,7 +91,7 @@ class Workspace:
         key = torch.device(device).index or 0
         buf = cls._cache.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(max(nbytes, 256) + 256, dtype=torch.uint8, device=device)
+            buf = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device=device)
             cls._cache[key] = buf
         off = (-buf.data_ptr()) % 256
         return buf[off:]

@@ -9,22 +9,28 @@
 //
 // Work decomposition.  A work item is (stream b, KV head h, split s): the
 // tokens [s*split, min((s+1)*split, kv_len[b])) of one KV head.  All G*Kq
-// query rows that share the KV head are served by the one pass over its
-// K/V bytes, so every K/V byte is read from HBM once per step.  The grid is
-// persistent: every workgroup derives the item list from kv_len (a prefix sum
-// of per-stream split counts, in LDS) and strides through it, so no workgroup
-// is launched for splits past a stream's end.
+// query rows that share the KV head are served by one pass over its K/V
+// bytes, so every K/V byte is read from HBM once per step.  Each wave owns
+// whole items: the grid is persistent, every workgroup derives the item list
+// from kv_len (a prefix sum of per-stream split counts, in LDS, built once),
+// and its waves stride through the list independently - no barrier, no LDS
+// and no cross-workgroup traffic in the main loop.
 //
-// Inside an item the 4 waves take 16-token tiles round-robin.  In a tile a
-// wave reads the keys as 16-byte loads, LPR lanes per key row (one 256-byte
-// row per 16 lanes for bf16, D = 128), so each load instruction covers whole
-// rows contiguously; the LPR partial dot products are summed with DPP inside
-// the 16-lane row.  Values are stored transposed inside a block ([D][bs]), so
-// a lane reads, for each of its head dimensions, the run of keys its group
-// scored - again contiguous across the wave.  Each key group keeps its own
-// online-softmax state (running max m, sum l, accumulator) in registers; the
-// groups of a wave are merged with shuffles, the waves through LDS, and the
-// splits of a (b, h) by the last workgroup to finish it, in split order.
+// Inside an item a wave walks 16-token tiles.  The block ids of the item's
+// pages are fetched once, one per lane, and picked out with readlane.  Keys
+// are read as 16-byte loads, LPR lanes per key row (16 lanes per 256-byte row
+// for bf16, D = 128), so one load instruction covers 4 whole rows; the LPR
+// partial dot products are summed with DPP inside the 16-lane row.  Values
+// are stored transposed inside a block ([D][bs]), so for each of its head
+// dimensions a lane reads the run of keys its group scored, contiguous
+// across the wave.  The next tile's loads are always in flight while the
+// current tile is computed (past the last tile the current one is re-read,
+// which hits in cache), so the wait counts stay exact.  Each 16-lane key
+// group keeps its own online-softmax state (running max m, sum l,
+// accumulator) in registers; the groups merge with shuffles at the end of an
+// item.  A stream that fits in one split is written directly; otherwise the
+// split's (m, l, acc) goes to the workspace and a second small kernel merges
+// the splits of each (stream, KV head) in split order (deterministic).
 #include "clm_device.h"
 #include "clm_launch.h"
 
@@ -34,7 +40,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxB = 4096;
-constexpr long kMaxCounters = 65536;  // completion counters: one per (stream, KV head)
 
 template <int BYTES> struct VecT;
 template <> struct VecT<4> { using type = uint32_t; };
@@ -93,38 +98,34 @@ struct KParams {
   const int32_t* block_table;
   const int32_t* kv_len;
   void* o;
-  int* counters;
-  float* part_ml;   // [B][H_kv][max_splits][NR][2]
+  float* part_ml;   // [B][H_kv][max_splits][NR][2]   (m in log2 units, l)
   float* part_acc;  // [B][H_kv][max_splits][NR][D]
   int max_blocks, cap, B, Kq, H_q, H_kv, G, nr, bs, num_blocks, split, max_splits;
   float scale_log2;
 };
 
-template <typename T, int D>
 __device__ __forceinline__ int split_count(int len, const KParams& P) {
   int n = clampi(len, 1, P.cap);
   int s = (n + P.split - 1) / P.split;
   return clampi(s, 1, P.max_splits);
 }
 
-template <typename T, int D, int NR>
-__global__ __launch_bounds__(kThreads) void decode_attention_kernel(KParams P) {
+template <typename T, int D, int NR, int BS>
+__global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
   using G_ = Geo<T, D>;
   constexpr int LPR = G_::LPR, CPL = G_::CPL, KPG = G_::KPG, DPL = G_::DPL, VE = G_::VE;
+  constexpr int NG = G_::NG;
   using VT = typename G_::VT;
 
   __shared__ int s_prefix[kMaxB + 1];
   __shared__ int s_wsum[kWaves];
-  __shared__ float s_m[kWaves][NR];
-  __shared__ float s_l[kWaves][NR];
-  __shared__ float s_acc[kWaves][NR][D];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
   const int g = lane / LPR;
   const int c = lane % LPR;
+  const int bs = BS ? BS : P.bs;
 
   const T* __restrict__ qp = static_cast<const T*>(P.q);
   const T* __restrict__ kc = static_cast<const T*>(P.kc);
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(KParams P) {
     int local = 0;
     for (int k = 0; k < per; ++k) {
       int b = b0 + k;
-      if (b < P.B) local += split_count<T, D>(P.kv_len[b], P);
+      if (b < P.B) local += split_count(P.kv_len[b], P);
     }
     int incl = wave_incl_scan_i(local, lane);
     if (lane == 63) s_wsum[w] = incl;
@@ -150,15 +151,16 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(KParams P) {
       int b = b0 + k;
       if (b < P.B) {
         s_prefix[b] = run;
-        run += split_count<T, D>(P.kv_len[b], P);
+        run += split_count(P.kv_len[b], P);
       }
     }
     if (tid == 0) s_prefix[P.B] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
     __syncthreads();
   }
   const int total_items = s_prefix[P.B] * P.H_kv;
+  const int nwaves = gridDim.x * kWaves;
 
-  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+  for (int item = blockIdx.x * kWaves + w; item < total_items; item += nwaves) {
     const int u = item / P.H_kv;
     const int h = item - u * P.H_kv;
     int lo = 0, hi = P.B - 1;  // largest b with s_prefix[b] <= u
@@ -168,13 +170,21 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(KParams P) {
     }
     const int b = uniform(lo);
     const int s = uniform(u - s_prefix[b]);
-    const int ns = s_prefix[b + 1] - s_prefix[b];
+    const int ns = uniform(s_prefix[b + 1] - s_prefix[b]);
 
-    const int n_total = clampi(P.kv_len[b], 1, P.cap);
+    const int n_total = uniform(clampi(P.kv_len[b], 1, P.cap));
     const int n_min = n_total - (P.Kq - 1);       // keys seen by the first query
     const int t0 = s * P.split;
     const int t1 = min(t0 + P.split, n_total);
     const int n_tiles = (t1 - t0 + 15) >> 4;
+    const int p0 = t0 / bs;
+
+    // block ids of the item's pages, one per lane (an item spans <= 64 pages)
+    int my_blk = 0;
+    {
+      const int n_pages = (t1 - 1) / bs - p0 + 1;
+      if (lane < n_pages) my_blk = clampi(P.block_table[(size_t)b * P.max_blocks + p0 + lane], 0, P.num_blocks - 1);
+    }
 
     // ---- this lane's slice of the query rows --------------------------------
     uint32_t qw[NR][4 * CPL];
@@ -206,65 +216,40 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(KParams P) {
       for (int jj = 0; jj < DPL; ++jj) acc[r][jj] = 0.f;
     }
 
-    const int32_t* bt_row = P.block_table + (size_t)b * P.max_blocks;
-    auto tile_bases = [&](int ti, size_t& kb, size_t& vb) {
+    auto issue = [&](int ti, uint4 (&kr)[KPG][CPL], VT (&vr)[DPL]) {
       const int tk = t0 + (ti << 4);
-      const int blk = clampi(bt_row[tk / P.bs], 0, P.num_blocks - 1);
-      const int slot0 = tk % P.bs;
+      const int blk = __builtin_amdgcn_readlane(my_blk, uniform(tk / bs - p0));
+      const int slot0 = tk % bs;
       const size_t hb = (size_t)blk * P.H_kv + h;
-      kb = (hb * P.bs + slot0) * D;
-      vb = hb * D * P.bs + slot0;
-    };
-
-    uint4 kr[KPG][CPL];
-    VT vr[DPL];
-    int ti = w;
-    if (ti < n_tiles) {
-      size_t kb, vb;
-      tile_bases(ti, kb, vb);
+      const T* kp = kc + (hb * bs + slot0 + g * KPG) * D + c * VE;
+      const T* vp = vc + hb * D * bs + slot0 + (size_t)c * bs + g * KPG;
 #pragma unroll
       for (int i = 0; i < KPG; ++i)
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc)
-          kr[i][cc] = *reinterpret_cast<const uint4*>(kc + kb + (size_t)(g * KPG + i) * D + (c + cc * LPR) * VE);
+          kr[i][cc] = *reinterpret_cast<const uint4*>(kp + i * D + cc * LPR * VE);
 #pragma unroll
       for (int jj = 0; jj < DPL; ++jj)
-        vr[jj] = *reinterpret_cast<const VT*>(vc + vb + (size_t)(c + LPR * jj) * P.bs + g * KPG);
-    }
+        vr[jj] = *reinterpret_cast<const VT*>(vp + (size_t)jj * LPR * bs);
+    };
 
-    for (; ti < n_tiles; ti += kWaves) {
-      // issue the next tile's loads before computing on this one
-      uint4 nk[KPG][CPL];
-      VT nv[DPL];
-      const int tn = ti + kWaves;
-      if (tn < n_tiles) {
-        size_t kb, vb;
-        tile_bases(tn, kb, vb);
-#pragma unroll
-        for (int i = 0; i < KPG; ++i)
-#pragma unroll
-          for (int cc = 0; cc < CPL; ++cc)
-            nk[i][cc] = *reinterpret_cast<const uint4*>(kc + kb + (size_t)(g * KPG + i) * D + (c + cc * LPR) * VE);
-#pragma unroll
-        for (int jj = 0; jj < DPL; ++jj)
-          nv[jj] = *reinterpret_cast<const VT*>(vc + vb + (size_t)(c + LPR * jj) * P.bs + g * KPG);
-      }
-
-      const int tk = t0 + (ti << 4);
-      const bool full = tk + 16 <= n_min;
+    // tk: first token of the tile; a tile past the item (tk >= t1) is masked
+    // entirely (its loads were a duplicate of the last tile).
+    auto compute = [&](int tk, const uint4 (&kr)[KPG][CPL], const VT (&vr)[DPL]) {
+      const bool full = tk + 16 <= n_min && tk + 16 <= t1;
+      const int vis = tk < t1 ? n_total : 0;   // keys with written slots
       float vf[DPL][KPG];
 #pragma unroll
       for (int jj = 0; jj < DPL; ++jj) unpack_v(vr[jj], vf[jj], T());
       if (!full) {
 #pragma unroll
         for (int i = 0; i < KPG; ++i) {
-          if (tk + g * KPG + i >= n_total) {
+          if (tk + g * KPG + i >= vis) {
 #pragma unroll
             for (int jj = 0; jj < DPL; ++jj) vf[jj][i] = 0.f;  // slot not written yet
           }
         }
       }
-
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         if (r < P.nr) {
@@ -277,9 +262,10 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(KParams P) {
             sc[i] = group_sum<LPR>(part) * P.scale_log2;
           }
           if (!full) {
+            const int lim = tk < t1 ? n_r[r] : 0;
 #pragma unroll
             for (int i = 0; i < KPG; ++i)
-              if (tk + g * KPG + i >= n_r[r]) sc[i] = -INFINITY;
+              if (tk + g * KPG + i >= lim) sc[i] = -INFINITY;
           }
           float mx = sc[0];
 #pragma unroll
@@ -304,13 +290,24 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(KParams P) {
           m[r] = m_new;
         }
       }
+    };
 
-#pragma unroll
-      for (int i = 0; i < KPG; ++i)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) kr[i][cc] = nk[i][cc];
-#pragma unroll
-      for (int jj = 0; jj < DPL; ++jj) vr[jj] = nv[jj];
+    uint4 ka[KPG][CPL], kb[KPG][CPL];
+    VT va[DPL], vb[DPL];
+    const int last = n_tiles - 1;
+    // Drain the prologue's loads (q, block ids) first, so that at the tile
+    // loop's head the only loads in flight are one tile buffer on every path
+    // and the waits inside the loop count them exactly.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    issue(0, ka, va);
+    // Two tiles per trip, no branch inside: while one buffer is computed the
+    // other one's loads are in flight.  Past the last tile, loads re-read the
+    // last tile (cache hits) and compute() masks everything.
+    for (int ti = 0; ti <= last; ti += 2) {
+      issue(min(ti + 1, last), kb, vb);
+      compute(t0 + (ti << 4), ka, va);
+      issue(min(ti + 2, last), ka, va);
+      compute(t0 + ((ti + 1) << 4), kb, vb);
     }
 
     // ---- merge the key groups of this wave (lanes c, c+LPR, c+2LPR, ...) -----
@@ -331,77 +328,87 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(KParams P) {
         }
       }
     }
-    if (lane < LPR) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        if (r < P.nr) {
-#pragma unroll
-          for (int jj = 0; jj < DPL; ++jj) s_acc[w][r][c + LPR * jj] = acc[r][jj];
-          if (lane == 0) { s_m[w][r] = m[r]; s_l[w][r] = l[r]; }
-        }
-      }
-    }
-    __syncthreads();
 
-    // ---- merge the 4 waves; finish or publish the split ------------------------
+    // every lane now holds the merged state for its dims c + LPR*jj; key
+    // group g writes the jj in [g*DPL/NG, (g+1)*DPL/NG) (all jj if DPL < NG)
+    constexpr int JPG = DPL >= NG ? DPL / NG : DPL;
+    const int jbase = DPL >= NG ? g * JPG : 0;
+    const bool writer = DPL >= NG ? true : (g == 0);
     const size_t bh = (size_t)b * P.H_kv + h;
-    for (int e = tid; e < P.nr * D; e += kThreads) {
-      const int r = e / D, d = e - (e / D) * D;
-      float M = s_m[0][r];
 #pragma unroll
-      for (int i = 1; i < kWaves; ++i) M = fmaxf(M, s_m[i][r]);
-      float L = 0.f, A = 0.f;
-#pragma unroll
-      for (int i = 0; i < kWaves; ++i) {
-        const float f = __builtin_amdgcn_exp2f(s_m[i][r] - M);
-        L = fmaf(f, s_l[i][r], L);
-        A = fmaf(f, s_acc[i][r][d], A);
-      }
-      if (ns == 1) {
-        const int j = r / P.G, gi = r - (r / P.G) * P.G;
-        store_out(op + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D + d, L > 0.f ? A / L : 0.f);
-      } else {
-        const size_t pr = (bh * P.max_splits + s) * NR + r;
-        P.part_acc[pr * D + d] = A;
-        if (d == 0) { P.part_ml[2 * pr] = M; P.part_ml[2 * pr + 1] = L; }
-      }
-    }
-    if (ns > 1) {
-      __threadfence();
-      __syncthreads();
-      if (tid == 0) {
-        const int old = atomicAdd(&P.counters[bh], 1);
-        const int last = (old == ns - 1);
-        if (last) atomicExch(&P.counters[bh], 0);
-        s_last = last;
-      }
-      __syncthreads();
-      if (s_last) {
-        __threadfence();
-        for (int e = tid; e < P.nr * D; e += kThreads) {
-          const int r = e / D, d = e - (e / D) * D;
-          const size_t p0 = (bh * P.max_splits) * NR + r;
-          float M = kNegBig;
-          for (int i = 0; i < ns; ++i) M = fmaxf(M, P.part_ml[2 * (p0 + (size_t)i * NR)]);
-          float L = 0.f, A = 0.f;
-          for (int i = 0; i < ns; ++i) {
-            const size_t pr = p0 + (size_t)i * NR;
-            const float f = __builtin_amdgcn_exp2f(P.part_ml[2 * pr] - M);
-            L = fmaf(f, P.part_ml[2 * pr + 1], L);
-            A = fmaf(f, P.part_acc[pr * D + d], A);
-          }
+    for (int r = 0; r < NR; ++r) {
+      if (r < P.nr && writer) {
+        if (ns == 1) {
           const int j = r / P.G, gi = r - (r / P.G) * P.G;
-          store_out(op + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D + d, L > 0.f ? A / L : 0.f);
+          T* orow = op + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D;
+          const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
+#pragma unroll
+          for (int k = 0; k < JPG; ++k) {
+            const int jj = jbase + k;
+            store_out(orow + c + LPR * jj, acc[r][jj] * inv);
+          }
+        } else {
+          const size_t pr = (bh * P.max_splits + s) * NR + r;
+#pragma unroll
+          for (int k = 0; k < JPG; ++k) {
+            const int jj = jbase + k;
+            P.part_acc[pr * D + c + LPR * jj] = acc[r][jj];
+          }
+          if (lane == 0) { P.part_ml[2 * pr] = m[r]; P.part_ml[2 * pr + 1] = l[r]; }
         }
       }
     }
-    __syncthreads();  // LDS is reused by the next item
   }
+}
+
+// Merge the splits of each (stream, KV head) that has more than one, in split
+// order: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+template <typename T, int D, int NR>
+__global__ __launch_bounds__(kThreads) void attn_combine_kernel(KParams P) {
+  const int bh = blockIdx.x;
+  const int b = bh / P.H_kv;
+  const int h = bh - b * P.H_kv;
+  const int ns = split_count(P.kv_len[b], P);
+  if (ns <= 1) return;
+  T* __restrict__ op = static_cast<T*>(P.o);
+  for (int e = threadIdx.x; e < P.nr * D; e += kThreads) {
+    const int r = e / D, d = e - (e / D) * D;
+    const size_t p0 = (size_t)bh * P.max_splits * NR + r;
+    float M = kNegBig;
+    for (int i = 0; i < ns; ++i) M = fmaxf(M, P.part_ml[2 * (p0 + (size_t)i * NR)]);
+    float L = 0.f, A = 0.f;
+    for (int i = 0; i < ns; ++i) {
+      const size_t pr = p0 + (size_t)i * NR;
+      const float f = __builtin_amdgcn_exp2f(P.part_ml[2 * pr] - M);
+      L = fmaf(f, P.part_ml[2 * pr + 1], L);
+      A = fmaf(f, P.part_acc[pr * D + d], A);
+    }
+    const int j = r / P.G, gi = r - (r / P.G) * P.G;
+    store_out(op + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D + d, L > 0.f ? A / L : 0.f);
+  }
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 template <typename T, int D, int NR>
 hipError_t launch_t(const KParams& P, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((decode_attention_kernel<T, D, NR>), dim3(grid), dim3(kThreads), 0, s, P);
+  if (P.bs == 16)
+    hipLaunchKernelGGL((attn_split_kernel<T, D, NR, 16>), dim3(grid), dim3(kThreads), 0, s, P);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<T, D, NR, 0>), dim3(grid), dim3(kThreads), 0, s, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || P.max_splits <= 1) return e;
+  hipLaunchKernelGGL((attn_combine_kernel<T, D, NR>), dim3(P.B * P.H_kv), dim3(kThreads), 0, s, P);
   return hipGetLastError();
 }
 
@@ -427,22 +434,18 @@ bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_l
   if (nr > 16) return false;
   p->nr = nr;
   p->nr_tmpl = nr <= 1 ? 1 : nr <= 2 ? 2 : nr <= 4 ? 4 : nr <= 8 ? 8 : 16;
-  // Aim for ~8192 work items when lengths average half the maximum, in
-  // multiples of 64 tokens (16-token tiles x 4 waves), between 64 and 512.
+  // Aim for ~16k wave work items when lengths average half the maximum; a
+  // split is a multiple of 64 tokens between 64 and 256 (an item then spans
+  // at most 17 blocks of 16 tokens).
   const double est = (double)B * H_kv * (max_kv_len > 1 ? max_kv_len / 2.0 : 1.0);
-  long split = (long)((est / 8192.0 + 63.0) / 64.0) * 64;
+  long split = (long)((est / 16384.0 + 63.0) / 64.0) * 64;
   if (split < 64) split = 64;
-  if (split > 512) split = 512;
+  if (split > 256) split = 256;
   p->split = (int)split;
   p->max_splits = (int)((max_kv_len + split - 1) / split);
   const size_t slots = (size_t)B * H_kv * p->max_splits * p->nr_tmpl;
-  // The counter area has one fixed size, whatever B and H_kv are, so a
-  // workspace reused by calls of other shapes never finds partial results
-  // where it expects zeroed counters.
-  if ((long)B * H_kv > kMaxCounters) return false;
-  p->counters_bytes = (size_t)kMaxCounters * sizeof(int);
-  p->ml_offset = p->counters_bytes;
-  p->acc_offset = p->ml_offset + align256(slots * 2 * sizeof(float));
+  p->ml_offset = 0;
+  p->acc_offset = align256(slots * 2 * sizeof(float));
   p->total_bytes = p->acc_offset + align256(slots * (size_t)D * sizeof(float));
   return true;
 }
@@ -452,7 +455,6 @@ hipError_t launch_decode_attention(const AttnArgs& a, const AttnPlan& p, hipStre
   P.q = a.q; P.kc = a.k_cache; P.vc = a.v_cache;
   P.block_table = a.block_table; P.kv_len = a.kv_len; P.o = a.o;
   char* ws = static_cast<char*>(a.workspace);
-  P.counters = reinterpret_cast<int*>(ws);
   P.part_ml = reinterpret_cast<float*>(ws + p.ml_offset);
   P.part_acc = reinterpret_cast<float*>(ws + p.acc_offset);
   P.max_blocks = a.max_blocks;
@@ -462,8 +464,10 @@ hipError_t launch_decode_attention(const AttnArgs& a, const AttnPlan& p, hipStre
   P.nr = p.nr; P.bs = a.block_size; P.num_blocks = a.num_blocks;
   P.split = p.split; P.max_splits = p.max_splits;
   P.scale_log2 = a.scale * kLog2e;
-  const long upper = (long)a.B * a.H_kv * p.max_splits;
-  const int grid = (int)(upper < 2048 ? upper : 2048);
+  const long items = (long)a.B * a.H_kv * p.max_splits;       // upper bound
+  const long want = (items + kWaves - 1) / kWaves;
+  const long cap_wg = 3L * device_cus();
+  const int grid = (int)(want < cap_wg ? want : cap_wg);
   if (a.bf16) {
     if (a.D == 128) return launch_nr<uint16_t, 128>(P, p.nr_tmpl, grid, s);
     if (a.D == 64) return launch_nr<uint16_t, 64>(P, p.nr_tmpl, grid, s);

@@ -25,7 +25,7 @@ struct AttnPlan {
   int max_splits;   // ceil(max_kv_len / split)
   int nr;           // query rows per KV head = G * Kq
   int nr_tmpl;      // compiled row capacity (>= nr)
-  size_t counters_bytes, ml_offset, acc_offset, total_bytes;
+  size_t ml_offset, acc_offset, total_bytes;
 };
 // Deterministic function of the sizes; the workspace query and the call use it.
 bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_len, AttnPlan* p);

@@ -110,8 +110,6 @@ int clm_kv_cache_append(const void* k_new, const void* v_new, void* k_cache, voi
  * Bytes of workspace clm_decode_attention needs for these sizes (0 on a size
  * error).  max_kv_len bounds kv_len[b] for every stream of the call.
  */
-#define CLM_ATTN_COUNTER_BYTES (65536 * 4)
-
 size_t clm_decode_attention_workspace_size(int B, int Kq, int H_q, int H_kv, int D,
                                            int max_kv_len);
 
@@ -134,15 +132,13 @@ size_t clm_decode_attention_workspace_size(int B, int Kq, int H_q, int H_kv, int
  *   o          [B, Kq, H_q, D]        output, element type dt
  *   scale                             score scale (1/sqrt(D) for standard attention)
  *   workspace  >= clm_decode_attention_workspace_size(...) bytes, 256-byte
- *              aligned.  Its first CLM_ATTN_COUNTER_BYTES bytes hold completion
- *              counters; they MUST be zero before the first call that uses
- *              this workspace, and every call leaves them zero again and
- *              writes nothing else there, so one workspace can serve calls of
- *              any shape.  Calls that share a workspace must be ordered on
- *              one stream.
+ *              aligned, caller-owned scratch for per-split partial results
+ *              (no initial contents needed).  Calls that share a workspace
+ *              must be ordered on one stream.
  * Arithmetic: fp32 dot products, exponentials, online softmax and
- * accumulation; o rounded to dt once.  Results do not depend on the order in
- * which workgroups finish (splits are merged in a fixed order).
+ * accumulation; o rounded to dt once.  Streams longer than one split are
+ * merged by a second kernel in split order, so results are the same from run
+ * to run and do not depend on the order in which workgroups finish.
  * Errors: INVALID_ARG (null, sizes < 1, H_q % H_kv != 0, max_kv_len < Kq,
  *   scale not finite), UNSUPPORTED (D not 64/128, G*Kq > 16, B > 4096,
  *   B*H_kv > 65536, block_size as for append, unknown dt), WORKSPACE (too
