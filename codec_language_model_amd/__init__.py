@@ -79,9 +79,9 @@ def _stream():
 
 
 class Workspace:
-    """Device scratch for decode_attention's per-split partial results, cached
-    per device and grown on demand; calls that share it must be ordered on one
-    stream (torch's current stream is used for every call)."""
+    """Device scratch for decode_attention's per-split partial results,
+    cached per device and grown on demand.  Calls that share it must be
+    ordered on one stream (torch's current stream is used for every call)."""
 
     _cache = {}
 

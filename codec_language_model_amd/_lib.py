@@ -41,12 +41,13 @@ SIGNATURES = {
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> C.CDLL:
-    """Load libclm.so (once).  Raises if it has not been built: the library
-    has no fallback path."""
+def load(path: str = None) -> C.CDLL:
+    """Load libclm.so (once): ``path``, else $CLM_LIBRARY, else the in-tree
+    build.  Raises if the library is missing: there is no fallback path."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("CLM_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m codec_language_model_amd.build` "

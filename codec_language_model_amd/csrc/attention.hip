@@ -10,11 +10,15 @@
 // Work decomposition.  A work item is (stream b, KV head h, split s): the
 // tokens [s*split, min((s+1)*split, kv_len[b])) of one KV head.  All G*Kq
 // query rows that share the KV head are served by one pass over its K/V
-// bytes, so every K/V byte is read from HBM once per step.  Each wave owns
-// whole items: the grid is persistent, every workgroup derives the item list
-// from kv_len (a prefix sum of per-stream split counts, in LDS, built once),
-// and its waves stride through the list independently - no barrier, no LDS
-// and no cross-workgroup traffic in the main loop.
+// bytes, so every K/V byte is read from HBM once per step.  The grid is
+// persistent: every workgroup rebuilds the item numbering from kv_len once
+// (stream lengths and prefix sums in LDS) - first every full-size split of
+// every stream, then each stream's shorter last split - and its waves take
+// items round-robin over the grid's waves.  (A shared ticket counter balanced
+// the tail better but cost more: device-wide atomics on one address serialise
+// across the chip.)  While a wave streams one item it already loads the next
+// item's block ids and query slice.  No barrier, LDS access or cross-wave
+// traffic in the main loop.
 //
 // Inside an item a wave walks 16-token tiles.  The block ids of the item's
 // pages are fetched once, one per lane, and picked out with readlane.  Keys
@@ -22,15 +26,17 @@
 // for bf16, D = 128), so one load instruction covers 4 whole rows; the LPR
 // partial dot products are summed with DPP inside the 16-lane row.  Values
 // are stored transposed inside a block ([D][bs]), so for each of its head
-// dimensions a lane reads the run of keys its group scored, contiguous
-// across the wave.  The next tile's loads are always in flight while the
-// current tile is computed (past the last tile the current one is re-read,
-// which hits in cache), so the wait counts stay exact.  Each 16-lane key
-// group keeps its own online-softmax state (running max m, sum l,
-// accumulator) in registers; the groups merge with shuffles at the end of an
-// item.  A stream that fits in one split is written directly; otherwise the
-// split's (m, l, acc) goes to the workspace and a second small kernel merges
-// the splits of each (stream, KV head) in split order (deterministic).
+// dimensions a lane reads the run of keys its group scored, contiguous across
+// the wave.  The loop body covers two tiles without a branch: while one tile
+// buffer is computed the other's loads are in flight (past the last tile the
+// loads re-read it, which hits in cache, and the tile is masked), so the wait
+// counts stay exact.  Each 16-lane key group keeps its own online-softmax
+// state (running max m, sum l, accumulator) in registers; the groups merge
+// with shuffles at the end of an item.  A stream that fits in one split is
+// written directly; otherwise the split's (m, l, acc) goes to the workspace
+// and a second kernel merges the splits of each row in split order.
+#include <type_traits>
+
 #include "clm_device.h"
 #include "clm_launch.h"
 
@@ -67,6 +73,10 @@ __device__ __forceinline__ void unpack_v(uint32_t w, float* f, uint16_t) {
 __device__ __forceinline__ void unpack_v(uint2 w, float* f, uint16_t) {
   f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
 }
+__device__ __forceinline__ void to_words(uint32_t v, uint32_t* w) { w[0] = v; }
+__device__ __forceinline__ void to_words(uint2 v, uint32_t* w) { w[0] = v.x; w[1] = v.y; }
+__device__ __forceinline__ void to_words(uint4 v, uint32_t* w) { w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; }
+
 __device__ __forceinline__ void unpack_v(uint4 w, float* f, float) {
   f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
   f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
@@ -104,108 +114,203 @@ struct KParams {
   float scale_log2;
 };
 
-__device__ __forceinline__ int split_count(int len, const KParams& P) {
-  int n = clampi(len, 1, P.cap);
-  int s = (n + P.split - 1) / P.split;
-  return clampi(s, 1, P.max_splits);
+__device__ __forceinline__ int stream_len(int len, const KParams& P) { return clampi(len, 1, P.cap); }
+__device__ __forceinline__ int full_splits(int n, const KParams& P) { return min(n / P.split, P.max_splits); }
+__device__ __forceinline__ int split_count(int n, const KParams& P) {
+  return clampi((n + P.split - 1) / P.split, 1, P.max_splits);
 }
 
-template <typename T, int D, int NR, int BS>
+// Exclusive block-wide prefix over B per-stream counts, into s[0..B].
+template <class F>
+__device__ void block_prefix(int* s, int* s_wsum, int B, F count) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (B + kThreads - 1) / kThreads;
+  const int b0 = tid * per;
+  int local = 0;
+  for (int k = 0; k < per; ++k)
+    if (b0 + k < B) local += count(b0 + k);
+  const int incl = wave_incl_scan_i(local, lane);
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int i = 0; i < w; ++i) run += s_wsum[i];
+  for (int k = 0; k < per; ++k) {
+    if (b0 + k < B) {
+      s[b0 + k] = run;
+      run += count(b0 + k);
+    }
+  }
+  if (tid == 0) s[B] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+  __syncthreads();
+}
+
+// largest b in [0, B) with s[b] <= u (s non-decreasing, s[0] = 0)
+__device__ __forceinline__ int find_stream(const int* s, int B, int u) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The streams whose last split is shorter than `split`, ordered by that
+// split's tile count (1..16) descending, then by stream index: s[0..n).  A
+// counting sort with one block-wide scan per tile count, so every workgroup
+// builds the same list.  tiles(b) = 0 means no short split.  Returns n.
+template <class F>
+__device__ int short_splits_sorted(int* s, int (*s_bins)[16], int B, F tiles) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (B + kThreads - 1) / kThreads;
+  const int b0 = tid * per;
+  int cnt[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) cnt[k] = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    const int t = b < B ? tiles(b) : 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) cnt[k] += (t == 16 - k);
+  }
+  int excl[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int incl = wave_incl_scan_i(cnt[k], lane);
+    excl[k] = incl - cnt[k];
+    if (lane == 63) s_bins[w][k] = incl;
+  }
+  __syncthreads();
+  int start = 0, n = 0;
+  int pos[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    int before = 0, tot = 0;
+    for (int i = 0; i < kWaves; ++i) {
+      before += i < w ? s_bins[i][k] : 0;
+      tot += s_bins[i][k];
+    }
+    pos[k] = start + before + excl[k];
+    start += tot;
+  }
+  n = start;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    const int t = b < B ? tiles(b) : 0;
+    if (t > 0) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (t == 16 - k) s[pos[k]++] = b;
+    }
+  }
+  __syncthreads();
+  return n;
+}
+
+template <typename T, int D, int NR, int BS, bool EXACT>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
   using G_ = Geo<T, D>;
   constexpr int LPR = G_::LPR, CPL = G_::CPL, KPG = G_::KPG, DPL = G_::DPL, VE = G_::VE;
   constexpr int NG = G_::NG;
   using VT = typename G_::VT;
 
-  __shared__ int s_prefix[kMaxB + 1];
+  __shared__ int s_full[kMaxB + 1];   // prefix of full-size splits per stream
+  __shared__ int s_plist[kMaxB];      // streams with a short last split, longest first
+  __shared__ int s_bins[kWaves][16];
+  __shared__ int s_len[kMaxB];        // clamped stream lengths
   __shared__ int s_wsum[kWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = uniform(tid >> 6);
   const int g = lane / LPR;
   const int c = lane % LPR;
   const int bs = BS ? BS : P.bs;
+  // query rows of this call: NR exactly when EXACT (no per-row test)
+  const int nrow = EXACT ? NR : P.nr;
 
   const T* __restrict__ qp = static_cast<const T*>(P.q);
   const T* __restrict__ kc = static_cast<const T*>(P.kc);
   const T* __restrict__ vc = static_cast<const T*>(P.vc);
   T* __restrict__ op = static_cast<T*>(P.o);
 
-  // ---- item list: exclusive prefix of per-stream split counts ---------------
-  {
-    const int per = (P.B + kThreads - 1) / kThreads;
-    const int b0 = tid * per;
-    int local = 0;
-    for (int k = 0; k < per; ++k) {
-      int b = b0 + k;
-      if (b < P.B) local += split_count(P.kv_len[b], P);
+  for (int b = tid; b < P.B; b += kThreads) s_len[b] = stream_len(P.kv_len[b], P);
+  __syncthreads();
+  block_prefix(s_full, s_wsum, P.B, [&](int b) { return full_splits(s_len[b], P); });
+  const int n_part = short_splits_sorted(s_plist, s_bins, P.B, [&](int b) {
+    const int rem = s_len[b] - full_splits(s_len[b], P) * P.split;
+    return rem > 0 ? (rem + 15) >> 4 : 0;
+  });
+  const int n_full = s_full[P.B] * P.H_kv;
+  const int total_items = n_full + n_part * P.H_kv;
+  const int nw_total = gridDim.x * kWaves;
+
+  // item -> (stream, split, KV head), from LDS only
+  auto locate = [&](int item, int& b, int& s, int& h) {
+    if (item < n_full) {
+      const int u = item / P.H_kv;
+      h = item - u * P.H_kv;
+      b = find_stream(s_full, P.B, u);
+      s = u - s_full[b];
+    } else {
+      const int t = item - n_full;
+      const int u = t / P.H_kv;
+      h = t - u * P.H_kv;
+      b = s_plist[u];
+      s = s_full[b + 1] - s_full[b];   // the last split follows the full ones
     }
-    int incl = wave_incl_scan_i(local, lane);
-    if (lane == 63) s_wsum[w] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int i = 0; i < w; ++i) base += s_wsum[i];
-    int run = base + incl - local;
-    for (int k = 0; k < per; ++k) {
-      int b = b0 + k;
-      if (b < P.B) {
-        s_prefix[b] = run;
-        run += split_count(P.kv_len[b], P);
+    b = uniform(b);
+    s = uniform(s);
+    h = uniform(h);
+  };
+  // the item's block ids (one page per lane; an item spans <= 64 pages) and
+  // this lane's slice of its query rows
+  auto fetch = [&](int item, int& blk, uint32_t (&qv)[NR][4 * CPL]) {
+    int b, s, h;
+    locate(item, b, s, h);
+    const int n = s_len[b];
+    const int t0 = s * P.split;
+    const int t1 = min(t0 + P.split, n);
+    const int p0 = t0 / bs;
+    const int n_pages = (t1 - 1) / bs - p0 + 1;
+    blk = 0;
+    if (lane < n_pages) blk = clampi(P.block_table[(size_t)b * P.max_blocks + p0 + lane], 0, P.num_blocks - 1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+      for (int i = 0; i < 4 * CPL; ++i) qv[r][i] = 0u;
+      if (r < nrow) {
+        const int j = r / P.G, gi = r - (r / P.G) * P.G;
+        const T* qrow = qp + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+          const uint4 v = *reinterpret_cast<const uint4*>(qrow + (c + cc * LPR) * VE);
+          qv[r][cc * 4 + 0] = v.x; qv[r][cc * 4 + 1] = v.y;
+          qv[r][cc * 4 + 2] = v.z; qv[r][cc * 4 + 3] = v.w;
+        }
       }
     }
-    if (tid == 0) s_prefix[P.B] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-    __syncthreads();
-  }
-  const int total_items = s_prefix[P.B] * P.H_kv;
-  const int nwaves = gridDim.x * kWaves;
+  };
 
-  for (int item = blockIdx.x * kWaves + w; item < total_items; item += nwaves) {
-    const int u = item / P.H_kv;
-    const int h = item - u * P.H_kv;
-    int lo = 0, hi = P.B - 1;  // largest b with s_prefix[b] <= u
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= u) lo = mid; else hi = mid - 1;
-    }
-    const int b = uniform(lo);
-    const int s = uniform(u - s_prefix[b]);
-    const int ns = uniform(s_prefix[b + 1] - s_prefix[b]);
+  // Items go round-robin over the grid's waves (full-size splits first); the
+  // next item's block ids and query slice are loaded while this one streams.
+  int item = blockIdx.x * kWaves + (tid >> 6);
+  int my_blk = 0;
+  uint32_t qw[NR][4 * CPL];
+  if (item < total_items) fetch(item, my_blk, qw);
 
-    const int n_total = uniform(clampi(P.kv_len[b], 1, P.cap));
+  while (item < total_items) {
+    const int next_item = item + nw_total;
+    int b, s, h;
+    locate(item, b, s, h);
+    const int n_total = s_len[b];
+    const int ns = split_count(n_total, P);
     const int n_min = n_total - (P.Kq - 1);       // keys seen by the first query
     const int t0 = s * P.split;
     const int t1 = min(t0 + P.split, n_total);
     const int n_tiles = (t1 - t0 + 15) >> 4;
     const int p0 = t0 / bs;
-
-    // block ids of the item's pages, one per lane (an item spans <= 64 pages)
-    int my_blk = 0;
-    {
-      const int n_pages = (t1 - 1) / bs - p0 + 1;
-      if (lane < n_pages) my_blk = clampi(P.block_table[(size_t)b * P.max_blocks + p0 + lane], 0, P.num_blocks - 1);
-    }
-
-    // ---- this lane's slice of the query rows --------------------------------
-    uint32_t qw[NR][4 * CPL];
     int n_r[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      n_r[r] = 0;
-#pragma unroll
-      for (int i = 0; i < 4 * CPL; ++i) qw[r][i] = 0u;
-      if (r < P.nr) {
-        const int j = r / P.G, gi = r - (r / P.G) * P.G;
-        n_r[r] = n_total - (P.Kq - 1 - j);
-        const T* qrow = qp + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D;
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) {
-          uint4 v = *reinterpret_cast<const uint4*>(qrow + (c + cc * LPR) * VE);
-          qw[r][cc * 4 + 0] = v.x; qw[r][cc * 4 + 1] = v.y;
-          qw[r][cc * 4 + 2] = v.z; qw[r][cc * 4 + 3] = v.w;
-        }
-      }
-    }
+    for (int r = 0; r < NR; ++r) n_r[r] = r < nrow ? n_total - (P.Kq - 1 - r / P.G) : 0;
 
     float m[NR], l[NR], acc[NR][DPL];
 #pragma unroll
@@ -233,76 +338,118 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
         vr[jj] = *reinterpret_cast<const VT*>(vp + (size_t)jj * LPR * bs);
     };
 
-    // tk: first token of the tile; a tile past the item (tk >= t1) is masked
-    // entirely (its loads were a duplicate of the last tile).
-    auto compute = [&](int tk, const uint4 (&kr)[KPG][CPL], const VT (&vr)[DPL]) {
-      const bool full = tk + 16 <= n_min && tk + 16 <= t1;
-      const int vis = tk < t1 ? n_total : 0;   // keys with written slots
-      float vf[DPL][KPG];
+    // P.V for one tile; MASK zeroes value lanes of keys past `vis` (slots
+    // that may hold anything, NaN included).  bf16: the transposed block
+    // layout puts a head dimension's values for two consecutive keys in one
+    // 32-bit word, so the products go through v_dot2_f32_bf16 against the
+    // probabilities packed to bf16 pairs (fp32 accumulation); fp32: FMAs.
+    auto pv = [&](auto mask_tag, const VT (&vr)[DPL], const float (&p)[NR][KPG], const float (&corr)[NR],
+                  int tk, int vis) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      if constexpr (std::is_same<T, uint16_t>::value) {
+        constexpr int NW = KPG / 2;
+        uint32_t pk[NR][NW];
 #pragma unroll
-      for (int jj = 0; jj < DPL; ++jj) unpack_v(vr[jj], vf[jj], T());
-      if (!full) {
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int i = 0; i < KPG; ++i) {
-          if (tk + g * KPG + i >= vis) {
+          for (int i2 = 0; i2 < NW; ++i2) pk[r][i2] = pack_bf16x2(p[r][2 * i2], p[r][2 * i2 + 1]);
+        uint32_t keep[NW];
 #pragma unroll
-            for (int jj = 0; jj < DPL; ++jj) vf[jj][i] = 0.f;  // slot not written yet
+        for (int i2 = 0; i2 < NW; ++i2) {
+          const int t = tk + g * KPG + 2 * i2;
+          keep[i2] = (t < vis ? 0x0000ffffu : 0u) | (t + 1 < vis ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) {
+          uint32_t wv[NW];
+          to_words(vr[jj], wv);
+          if (MASK) {
+#pragma unroll
+            for (int i2 = 0; i2 < NW; ++i2) wv[i2] &= keep[i2];
+          }
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            if (r < nrow) {
+              float a = acc[r][jj] * corr[r];
+#pragma unroll
+              for (int i2 = 0; i2 < NW; ++i2) a = dot2_bf16(pk[r][i2], wv[i2], a);
+              acc[r][jj] = a;
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) {
+          float vf[KPG];
+          unpack_v(vr[jj], vf, T());
+          if (MASK) {
+#pragma unroll
+            for (int i = 0; i < KPG; ++i) vf[i] = (tk + g * KPG + i < vis) ? vf[i] : 0.f;
+          }
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            if (r < nrow) {
+              float a = acc[r][jj] * corr[r];
+#pragma unroll
+              for (int i = 0; i < KPG; ++i) a = fmaf(p[r][i], vf[i], a);
+              acc[r][jj] = a;
+            }
           }
         }
       }
+    };
+
+    // tk: first token of the tile; a tile past the item (tk >= t1) is masked
+    // entirely (its loads were a duplicate of the last tile).  No branch:
+    // the key masks are applied on every tile (all-pass on full tiles), which
+    // costs a few selects but keeps the accumulators in place.
+    auto compute = [&](int tk, const uint4 (&kr)[KPG][CPL], const VT (&vr)[DPL]) {
+      const int vis = tk < t1 ? n_total : 0;   // keys whose slots are written
+      float p[NR][KPG], corr[NR];
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        if (r < P.nr) {
+        corr[r] = 1.f;
+#pragma unroll
+        for (int i = 0; i < KPG; ++i) p[r][i] = 0.f;
+        if (r < nrow) {
+          const int lim = tk < t1 ? n_r[r] : 0;
           float sc[KPG];
 #pragma unroll
           for (int i = 0; i < KPG; ++i) {
             float part = 0.f;
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) part = chunk_dot(&qw[r][cc * 4], kr[i][cc], part, T());
-            sc[i] = group_sum<LPR>(part) * P.scale_log2;
-          }
-          if (!full) {
-            const int lim = tk < t1 ? n_r[r] : 0;
-#pragma unroll
-            for (int i = 0; i < KPG; ++i)
-              if (tk + g * KPG + i >= lim) sc[i] = -INFINITY;
+            const float sum = group_sum<LPR>(part) * P.scale_log2;   // every lane of the row
+            sc[i] = tk + g * KPG + i < lim ? sum : -INFINITY;
           }
           float mx = sc[0];
 #pragma unroll
           for (int i = 1; i < KPG; ++i) mx = fmaxf(mx, sc[i]);
           const float m_new = fmaxf(m[r], mx);
-          const float corr = __builtin_amdgcn_exp2f(m[r] - m_new);
-          float p[KPG];
+          corr[r] = __builtin_amdgcn_exp2f(m[r] - m_new);
           float psum = 0.f;
 #pragma unroll
           for (int i = 0; i < KPG; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
-            psum += p[i];
+            p[r][i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+            psum += p[r][i];
           }
-          l[r] = l[r] * corr + psum;
-#pragma unroll
-          for (int jj = 0; jj < DPL; ++jj) {
-            float a = acc[r][jj] * corr;
-#pragma unroll
-            for (int i = 0; i < KPG; ++i) a = fmaf(p[i], vf[jj][i], a);
-            acc[r][jj] = a;
-          }
+          l[r] = l[r] * corr[r] + psum;
           m[r] = m_new;
         }
       }
+      pv(std::true_type(), vr, p, corr, tk, vis);
     };
 
     uint4 ka[KPG][CPL], kb[KPG][CPL];
     VT va[DPL], vb[DPL];
     const int last = n_tiles - 1;
-    // Drain the prologue's loads (q, block ids) first, so that at the tile
-    // loop's head the only loads in flight are one tile buffer on every path
-    // and the waits inside the loop count them exactly.
+    // Drain what is still in flight (the previous item's trailing duplicate
+    // tile, cache hits) so that the tile loop's waits count exactly.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     issue(0, ka, va);
-    // Two tiles per trip, no branch inside: while one buffer is computed the
-    // other one's loads are in flight.  Past the last tile, loads re-read the
-    // last tile (cache hits) and compute() masks everything.
+    int nblk = 0;
+    uint32_t nq[NR][4 * CPL];
+    if (next_item < total_items) fetch(next_item, nblk, nq);
     for (int ti = 0; ti <= last; ti += 2) {
       issue(min(ti + 1, last), kb, vb);
       compute(t0 + (ti << 4), ka, va);
@@ -315,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
     for (int off = LPR; off < 64; off <<= 1) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        if (r < P.nr) {
+        if (r < nrow) {
           const float mo = __shfl_xor(m[r], off, 64);
           const float lo_ = __shfl_xor(l[r], off, 64);
           const float M = fmaxf(m[r], mo);
@@ -337,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
     const size_t bh = (size_t)b * P.H_kv + h;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      if (r < P.nr && writer) {
+      if (r < nrow && writer) {
         if (ns == 1) {
           const int j = r / P.G, gi = r - (r / P.G) * P.G;
           T* orow = op + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D;
@@ -358,34 +505,77 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
         }
       }
     }
+    item = next_item;
+    my_blk = nblk;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int i = 0; i < 4 * CPL; ++i) qw[r][i] = nq[r][i];
   }
 }
 
-// Merge the splits of each (stream, KV head) that has more than one, in split
-// order: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+// Merge the splits of each (stream, KV head, query row) that has more than
+// one: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, in split order.
+// One wave per row: lane i holds split i's (m, l); each lane accumulates
+// D/64 head dimensions.
 template <typename T, int D, int NR>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(KParams P) {
-  const int bh = blockIdx.x;
+  constexpr int DL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= P.B * P.H_kv * P.nr) return;
+  const int r = row % P.nr;
+  const int bh = row / P.nr;
   const int b = bh / P.H_kv;
   const int h = bh - b * P.H_kv;
-  const int ns = split_count(P.kv_len[b], P);
+  const int ns = uniform(split_count(stream_len(P.kv_len[b], P), P));
   if (ns <= 1) return;
-  T* __restrict__ op = static_cast<T*>(P.o);
-  for (int e = threadIdx.x; e < P.nr * D; e += kThreads) {
-    const int r = e / D, d = e - (e / D) * D;
-    const size_t p0 = (size_t)bh * P.max_splits * NR + r;
-    float M = kNegBig;
-    for (int i = 0; i < ns; ++i) M = fmaxf(M, P.part_ml[2 * (p0 + (size_t)i * NR)]);
-    float L = 0.f, A = 0.f;
-    for (int i = 0; i < ns; ++i) {
-      const size_t pr = p0 + (size_t)i * NR;
-      const float f = __builtin_amdgcn_exp2f(P.part_ml[2 * pr] - M);
-      L = fmaf(f, P.part_ml[2 * pr + 1], L);
-      A = fmaf(f, P.part_acc[pr * D + d], A);
-    }
-    const int j = r / P.G, gi = r - (r / P.G) * P.G;
-    store_out(op + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D + d, L > 0.f ? A / L : 0.f);
+  const size_t base = (size_t)bh * P.max_splits * NR + r;
+
+  // (m, l) of up to 64 splits per lane-parallel pass; accumulators in
+  // batches of 16 splits whose loads are all issued before any is used
+  float M = kNegBig;
+  for (int i0 = 0; i0 < ns; i0 += 64) {
+    const int i = i0 + lane;
+    const float mi = i < ns ? P.part_ml[2 * (base + (size_t)i * NR)] : kNegBig;
+    M = fmaxf(M, wave_max(mi));
   }
+  float L = 0.f, A[DL];
+#pragma unroll
+  for (int e = 0; e < DL; ++e) A[e] = 0.f;
+  for (int i0 = 0; i0 < ns; i0 += 64) {
+    const int i = i0 + lane;
+    float f = 0.f, li = 0.f;
+    if (i < ns) {
+      f = __builtin_amdgcn_exp2f(P.part_ml[2 * (base + (size_t)i * NR)] - M);
+      li = P.part_ml[2 * (base + (size_t)i * NR) + 1];
+    }
+    L += wave_sum(f * li);
+    const int cnt = min(64, ns - i0);
+    for (int k0 = 0; k0 < cnt; k0 += 16) {
+      float v[16][DL];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int kk = min(k0 + k, cnt - 1);
+        const float* a = P.part_acc + (base + (size_t)(i0 + kk) * NR) * D + lane;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) v[k][e] = a[64 * e];
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float fk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), min(k0 + k, 63)));
+        if (k0 + k < cnt) {
+#pragma unroll
+          for (int e = 0; e < DL; ++e) A[e] = fmaf(fk, v[k][e], A[e]);
+        }
+      }
+    }
+  }
+  const int j = r / P.G, gi = r - (r / P.G) * P.G;
+  T* orow = static_cast<T*>(P.o) + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < DL; ++e) store_out(orow + lane + 64 * e, A[e] * inv);
 }
 
 int device_cus() {
@@ -402,13 +592,17 @@ int device_cus() {
 
 template <typename T, int D, int NR>
 hipError_t launch_t(const KParams& P, int grid, hipStream_t s) {
-  if (P.bs == 16)
-    hipLaunchKernelGGL((attn_split_kernel<T, D, NR, 16>), dim3(grid), dim3(kThreads), 0, s, P);
+  const bool exact = P.nr == NR;
+  if (P.bs == 16 && exact)
+    hipLaunchKernelGGL((attn_split_kernel<T, D, NR, 16, true>), dim3(grid), dim3(kThreads), 0, s, P);
+  else if (P.bs == 16)
+    hipLaunchKernelGGL((attn_split_kernel<T, D, NR, 16, false>), dim3(grid), dim3(kThreads), 0, s, P);
   else
-    hipLaunchKernelGGL((attn_split_kernel<T, D, NR, 0>), dim3(grid), dim3(kThreads), 0, s, P);
+    hipLaunchKernelGGL((attn_split_kernel<T, D, NR, 0, false>), dim3(grid), dim3(kThreads), 0, s, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.max_splits <= 1) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<T, D, NR>), dim3(P.B * P.H_kv), dim3(kThreads), 0, s, P);
+  const long rows = (long)P.B * P.H_kv * P.nr;
+  hipLaunchKernelGGL((attn_combine_kernel<T, D, NR>), dim3((rows + kWaves - 1) / kWaves), dim3(kThreads), 0, s, P);
   return hipGetLastError();
 }
 
@@ -419,6 +613,7 @@ hipError_t launch_nr(const KParams& P, int nr_tmpl, int grid, hipStream_t s) {
     case 2: return launch_t<T, D, 2>(P, grid, s);
     case 4: return launch_t<T, D, 4>(P, grid, s);
     case 8: return launch_t<T, D, 8>(P, grid, s);
+    case 12: return launch_t<T, D, 12>(P, grid, s);
     case 16: return launch_t<T, D, 16>(P, grid, s);
   }
   return hipErrorInvalidValue;
@@ -433,10 +628,10 @@ bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_l
   const int nr = (H_q / H_kv) * Kq;
   if (nr > 16) return false;
   p->nr = nr;
-  p->nr_tmpl = nr <= 1 ? 1 : nr <= 2 ? 2 : nr <= 4 ? 4 : nr <= 8 ? 8 : 16;
-  // Aim for ~16k wave work items when lengths average half the maximum; a
-  // split is a multiple of 64 tokens between 64 and 256 (an item then spans
-  // at most 17 blocks of 16 tokens).
+  p->nr_tmpl = nr <= 1 ? 1 : nr <= 2 ? 2 : nr <= 4 ? 4 : nr <= 8 ? 8 : nr <= 12 ? 12 : 16;
+  // Aim for ~16k work items when lengths average half the maximum; a split
+  // is a multiple of 64 tokens between 64 and 256 (an item then spans at most
+  // 17 blocks of 16 tokens).
   const double est = (double)B * H_kv * (max_kv_len > 1 ? max_kv_len / 2.0 : 1.0);
   long split = (long)((est / 16384.0 + 63.0) / 64.0) * 64;
   if (split < 64) split = 64;
@@ -445,7 +640,7 @@ bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_l
   p->max_splits = (int)((max_kv_len + split - 1) / split);
   const size_t slots = (size_t)B * H_kv * p->max_splits * p->nr_tmpl;
   p->ml_offset = 0;
-  p->acc_offset = align256(slots * 2 * sizeof(float));
+  p->acc_offset = p->ml_offset + align256(slots * 2 * sizeof(float));
   p->total_bytes = p->acc_offset + align256(slots * (size_t)D * sizeof(float));
   return true;
 }

@@ -132,8 +132,8 @@ size_t clm_decode_attention_workspace_size(int B, int Kq, int H_q, int H_kv, int
  *   o          [B, Kq, H_q, D]        output, element type dt
  *   scale                             score scale (1/sqrt(D) for standard attention)
  *   workspace  >= clm_decode_attention_workspace_size(...) bytes, 256-byte
- *              aligned, caller-owned scratch for per-split partial results
- *              (no initial contents needed).  Calls that share a workspace
+ *              aligned, caller-owned scratch for per-split partial results;
+ *              no initial contents are needed.  Calls that share a workspace
  *              must be ordered on one stream.
  * Arithmetic: fp32 dot products, exponentials, online softmax and
  * accumulation; o rounded to dt once.  Streams longer than one split are
