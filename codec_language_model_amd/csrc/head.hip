@@ -4,14 +4,24 @@
 //
 // bf16: matrix-core kernel.  A workgroup owns VT*16 codebook entries of one
 // stage's W and up to 64 rows of that stage (rows are gathered by head id, in
-// batch order), so each W byte is streamed from HBM once per 64 rows.  The
-// products use v_mfma_f32_16x16x32_bf16 with W as the A operand (16 codebook
-// entries x 32 k) and h as B (32 k x 16 rows): the accumulator lane l holds
-// logits for row l%16 and 4 consecutive entries, which become one 16-byte
-// store.  The four waves split the reduction (k) dimension; their partial
-// tiles are summed in LDS in wave order, so the result is deterministic.
-// Operands come straight from global memory with the next k-step's loads in
-// flight; h (<= 64 rows) stays resident in L2 while W streams past it.
+// batch order).  The products use v_mfma_f32_16x16x32_bf16 with W as the A
+// operand (16 codebook entries x 32 k) and h as B (32 k x 16 rows): the
+// accumulator lane l holds logits for row l%16 and 4 consecutive entries.
+// The four waves split the reduction (k) dimension; their partial tiles are
+// summed in LDS in wave order, so the result is deterministic.
+//
+// Operands come straight from global memory through a 3-deep register ring:
+// two k-steps of loads are in flight while one is multiplied, and the
+// steady-state loop has no branch at all (loads past the end re-read the last
+// k-step, which hits in cache; the last k-steps are multiplied after the
+// loop), so wait counts stay exact.  When a stage has several row chunks,
+// they read the same W tile: the 1-D grid is laid out so those workgroups sit
+// on one XCD (the hardware deals workgroup i to XCD i % 8) and are dispatched
+// together, so W comes from HBM once and from that XCD's L2 after.
+//
+// More than 64 rows per call: tiles of up to 128 codebook entries x 128 rows
+// are staged through LDS by the global-to-LDS DMA loads, so the operands never
+// pass through registers on their way in; the matrix cores read them from LDS.
 //
 // fp32: a plain wave-per-row GEMV (used by the small fp32 workload).
 #include "clm_device.h"
@@ -21,27 +31,39 @@ namespace clm {
 namespace {
 
 constexpr int kRowsPerWG = 64;
+constexpr int kXcds = 8;
+constexpr int kRing = 3;
+constexpr int kSplitK = 4;             // waves per workgroup, each 1/4 of k
+constexpr int kThreads = kSplitK * 64;
 
 struct HeadP {
   const uint16_t* h;
   const uint16_t* W[8];
   const int32_t* head_id;
   float* logits;
-  int G, M, d, V, row_chunks;
+  int G, M, d, V, row_chunks, nvt, nvt_pad;
 };
 
-template <int VT>
-__global__ __launch_bounds__(256) void head_mfma_kernel(HeadP P) {
+template <int VT, int RT>
+__global__ __launch_bounds__(kThreads) void head_mfma_kernel(HeadP P) {
   constexpr int NV = VT * 16;        // codebook entries per workgroup
   constexpr int LDW = NV + 4;        // padded LDS row (floats)
   __shared__ int s_rows[kRowsPerWG];
-  __shared__ int s_cnt[4];
-  __shared__ float s_red[4][kRowsPerWG][LDW];
+  __shared__ int s_cnt[kSplitK];
+  __shared__ float s_red[kSplitK][kRowsPerWG][LDW];
 
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
-  const int grp = blockIdx.y / P.row_chunks;
-  const int rc = blockIdx.y - grp * P.row_chunks;
-  const int v0 = blockIdx.x * NV;
+
+  // ---- (vocab tile, row chunk, stage) from the XCD-aware 1-D grid ---------
+  const int per_grp = P.nvt_pad * P.row_chunks;
+  const int grp = blockIdx.x / per_grp;
+  const int id = blockIdx.x - grp * per_grp;
+  const int super = id / (kXcds * P.row_chunks);
+  const int rem = id - super * kXcds * P.row_chunks;
+  const int rc = rem / kXcds;
+  const int vt = super * kXcds + (rem - rc * kXcds);
+  if (vt >= P.nvt) return;
+  const int v0 = vt * NV;
 
   // ---- rows of this stage, chunk rc (batch order) ---------------------------
   int n_rows;
@@ -50,7 +72,7 @@ __global__ __launch_bounds__(256) void head_mfma_kernel(HeadP P) {
     if (tid < kRowsPerWG) s_rows[tid] = min(rc * kRowsPerWG + tid, P.M - 1);
     __syncthreads();
   } else {
-    const int per = (P.M + 255) / 256;
+    const int per = (P.M + kThreads - 1) / kThreads;
     const int r0 = tid * per;
     int cnt = 0;
     for (int k = 0; k < per; ++k) {
@@ -61,8 +83,11 @@ __global__ __launch_bounds__(256) void head_mfma_kernel(HeadP P) {
     if (lane == 63) s_cnt[w] = incl;
     __syncthreads();
     int rank = incl - cnt;
-    for (int i = 0; i < w; ++i) rank += s_cnt[i];
-    const int total = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    int total = 0;
+    for (int i = 0; i < kSplitK; ++i) {
+      rank += i < w ? s_cnt[i] : 0;
+      total += s_cnt[i];
+    }
     for (int k = 0; k < per; ++k) {
       int r = r0 + k;
       if (r < P.M && clampi(P.head_id[r], 0, P.G - 1) == grp) {
@@ -81,72 +106,264 @@ __global__ __launch_bounds__(256) void head_mfma_kernel(HeadP P) {
   const int n_rt = (n_rows + 15) >> 4;
 
   const uint16_t* __restrict__ Wg = P.W[grp];
-  const int kq = P.d >> 2;              // k range per wave
+  const int kq = P.d / kSplitK;         // k range per wave
   const int kb = w * kq;
+  const int nk = kq >> 5;               // k-steps of 32 per wave
   const int l16 = lane & 15, lg = lane >> 4;
 
   const uint16_t* aptr[VT];
 #pragma unroll
-  for (int vt = 0; vt < VT; ++vt) {
-    const int v = min(v0 + vt * 16 + l16, P.V - 1);
-    aptr[vt] = Wg + (size_t)v * P.d + kb + lg * 8;
+  for (int vt_ = 0; vt_ < VT; ++vt_) {
+    const int v = min(v0 + vt_ * 16 + l16, P.V - 1);
+    aptr[vt_] = Wg + (size_t)v * P.d + kb + lg * 8;
   }
-  const uint16_t* bptr[4];
+  // RT row tiles are loaded every k-step (rows past n_rows repeat a valid
+  // row); only the products are skipped for row tiles past n_rt.
+  const uint16_t* bptr[RT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) bptr[rt] = P.h + (size_t)s_rows[rt * 16 + l16] * P.d + kb + lg * 8;
+  for (int rt = 0; rt < RT; ++rt) bptr[rt] = P.h + (size_t)s_rows[rt * 16 + l16] * P.d + kb + lg * 8;
 
-  f32x4_t acc[VT][4];
+  f32x4_t acc[VT][RT];
 #pragma unroll
-  for (int vt = 0; vt < VT; ++vt)
+  for (int vt_ = 0; vt_ < VT; ++vt_)
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) acc[vt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RT; ++rt) acc[vt_][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8_t a[VT], bb[4];
+  bf16x8_t a[kRing][VT], bb[kRing][RT];
+  // loads of k-step ks (clamped to the last one) into ring slot s
+  auto issue = [&](int ks, int s) {
+    const int k = min(ks, nk - 1) << 5;
 #pragma unroll
-  for (int vt = 0; vt < VT; ++vt) a[vt] = *reinterpret_cast<const bf16x8_t*>(aptr[vt]);
+    for (int vt_ = 0; vt_ < VT; ++vt_) a[s][vt_] = *reinterpret_cast<const bf16x8_t*>(aptr[vt_] + k);
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-    if (rt < n_rt) bb[rt] = *reinterpret_cast<const bf16x8_t*>(bptr[rt]);
+    for (int rt = 0; rt < RT; ++rt) bb[s][rt] = *reinterpret_cast<const bf16x8_t*>(bptr[rt] + k);
+  };
+  // all RT row tiles are multiplied (tiles past n_rt hold repeated rows
+  // whose results are never stored), so the steady-state loop is branch-free
+  auto mma = [&](int s) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int vt_ = 0; vt_ < VT; ++vt_)
+        acc[vt_][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][vt_], bb[s][rt], acc[vt_][rt], 0, 0, 0);
+  };
 
-  for (int k = 0; k < kq; k += 32) {
-    bf16x8_t na[VT], nb[4];
-    if (k + 32 < kq) {
-#pragma unroll
-      for (int vt = 0; vt < VT; ++vt) na[vt] = *reinterpret_cast<const bf16x8_t*>(aptr[vt] + k + 32);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        if (rt < n_rt) nb[rt] = *reinterpret_cast<const bf16x8_t*>(bptr[rt] + k + 32);
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      if (rt < n_rt) {
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt)
-          acc[vt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[vt], bb[rt], acc[vt][rt], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt) a[vt] = na[vt];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) bb[rt] = nb[rt];
+  issue(0, 0);
+  issue(1, 1);
+  int ks = 0;
+  for (; ks + 3 <= nk; ks += 3) {
+    issue(ks + 2, 2);
+    mma(0);
+    issue(ks + 3, 0);
+    mma(1);
+    issue(ks + 4, 1);
+    mma(2);
   }
+  // slots 0 and 1 now hold k-steps ks and ks+1 (clamped); finish the rest
+  if (ks < nk) mma(0);
+  if (ks + 1 < nk) mma(1);
 
   // ---- sum the four k-slices in wave order and store ------------------------
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    if (rt < n_rt) {
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int vt = 0; vt < VT; ++vt)
-        *reinterpret_cast<f32x4_t*>(&s_red[w][rt * 16 + l16][vt * 16 + lg * 4]) = acc[vt][rt];
-    }
-  }
+    for (int vt_ = 0; vt_ < VT; ++vt_)
+      *reinterpret_cast<f32x4_t*>(&s_red[w][rt * 16 + l16][vt_ * 16 + lg * 4]) = acc[vt_][rt];
   __syncthreads();
-  for (int e = tid; e < n_rows * NV; e += 256) {
+  for (int e = tid; e < n_rows * NV; e += kThreads) {
     const int rl = e / NV, vl = e - (e / NV) * NV;
     const int v = v0 + vl;
     if (v < P.V) {
       const float s = ((s_red[0][rl][vl] + s_red[1][rl][vl]) + s_red[2][rl][vl]) + s_red[3][rl][vl];
       P.logits[(size_t)s_rows[rl] * P.V + v] = s;
+    }
+  }
+}
+
+// Rows of stage grp that fall in row chunk rc (MR rows each, batch order) into
+// s_rows; slots past the last row repeat a valid row so loads stay in bounds.
+// Returns the chunk's row count (<= 0: nothing to do), the same in all lanes.
+template <int MR>
+__device__ __forceinline__ int gather_rows(const HeadP& P, int grp, int rc, int* s_rows, int* s_cnt,
+                                           int tid, int lane, int w) {
+  int n_rows;
+  if (P.G == 1) {
+    n_rows = min(MR, P.M - rc * MR);
+    for (int i = tid; i < MR; i += 256) s_rows[i] = min(rc * MR + i, P.M - 1);
+    __syncthreads();
+  } else {
+    const int per = (P.M + 255) / 256;
+    const int r0 = tid * per;
+    int cnt = 0;
+    for (int k = 0; k < per; ++k) {
+      const int r = r0 + k;
+      if (r < P.M && clampi(P.head_id[r], 0, P.G - 1) == grp) ++cnt;
+    }
+    const int incl = wave_incl_scan_i(cnt, lane);
+    if (lane == 63) s_cnt[w] = incl;
+    __syncthreads();
+    int rank = incl - cnt;
+    for (int i = 0; i < w; ++i) rank += s_cnt[i];
+    const int total = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    for (int k = 0; k < per; ++k) {
+      const int r = r0 + k;
+      if (r < P.M && clampi(P.head_id[r], 0, P.G - 1) == grp) {
+        const int slot = rank - rc * MR;
+        if (slot >= 0 && slot < MR) s_rows[slot] = r;
+        ++rank;
+      }
+    }
+    n_rows = min(MR, total - rc * MR);
+    __syncthreads();
+    for (int i = tid; i < MR; i += 256)
+      if (n_rows > 0 && i >= n_rows) s_rows[i] = s_rows[0];
+    __syncthreads();
+  }
+  return uniform(n_rows);
+}
+
+// 16 bytes per lane from global memory straight into LDS (no registers):
+// lane l's bytes land at lds_byte_addr + 16 l, lds_byte_addr being wave-uniform
+// (M0).  The compiler does not see these loads; waits for them are explicit
+// s_waitcnt vmcnt(n) (vmcnt retires in issue order, so the compiler's own
+// waits stay correct, only more conservative).
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_byte_addr) : "memory");
+}
+// s_waitcnt with only vmcnt = n (0..63) constrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Many rows, LDS fed by DMA: S LDS stages of one 64-k chunk each, holding NV
+// codebook rows then MR h rows (128 bytes per row, the 16-byte pieces
+// XOR-swizzled by row so the operand reads are bank-conflict free).  Each
+// wave's DMA instruction fills 8 whole rows (1 KiB), lane l taking the piece
+// that belongs in slot l % 8.  S - 1 chunks are in flight while one is
+// multiplied; one barrier per chunk.  Waves are laid out 2 (entries) x 2
+// (rows); each owns NV/2 entries x MR/2 rows and writes its logits directly.
+template <int NV, int MR, int S>
+__global__ __launch_bounds__(256) void head_dma_kernel(HeadP P) {
+  constexpr int KC = 64;                      // k per chunk
+  constexpr int ROWS = NV + MR;               // LDS rows per stage
+  constexpr int STAGE = ROWS * KC;            // bf16 elements per stage
+  constexpr int NI = ROWS / 32;               // DMA instructions per wave per chunk
+  constexpr int VTW = NV / 32, RTW = MR / 32; // 16-wide tiles per wave
+  static_assert(S >= 2 && (S - 2) * NI < 64, "pipeline depth");
+  __shared__ int s_rows[MR];
+  __shared__ int s_cnt[4];
+  __shared__ __attribute__((aligned(1024))) uint16_t s_buf[S * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int per_grp = P.nvt_pad * P.row_chunks;
+  const int grp = blockIdx.x / per_grp;
+  const int id = blockIdx.x - grp * per_grp;
+  const int super = id / (kXcds * P.row_chunks);
+  const int rem = id - super * kXcds * P.row_chunks;
+  const int rc = rem / kXcds;
+  const int vt = super * kXcds + (rem - rc * kXcds);
+  if (vt >= P.nvt) return;
+  const int v0 = vt * NV;
+  const int n_rows = gather_rows<MR>(P, grp, rc, s_rows, s_cnt, tid, lane, w);
+  if (n_rows <= 0) return;
+
+  const uint16_t* __restrict__ Wg = P.W[grp];
+  const int nch = P.d / KC;
+  // DMA instruction j of wave w fills rows 8g..8g+7, g = 4 j + w; lane l reads
+  // row 8g + l/8, piece (l % 8) ^ (l / 8) (row & 7 == l / 8).
+  const uint16_t* src[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int R = 8 * (4 * j + w) + (lane >> 3);
+    const int piece = (lane & 7) ^ (lane >> 3);
+    const uint16_t* row = R < NV ? Wg + (size_t)min(v0 + R, P.V - 1) * P.d
+                                 : P.h + (size_t)s_rows[R - NV] * P.d;
+    src[j] = row + piece * 8;
+  }
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(s_buf);
+  auto issue = [&](int chunk, int stage) __attribute__((always_inline)) {
+    const uint32_t base = lds0 + (uint32_t)(stage * STAGE * 2);
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      dma16(src[j] + chunk * KC, uniform(base + (uint32_t)((4 * j + w) * 1024)));
+  };
+
+  const int wv = w & 1, wr = w >> 1;
+  const int l16 = lane & 15, lg = lane >> 4;
+  int aoff[VTW][2], boff[RTW][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int c = 4 * s + lg;
+#pragma unroll
+    for (int t = 0; t < VTW; ++t) {
+      const int R = (NV / 2) * wv + 16 * t + l16;
+      aoff[t][s] = R * KC + ((c ^ (R & 7)) << 3);
+    }
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      const int R = NV + wr * (MR / 2) + 16 * t + l16;
+      boff[t][s] = R * KC + ((c ^ (R & 7)) << 3);
+    }
+  }
+  f32x4_t acc[VTW][RTW];
+#pragma unroll
+  for (int a = 0; a < VTW; ++a)
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) acc[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int stage) __attribute__((always_inline)) {
+    const uint16_t* sb = s_buf + stage * STAGE;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8_t A[VTW], Bm[RTW];
+#pragma unroll
+      for (int t = 0; t < VTW; ++t) A[t] = *reinterpret_cast<const bf16x8_t*>(sb + aoff[t][s]);
+#pragma unroll
+      for (int t = 0; t < RTW; ++t) Bm[t] = *reinterpret_cast<const bf16x8_t*>(sb + boff[t][s]);
+#pragma unroll
+      for (int t = 0; t < RTW; ++t)
+#pragma unroll
+        for (int a = 0; a < VTW; ++a)
+          acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[a], Bm[t], acc[a][t], 0, 0, 0);
+    }
+  };
+
+  // Chunk c lives in stage c % S.  At the top of iteration i, chunks
+  // i+1 .. i+S-2 may still be in flight ((S-2)*NI loads of this wave); near
+  // the end fewer were issued, so wait for all.  The barrier then also
+  // retires every wave's reads of stage (i-1) % S, which is refilled next.
+#pragma unroll
+  for (int c = 0; c < S - 1; ++c)
+    if (c < nch) issue(c, c);
+  int stage = 0;
+  for (int i = 0; i < nch; ++i) {
+    if (i + S - 2 < nch) wait_vmcnt<(S - 2) * NI>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (i + S - 1 < nch) issue(i + S - 1, stage == 0 ? S - 1 : stage - 1);
+    compute(stage);
+    stage = stage == S - 1 ? 0 : stage + 1;
+  }
+
+#pragma unroll
+  for (int t = 0; t < RTW; ++t) {
+    const int R = wr * (MR / 2) + 16 * t + l16;
+    if (R < n_rows) {
+      float* orow = P.logits + (size_t)s_rows[R] * P.V;
+#pragma unroll
+      for (int a = 0; a < VTW; ++a) {
+        const int v = v0 + (NV / 2) * wv + 16 * a + 4 * lg;
+        if (v + 3 < P.V) {
+          *reinterpret_cast<f32x4_t*>(orow + v) = acc[a][t];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (v + e < P.V) orow[v + e] = acc[a][t][e];
+        }
+      }
     }
   }
 }
@@ -192,16 +409,37 @@ hipError_t launch_codebook_head(const HeadArgs& a, hipStream_t s) {
     P.head_id = a.head_id;
     P.logits = a.logits;
     P.G = a.G; P.M = a.M; P.d = a.d; P.V = a.V;
-    P.row_chunks = (a.M + kRowsPerWG - 1) / kRowsPerWG;
-    // Enough workgroups to cover the chip: 64-entry tiles when that already
-    // gives >= 512 workgroups, else 32-entry tiles.
-    const long wg64 = (long)((a.V + 63) / 64) * a.G * P.row_chunks;
-    if (wg64 >= 512) {
-      dim3 grid((a.V + 63) / 64, a.G * P.row_chunks);
-      hipLaunchKernelGGL(head_mfma_kernel<4>, grid, dim3(256), 0, s, P);
+    if (a.M > kRowsPerWG) {
+      // many rows: LDS-staged tiles of 128 rows and 128 entries, or 64
+      // entries when 128 would leave CUs without a workgroup
+      P.row_chunks = (a.M + 127) / 128;
+      const bool wide = (long)((a.V + 127) / 128) * P.row_chunks * a.G >= 256;
+      const int nv = wide ? 128 : 64;
+      P.nvt = (a.V + nv - 1) / nv;
+      P.nvt_pad = (P.nvt + kXcds - 1) / kXcds * kXcds;
+      const dim3 g((unsigned)((long)P.nvt_pad * P.row_chunks * a.G));
+      if (wide) hipLaunchKernelGGL((head_dma_kernel<128, 128, 4>), g, dim3(256), 0, s, P);
+      else hipLaunchKernelGGL((head_dma_kernel<64, 128, 4>), g, dim3(256), 0, s, P);
+      return hipGetLastError();
+    }
+    P.row_chunks = 1;
+    // 64-entry tiles when that already gives >= 512 workgroups, else 32.
+    const bool wide = (long)((a.V + 63) / 64) * a.G >= 512;
+    const int nv = wide ? 64 : 32;
+    P.nvt = (a.V + nv - 1) / nv;
+    P.nvt_pad = (P.nvt + kXcds - 1) / kXcds * kXcds;
+    const long grid = (long)P.nvt_pad * P.row_chunks * a.G;
+    // row tiles per workgroup: enough for the rows (<= 64)
+    const int rt = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
+    const dim3 g((unsigned)grid), b(kThreads);
+    if (wide) {
+      if (rt == 1) hipLaunchKernelGGL((head_mfma_kernel<4, 1>), g, b, 0, s, P);
+      else if (rt == 2) hipLaunchKernelGGL((head_mfma_kernel<4, 2>), g, b, 0, s, P);
+      else hipLaunchKernelGGL((head_mfma_kernel<4, 4>), g, b, 0, s, P);
     } else {
-      dim3 grid((a.V + 31) / 32, a.G * P.row_chunks);
-      hipLaunchKernelGGL(head_mfma_kernel<2>, grid, dim3(256), 0, s, P);
+      if (rt == 1) hipLaunchKernelGGL((head_mfma_kernel<2, 1>), g, b, 0, s, P);
+      else if (rt == 2) hipLaunchKernelGGL((head_mfma_kernel<2, 2>), g, b, 0, s, P);
+      else hipLaunchKernelGGL((head_mfma_kernel<2, 4>), g, b, 0, s, P);
     }
     return hipGetLastError();
   }

@@ -155,18 +155,23 @@ def test_codebook_head_isolated(clm_gpu, cfg):
 
 
 def test_codebook_head_ragged_rows(clm_gpu):
-    """Row counts that are not multiples of 16 or 64, a vocabulary that is not
-    a multiple of 64, and several row chunks per head."""
+    """Row counts that are not multiples of 16, 64 or 128, vocabularies that
+    are not multiples of the entry tile, several row chunks per head, one head
+    holding most rows, and d from 128 up."""
     rng = np.random.default_rng(5)
-    for M, V, G in [(1, 4096, 1), (17, 1000, 1), (70, 4096, 3), (130, 4160, 2)]:
-        d = 256
+    cases = [(1, 4096, 1, 256), (17, 1000, 1, 256), (70, 4096, 3, 256), (130, 4160, 2, 256),
+             (129, 1000, 1, 128), (300, 4160, 1, 384), (260, 20000, 1, 256),
+             (300, 4096, 2, 256)]
+    for M, V, G, d in cases:
         h = synth.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32))
         W = synth.f32_to_bf16_bits((rng.standard_normal((G, V, d)) * 0.05).astype(np.float32))
         hid = rng.integers(0, G, size=M).astype(np.int32)
+        if G == 2 and M == 300:
+            hid[:220] = 1                       # one head takes 220 of the rows
         logits = clm_gpu.codebook_head(to_torch(h, bf16=True), to_torch(W, bf16=True),
                                        to_torch(hid) if G > 1 else None)
         ref = oracle.codebook_head(synth.bf16_bits_to_f32(h), synth.bf16_bits_to_f32(W), hid)
-        check_close(logits.cpu().numpy(), ref, f"head M={M} V={V} G={G}")
+        check_close(logits.cpu().numpy(), ref, f"head M={M} V={V} G={G} d={d}")
 
 
 @pytest.mark.parametrize("cfg,scale", [(2, 1.0), (2, 4.0), (5, 1.0), (3, 1.0)])
