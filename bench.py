@@ -24,6 +24,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -34,7 +35,8 @@ if ROOT not in sys.path:
 METRIC = "codec decode steps/s (streams×tokens) and % HBM roofline of KV attention"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_c5_traffic.txt")
-ATTN_SRC = os.path.join(ROOT, "codec_language_model_amd", "csrc", "attention.hip")
+ATTN_SRCS = [os.path.join(ROOT, "codec_language_model_amd", "csrc", f) for f in ("attention.hip", "clm_device.h")]
+COPY_BYTES = 1 << 30
 
 
 def log(*a):
@@ -50,9 +52,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-streams", type=int, default=0,
                     help="streams in the oracle's timed sample (0 = the whole batch)")
-    ap.add_argument("--cpu-reps", type=int, default=3, help="oracle repetitions timed")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="the oracle is repeated over its sample until this much CPU time has passed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --copy-calibration run into the attention traffic record")
     return ap.parse_args()
 
 
@@ -65,12 +71,79 @@ def attention_bytes(cfg, kv_len):
     return kv + qo
 
 
+def attention_source_hash():
+    h = hashlib.sha256()
+    for f in ATTN_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def pmc_summary(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
+    """HBM bytes per decode_attention launch from two PMC runs.  FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) are averaged per kernel over its dispatches,
+    summed over the call's kernels (split pass and merge pass), and each scaled
+    by what the same counter reads for a plain 1 GiB device copy."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        copies = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            name = r["Kernel_Name"]
+            m = re.search(r"attn_\w+", name)
+            if m:
+                vals[m.group(0)].append(v)
+            elif "copyBuffer" in name and int(r["Grid_Size"]) >= 65536:
+                copies.append(v)
+        if not vals or not copies:
+            raise SystemExit(f"{path}: no attention dispatches or no 1 GiB copy for {counter}")
+        avg = {k: sum(v) / len(v) for k, v in vals.items()}
+        return avg, sum(copies) / len(copies)
+
+    f_avg, f_copy = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_avg, w_copy = per_kernel(write_csv, "WRITE_SIZE")
+    # a 1 GiB copy reads and writes 1 GiB = 1048576 KiB
+    f_scale = (COPY_BYTES / 1024) / f_copy
+    w_scale = (COPY_BYTES / 1024) / w_copy
+    fetch = sum(f_avg.values()) * f_scale * 1024
+    write = sum(w_avg.values()) * w_scale * 1024
+    lines = [
+        "# HBM traffic of one decode_attention call (its split pass and merge pass),",
+        "# 256 streams, 16/8 heads, head_dim 128, bf16, log-uniform KV lengths in [64, 8192].",
+        "# Counters from two runs of",
+        "#   rocprofv3 --pmc FETCH_SIZE -d <dir> -o f -- python3 bench.py --steps 3 --warmup 1 "
+        "--no-cpu-baseline --copy-calibration",
+        "#   rocprofv3 --pmc WRITE_SIZE -d <dir> -o w -- python3 bench.py --steps 3 --warmup 1 "
+        "--no-cpu-baseline --copy-calibration",
+        "# reduced by: python3 bench.py --pmc-summary <dir>/f_counter_collection.csv "
+        "<dir>/w_counter_collection.csv",
+        "# Each counter is scaled by its reading for a plain 1 GiB device-to-device copy.",
+    ]
+    for k in sorted(f_avg):
+        lines.append(f"# {k}: FETCH_SIZE {f_avg[k]:.1f} KiB, WRITE_SIZE {w_avg.get(k, 0.0):.1f} KiB per dispatch")
+    lines += [
+        f"# 1 GiB copy: FETCH_SIZE {f_copy:.1f} KiB, WRITE_SIZE {w_copy:.1f} KiB per dispatch",
+        f"attention_source_sha256_16 = {attention_source_hash()}",
+        f"fetch_scale = {f_scale:.4f}",
+        f"write_scale = {w_scale:.4f}",
+        f"hbm_fetch_bytes_per_launch = {fetch:.0f}",
+        f"hbm_write_bytes_per_launch = {write:.0f}",
+        f"hbm_bytes_per_launch = {fetch + write:.0f}",
+    ]
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_for_current_kernel():
     """HBM bytes per attention launch measured by rocprofv3 PMC counters, if
     the record was taken on the current attention source; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+    src_hash = attention_source_hash()
     vals = {}
     for line in open(TRAFFIC_FILE):
         if "=" in line and not line.lstrip().startswith("#"):
@@ -84,10 +157,10 @@ def traffic_for_current_kernel():
         return None
 
 
-def cpu_baseline(x, n_streams, reps=1):
+def cpu_baseline(x, n_streams, min_seconds):
     """The oracle, as it stands, on n_streams streams spread over the length
     distribution (all of them when n_streams is 0 or >= B): attention, head
-    and token choice per stream, repeated reps times."""
+    and token choice per stream, repeated until min_seconds have passed."""
     import numpy as np
 
     import oracle
@@ -102,9 +175,11 @@ def cpu_baseline(x, n_streams, reps=1):
     W = x.f32(x.W)
     scale = 1.0 / math.sqrt(c.D)
     t0 = time.perf_counter()
-    for _ in range(reps):
+    reps = 0
+    while reps == 0 or time.perf_counter() - t0 < min_seconds:
         oracle.decode_step(q, keys, vals, x.kv_len, scale, c.H_kv, W, x.head_id if c.G > 1 else None,
                            c.dtype == "bf16", streams=streams)
+        reps += 1
     dt = time.perf_counter() - t0
     threads = os.cpu_count()
     try:
@@ -125,6 +200,9 @@ def cpu_baseline(x, n_streams, reps=1):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only: the decode step shards by stream with no exchange, "
@@ -183,45 +261,48 @@ def main():
         num_em = torch.empty(c.B, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-
-    def step(timed):
-        if timed:
+    def step(ev=None):
+        if ev is not None:
             ev[0].record()
         clm.kv_cache_append(k_new, v_new, k_cache, v_cache, bt, len_before, block_size=c.block_size)
-        if timed:
+        if ev is not None:
             ev[1].record()
         clm.decode_attention(q, k_cache, v_cache, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
-        if timed:
+        if ev is not None:
             ev[2].record()
         clm.codebook_head(o.view(c.M, c.d_model), W, head_id, out=logits)
-        if timed:
+        if ev is not None:
             ev[3].record()
         if spec is not None:
             clm.spec_verify(logits.view(c.B, c.Kq, c.V), *spec, c.temperature, out_tokens=out_tok,
                             num_emitted=num_em)
         else:
             clm.sample_or_argmax(logits, temp, uni, out=tokens)
-        if timed:
+        if ev is not None:
             ev[4].record()
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
 
-    # whole-step throughput: K steps, no per-call events inside
+    # whole-step throughput: K steps back to back, no events inside
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(False)
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-call durations: the same K steps again, with events between calls
+    # per-call durations: the same K steps again with HIP events between the
+    # calls, recorded on the stream the kernels run on (torch's current stream)
+    # and read after one synchronisation at the end, so the host stays ahead of
+    # the GPU and no launch gap is timed
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     per = np.zeros(4)
-    for _ in range(args.steps):
-        step(True)
-        torch.cuda.synchronize()
-        per += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    for e in evs:
+        per += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
     per_us = per / args.steps * 1e3
 
     ms_per_step = wall / args.steps * 1e3
@@ -246,7 +327,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
-        cpu = cpu_baseline(x, args.cpu_streams, args.cpu_reps)
+        cpu = cpu_baseline(x, args.cpu_streams, args.cpu_seconds)
         log(f"[bench] cpu oracle: {cpu['value']:.2f} {cpu['unit']} ({cpu['sample']})")
 
     head_flops = 2.0 * c.M * c.d_model * c.V
