@@ -64,14 +64,41 @@ __device__ __forceinline__ int block_max_int(int x, Scratch& sc) {
   return max(max(sc.ri[0], sc.ri[1]), max(sc.ri[2], sc.ri[3]));
 }
 
-// Lowest index of the largest value among x[0:n].
+// Lowest index of the largest value among x[0:n].  Each thread scans its
+// entries in increasing index order (strict >, so its first occurrence wins),
+// then (value, index) pairs are reduced with ties going to the lower index.
+// When the row is 16-byte aligned the scan reads float4s, eight of them in
+// flight per thread before any is compared, so a row streams at memory rate.
 __device__ int block_argmax(const float* __restrict__ x, int n, Scratch& sc) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < n; i += kT) {
+  int done = 0;
+  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+    constexpr int U = 8;
+    const int n4 = n >> 2;
+    const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x);
+    for (int j0 = 0; j0 < n4; j0 += kT * U) {
+      float4 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int j = j0 + k * kT + tid;
+        v[k] = j < n4 ? x4[j] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int i = (j0 + k * kT + tid) * 4;
+        if (v[k].x > bv) { bv = v[k].x; bi = i; }
+        if (v[k].y > bv) { bv = v[k].y; bi = i + 1; }
+        if (v[k].z > bv) { bv = v[k].z; bi = i + 2; }
+        if (v[k].w > bv) { bv = v[k].w; bi = i + 3; }
+      }
+    }
+    done = n4 * 4;
+  }
+  for (int i = done + tid; i < n; i += kT) {
     const float v = x[i];
-    if (v > bv) { bv = v; bi = i; }  // i increases: first occurrence wins
+    if (v > bv) { bv = v; bi = i; }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -87,6 +114,30 @@ __device__ int block_argmax(const float* __restrict__ x, int n, Scratch& sc) {
   for (int i = 1; i < 4; ++i)
     if (sc.rf[i] > bv || (sc.rf[i] == bv && sc.ri[i] < bi)) { bv = sc.rf[i]; bi = sc.ri[i]; }
   return bi == 0x7fffffff ? 0 : bi;
+}
+
+// Largest of x[0:n], with the same float4 streaming as block_argmax.
+__device__ float block_row_max(const float* __restrict__ x, int n, Scratch& sc) {
+  float mx = -INFINITY;
+  int done = 0;
+  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+    constexpr int U = 8;
+    const int n4 = n >> 2;
+    const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x);
+    for (int j0 = 0; j0 < n4; j0 += kT * U) {
+      float4 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int j = j0 + k * kT + threadIdx.x;
+        v[k] = j < n4 ? x4[j] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) mx = fmaxf(mx, fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w)));
+    }
+    done = n4 * 4;
+  }
+  for (int i = done + threadIdx.x; i < n; i += kT) mx = fmaxf(mx, x[i]);
+  return block_max(mx, sc);
 }
 
 // min{ i : u*S < w_0 + ... + w_i } over i < n for the weights wf(i) >= 0, S
@@ -176,9 +227,7 @@ __global__ __launch_bounds__(kT) void sample_kernel(SampleArgs P) {
   if (!(T > 0.f)) {
     tok = block_argmax(x, n, sc);
   } else {
-    float mx = -INFINITY;
-    for (int i = threadIdx.x; i < n; i += kT) mx = fmaxf(mx, x[i]);
-    mx = block_max(mx, sc);
+    const float mx = block_row_max(x, n, sc);
     const float m = mx / T;
     const float u = P.uniforms[r];
     tok = block_inverse_cdf(n, u, [&](int i) { return expf(x[i] / T - m); }, sc);
@@ -200,9 +249,7 @@ __global__ __launch_bounds__(kT) void verify_kernel(VerifyArgs P) {
     const int xt = clampi(P.draft_tokens[row], 0, V - 1);
     const float qx = q[xt];
     if (T > 0.f) {
-      float mx = -INFINITY;
-      for (int j = threadIdx.x; j < V; j += kT) mx = fmaxf(mx, x[j]);
-      mx = block_max(mx, sc);
+      const float mx = block_row_max(x, V, sc);
       const float m = mx / T;
       float s = 0.f;
       for (int j = threadIdx.x; j < V; j += kT) s += expf(x[j] / T - m);

@@ -222,6 +222,32 @@ def test_sampler_closed_forms(clm_gpu):
     assert int(t0.cpu()[0]) == 3000
 
 
+def test_argmax_ties_alignment_and_tails(clm_gpu):
+    """Greedy rows whose maximum is planted at two or three positions (the
+    lowest must win), rows that are not 16-byte aligned (ld not a multiple of
+    4), vocabularies that are not multiples of 4 or shorter than 4, and masks
+    that cut between the planted positions."""
+    rng = np.random.default_rng(11)
+    for V, ld in [(1, 1), (3, 3), (5, 8), (1003, 1003), (4096, 4099), (16384, 16384), (16387, 16388)]:
+        M = 9
+        x = rng.standard_normal((M, ld)).astype(np.float32)
+        for r in range(M):
+            pos = rng.choice(V, size=min(3, V), replace=False)
+            x[r, pos] = np.float32(10.0 + (r % 2))
+        if V >= 8:
+            x[0, V - 1] = 50.0                 # maximum in the last entry (scalar tail when V % 4)
+            x[1, 0] = 50.0                     # ... and in the first
+        lt = to_torch(x)[:, :V]
+        got = clm_gpu.sample_or_argmax(lt).cpu().numpy()
+        want = [oracle.argmax_token(x[r, :V]) for r in range(M)]
+        assert got.tolist() == want, (V, ld, got.tolist(), want)
+        vv = rng.integers(1, V + 1, size=M).astype(np.int32)
+        got = clm_gpu.sample_or_argmax(lt, to_torch(np.zeros(M, np.float32)), to_torch(np.zeros(M, np.float32)),
+                                       to_torch(vv)).cpu().numpy()
+        want = [oracle.argmax_token(x[r, :V], vv[r]) for r in range(M)]
+        assert got.tolist() == want, (V, ld, "masked", got.tolist(), want)
+
+
 def _spec_inputs_torch(s):
     return (to_torch(s["draft_probs"]), to_torch(s["draft_tokens"]), to_torch(s["u_accept"]),
             to_torch(s["u_resample"]))
