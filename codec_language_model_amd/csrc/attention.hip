@@ -24,10 +24,12 @@
 // pages are fetched once, one per lane, and picked out with readlane.  Keys
 // are read as 16-byte loads, LPR lanes per key row (16 lanes per 256-byte row
 // for bf16, D = 128), so one load instruction covers 4 whole rows; the LPR
-// partial dot products are summed with DPP inside the 16-lane row.  Values
-// are stored transposed inside a block ([D][bs]), so for each of its head
-// dimensions a lane reads the run of keys its group scored, contiguous across
-// the wave.  The loop body covers two tiles without a branch: while one tile
+// partial dot products are summed with DPP inside the 16-lane row.  K and V
+// are read with non-temporal loads: every byte is used once per call, and on
+// gfx950 that policy streams scattered 4 KiB pages faster than the default.
+// Values are stored transposed inside a block ([D][bs]), so for each of its
+// head dimensions a lane reads the run of keys its group scored, contiguous
+// across the wave.  The loop body covers two tiles without a branch: while one tile
 // buffer is computed the other's loads are in flight (past the last tile the
 // loads re-read it, which hits in cache, and the tile is masked), so the wait
 // counts stay exact.  Each 16-lane key group keeps its own online-softmax
@@ -155,11 +157,11 @@ __device__ __forceinline__ int find_stream(const int* s, int B, int u) {
 }
 
 // The streams whose last split is shorter than `split`, ordered by that
-// split's tile count (1..16) descending, then by stream index: s[0..n).  A
-// counting sort with one block-wide scan per tile count, so every workgroup
-// builds the same list.  tiles(b) = 0 means no short split.  Returns n.
+// split's length bin (1..16, 16 = longest) descending, then by stream index:
+// s[0..n).  A counting sort with one block-wide scan per bin, so every
+// workgroup builds the same list.  bin(b) = 0 means no short split.  Returns n.
 template <class F>
-__device__ int short_splits_sorted(int* s, int (*s_bins)[16], int B, F tiles) {
+__device__ int short_splits_sorted(int* s, int (*s_bins)[16], int B, F bin) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per = (B + kThreads - 1) / kThreads;
   const int b0 = tid * per;
@@ -168,7 +170,7 @@ __device__ int short_splits_sorted(int* s, int (*s_bins)[16], int B, F tiles) {
   for (int k = 0; k < 16; ++k) cnt[k] = 0;
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
-    const int t = b < B ? tiles(b) : 0;
+    const int t = b < B ? bin(b) : 0;
 #pragma unroll
     for (int k = 0; k < 16; ++k) cnt[k] += (t == 16 - k);
   }
@@ -195,7 +197,7 @@ __device__ int short_splits_sorted(int* s, int (*s_bins)[16], int B, F tiles) {
   n = start;
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
-    const int t = b < B ? tiles(b) : 0;
+    const int t = b < B ? bin(b) : 0;
     if (t > 0) {
 #pragma unroll
       for (int k = 0; k < 16; ++k)
@@ -235,9 +237,11 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
   for (int b = tid; b < P.B; b += kThreads) s_len[b] = stream_len(P.kv_len[b], P);
   __syncthreads();
   block_prefix(s_full, s_wsum, P.B, [&](int b) { return full_splits(s_len[b], P); });
+  // short last splits, binned by length in sixteenths of a split
+  const int tps = P.split >> 4;
   const int n_part = short_splits_sorted(s_plist, s_bins, P.B, [&](int b) {
     const int rem = s_len[b] - full_splits(s_len[b], P) * P.split;
-    return rem > 0 ? (rem + 15) >> 4 : 0;
+    return rem > 0 ? (((rem + 15) >> 4) * 16 + tps - 1) / tps : 0;
   });
   const int n_full = s_full[P.B] * P.H_kv;
   const int total_items = n_full + n_part * P.H_kv;
@@ -332,10 +336,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
       for (int i = 0; i < KPG; ++i)
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc)
-          kr[i][cc] = *reinterpret_cast<const uint4*>(kp + i * D + cc * LPR * VE);
+          kr[i][cc] = ld_nt(reinterpret_cast<const uint4*>(kp + i * D + cc * LPR * VE));
 #pragma unroll
       for (int jj = 0; jj < DPL; ++jj)
-        vr[jj] = *reinterpret_cast<const VT*>(vp + (size_t)jj * LPR * bs);
+        vr[jj] = ld_nt(reinterpret_cast<const VT*>(vp + (size_t)jj * LPR * bs));
     };
 
     // P.V for one tile; MASK zeroes value lanes of keys past `vis` (slots

@@ -92,6 +92,27 @@ __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
   return x;
 }
 
+// ---- streaming loads ----------------------------------------------------------
+// Non-temporal global loads (the nt bit): for data read once per call (the
+// KV cache, head weights, logits).  On gfx950 they sustain a higher HBM read
+// rate than default-policy loads on scattered 4 KiB pages.
+typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned nt_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_nt(const uint2* p) {
+  const nt_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ld_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float4 ld_nt(const float4* p) {
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }

@@ -136,9 +136,11 @@ size_t clm_decode_attention_workspace_size(int B, int Kq, int H_q, int H_kv, int
  *              no initial contents are needed.  Calls that share a workspace
  *              must be ordered on one stream.
  * Arithmetic: fp32 dot products, exponentials, online softmax and
- * accumulation; o rounded to dt once.  Streams longer than one split are
- * merged by a second kernel in split order, so results are the same from run
- * to run and do not depend on the order in which workgroups finish.
+ * accumulation; o rounded to dt once.  Splits are fixed token ranges of each
+ * stream; streams longer than one split are merged by a second kernel in
+ * split order, so results are the same from run to run and do not depend on
+ * the order in which workgroups finish, nor on the other streams of the
+ * batch.
  * Errors: INVALID_ARG (null, sizes < 1, H_q % H_kv != 0, max_kv_len < Kq,
  *   scale not finite), UNSUPPORTED (D not 64/128, G*Kq > 16, B > 4096,
  *   B*H_kv > 65536, block_size as for append, unknown dt), WORKSPACE (too
@@ -160,8 +162,9 @@ int clm_decode_attention(const void* q, const void* k_cache, const void* v_cache
  *   head_id  [M] int32 in [0, G), or NULL when G == 1
  *   logits   [M, V] float32           output
  * Each W_g is streamed from memory once per call for up to 64 rows of its
- * group (more rows: once per 64-row chunk).  Arithmetic: products of dt
- * values accumulated in fp32.
+ * group; more rows are taken in chunks of 128 whose workgroups read the same
+ * W tile close together in time, so it comes from memory about once.
+ * Arithmetic: products of dt values accumulated in fp32.
  * Errors: INVALID_ARG (null, sizes < 1, G > 8, head_id NULL with G > 1,
  *   h or a W not 16-byte aligned), UNSUPPORTED (bf16 with d % 128 != 0, f32
  *   with d % 4 != 0, M > 65536, unknown dt).
