@@ -110,7 +110,7 @@ def test_decode_attention_split_plan_and_batch_order(clm_gpu, cfg):
     d = Dev(x, include_new=True)
     scale = 1.0 / math.sqrt(x.cfg.D)
     o = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len, scale=scale)
-    loose = 8 * d.max_kv_len
+    loose = 3 * d.max_kv_len
     assert clm_gpu.decode_attention_workspace_size(x.cfg.B, 1, 16, 8, 128, loose) != \
         clm_gpu.decode_attention_workspace_size(x.cfg.B, 1, 16, 8, 128, d.max_kv_len)
     o_big = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, loose, scale=scale)
