@@ -113,8 +113,9 @@ def test_workspace_size_query(lib):
     small = f(16, 1, 16, 8, 128, 1500)
     big = f(256, 1, 16, 8, 128, 8192)
     assert 0 < small < big
-    # (m, l) + accumulators for every (stream, KV head, split, row)
-    assert big >= 256 * 8 * 32 * 2 * 130 * 4
+    # (m, l) + accumulators for every (stream, KV head, split, row): at 256
+    # streams of up to 8192 keys a split is 1024 tokens, so 8 splits
+    assert big >= 256 * 8 * 8 * 2 * 130 * 4
     assert f(4096, 1, 16, 32, 128, 100) == 0            # more than 65536 (stream, KV head) pairs
 
 
