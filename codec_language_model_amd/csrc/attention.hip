@@ -518,6 +518,214 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
   }
 }
 
+// Matrix-core variant for bf16 blocks of up to 16 query rows per KV head (a
+// verification block of K drafted positions times the GQA group).  Same work
+// items and item order as attn_split_kernel; per 16-token tile:
+//   S[t][r]  = sum_d K[t][d] q[r][d]      four (D/32) v_mfma_f32_16x16x32_bf16,
+//              A = K (16 tokens x 32 dims), B = q (32 dims x 16 rows)
+//   online softmax per row r on S; lane l holds tokens 4*(l/16)..+3 of row
+//   l%16, so a row's max needs two cross-lane steps and its sum none (lanes
+//   keep partial sums, added at the end of the item)
+//   O^T[e][r] += sum_t V[t][e] P[r][t]    eight (D/16) v_mfma_f32_16x16x16_bf16,
+//              A = V^T (16 dims x 16 tokens: the transposed value block gives
+//              each lane 4 consecutive tokens of one dim, one 8-byte load),
+//              B = P^T (16 tokens x 16 rows: exactly the layout S came out in)
+// Per lane: 4 score, D/2 accumulator and D/8 query registers, whatever the
+// row count, where the vector kernel needs NR*D/16 accumulators per lane.
+template <int D, int NR, int BS>
+__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(KParams P) {
+  typedef short bf16x4s __attribute__((ext_vector_type(4)));
+  constexpr int NS = D / 32;   // score MFMAs per tile
+  constexpr int NJ = D / 16;   // value MFMAs per tile
+  static_assert(NR <= 16, "one MFMA column block of query rows");
+
+  __shared__ int s_full[kMaxB + 1];
+  __shared__ int s_plist[kMaxB];
+  __shared__ int s_bins[kWaves][16];
+  __shared__ int s_len[kMaxB];
+  __shared__ int s_wsum[kWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int bs = BS ? BS : P.bs;
+  const int nrow = P.nr;
+
+  const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(P.q);
+  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(P.kc);
+  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(P.vc);
+  uint16_t* __restrict__ op = static_cast<uint16_t*>(P.o);
+
+  for (int b = tid; b < P.B; b += kThreads) s_len[b] = stream_len(P.kv_len[b], P);
+  __syncthreads();
+  block_prefix(s_full, s_wsum, P.B, [&](int b) { return full_splits(s_len[b], P); });
+  const int tps = P.split >> 4;
+  const int n_part = short_splits_sorted(s_plist, s_bins, P.B, [&](int b) {
+    const int rem = s_len[b] - full_splits(s_len[b], P) * P.split;
+    return rem > 0 ? (((rem + 15) >> 4) * 16 + tps - 1) / tps : 0;
+  });
+  const int n_full = s_full[P.B] * P.H_kv;
+  const int total_items = n_full + n_part * P.H_kv;
+  const int nw_total = gridDim.x * kWaves;
+
+  auto locate = [&](int item, int& b, int& s, int& h) {
+    if (item < n_full) {
+      const int u = item / P.H_kv;
+      h = item - u * P.H_kv;
+      b = find_stream(s_full, P.B, u);
+      s = u - s_full[b];
+    } else {
+      const int t = item - n_full;
+      const int u = t / P.H_kv;
+      h = t - u * P.H_kv;
+      b = s_plist[u];
+      s = s_full[b + 1] - s_full[b];
+    }
+    b = uniform(b);
+    s = uniform(s);
+    h = uniform(h);
+  };
+  // block ids (one page per lane) and this lane's query fragments: row l%16,
+  // dims 32*k + 8*(l/16) .. +7 for k < NS (zeros for rows past the block)
+  auto fetch = [&](int item, int& blk, bf16x8_t (&qf)[NS]) {
+    int b, s, h;
+    locate(item, b, s, h);
+    const int n = s_len[b];
+    const int t0 = s * P.split;
+    const int t1 = min(t0 + P.split, n);
+    const int p0 = t0 / bs;
+    const int n_pages = (t1 - 1) / bs - p0 + 1;
+    blk = 0;
+    if (lane < n_pages) blk = clampi(P.block_table[(size_t)b * P.max_blocks + p0 + lane], 0, P.num_blocks - 1);
+#pragma unroll
+    for (int k = 0; k < NS; ++k) qf[k] = bf16x8_t{};
+    if (l16 < nrow) {
+      const int j = l16 / P.G, gi = l16 - (l16 / P.G) * P.G;
+      const uint16_t* qrow = qp + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D + 8 * lg;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) qf[k] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * k);
+    }
+  };
+
+  int item = blockIdx.x * kWaves + (tid >> 6);
+  int my_blk = 0;
+  bf16x8_t qf[NS];
+  if (item < total_items) fetch(item, my_blk, qf);
+
+  while (item < total_items) {
+    const int next_item = item + nw_total;
+    int b, s, h;
+    locate(item, b, s, h);
+    const int n_total = s_len[b];
+    const int ns = split_count(n_total, P);
+    const int t0 = s * P.split;
+    const int t1 = min(t0 + P.split, n_total);
+    const int n_tiles = (t1 - t0 + 15) >> 4;
+    const int p0 = t0 / bs;
+    // keys visible to this lane's query row (0 for rows past the block)
+    const int n_row = l16 < nrow ? n_total - (P.Kq - 1 - l16 / P.G) : 0;
+
+    float m = kNegBig, lsum = 0.f;
+    f32x4_t acc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int ti, bf16x8_t (&kr)[NS], uint2 (&vr)[NJ]) {
+      const int tk = t0 + (ti << 4);
+      const int blk = __builtin_amdgcn_readlane(my_blk, uniform(tk / bs - p0));
+      const int slot0 = tk % bs;
+      const size_t hb = (size_t)blk * P.H_kv + h;
+      const uint16_t* kp = kc + (hb * bs + slot0 + l16) * D + 8 * lg;
+      const uint16_t* vp = vc + hb * D * bs + (size_t)l16 * bs + slot0 + 4 * lg;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const uint4 w = ld_nt(reinterpret_cast<const uint4*>(kp + 32 * k));
+        kr[k] = __builtin_bit_cast(bf16x8_t, w);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) vr[j] = ld_nt(reinterpret_cast<const uint2*>(vp + (size_t)16 * j * bs));
+    };
+
+    // tk: first token of the tile; tiles past the item (tk >= t1) are
+    // duplicates of its last tile and are masked entirely
+    auto compute = [&](int tk, const bf16x8_t (&kr)[NS], const uint2 (&vr)[NJ]) {
+      f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NS; ++k) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k], qf[k], S, 0, 0, 0);
+      const int lim = tk < t1 ? n_row : 0;
+      const int tl = tk + 4 * lg;                 // this lane's first token
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = tl + i < lim ? S[i] * P.scale_log2 : -INFINITY;
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m, mx);
+      const float corr = __builtin_amdgcn_exp2f(m - m_new);
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+      lsum = lsum * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m = m_new;
+      const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+      const bf16x4s pb = __builtin_bit_cast(bf16x4s, make_uint2(p01, p23));
+      // values of slots that hold no key yet may be anything (NaN): zero them
+      const int vis = tk < t1 ? n_total : 0;
+      const uint32_t keep0 = (tl < vis ? 0x0000ffffu : 0u) | (tl + 1 < vis ? 0xffff0000u : 0u);
+      const uint32_t keep1 = (tl + 2 < vis ? 0x0000ffffu : 0u) | (tl + 3 < vis ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bf16x4s va = __builtin_bit_cast(bf16x4s, make_uint2(vr[j].x & keep0, vr[j].y & keep1));
+        acc[j] = acc[j] * corr;
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[j], 0, 0, 0);
+      }
+    };
+
+    bf16x8_t ka[NS], kb[NS];
+    uint2 va[NJ], vb[NJ];
+    const int last = n_tiles - 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see attn_split_kernel
+    issue(0, ka, va);
+    int nblk = 0;
+    bf16x8_t nq[NS];
+    if (next_item < total_items) fetch(next_item, nblk, nq);
+    for (int ti = 0; ti <= last; ti += 2) {
+      issue(min(ti + 1, last), kb, vb);
+      compute(t0 + (ti << 4), ka, va);
+      issue(min(ti + 2, last), ka, va);
+      compute(t0 + ((ti + 1) << 4), kb, vb);
+    }
+
+    // row sums: add the four lanes of each row
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    // lane l holds O^T[16 j + 4 (l/16) + i][row l%16]
+    if (l16 < nrow) {
+      const size_t bh = (size_t)b * P.H_kv + h;
+      if (ns == 1) {
+        const int j = l16 / P.G, gi = l16 - (l16 / P.G) * P.G;
+        uint16_t* orow = op + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D + 4 * lg;
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          const f32x4_t a = acc[jj] * inv;
+          *reinterpret_cast<uint2*>(orow + 16 * jj) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+        }
+      } else {
+        const size_t pr = (bh * P.max_splits + s) * NR + l16;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          *reinterpret_cast<f32x4_t*>(P.part_acc + pr * D + 16 * jj + 4 * lg) = acc[jj];
+        if (lg == 0) { P.part_ml[2 * pr] = m; P.part_ml[2 * pr + 1] = lsum; }
+      }
+    }
+    item = next_item;
+    my_blk = nblk;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) qf[k] = nq[k];
+  }
+}
+
 // Merge the splits of each (stream, KV head, query row) that has more than
 // one: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, in split order.
 // One wave per row: lane i holds split i's (m, l); each lane accumulates
@@ -597,7 +805,12 @@ int device_cus() {
 template <typename T, int D, int NR>
 hipError_t launch_t(const KParams& P, int grid, hipStream_t s) {
   const bool exact = P.nr == NR;
-  if (P.bs == 16 && exact)
+  if constexpr (std::is_same<T, uint16_t>::value && NR > 2) {
+    if (P.bs == 16)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 16>), dim3(grid), dim3(kThreads), 0, s, P);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 0>), dim3(grid), dim3(kThreads), 0, s, P);
+  } else if (P.bs == 16 && exact)
     hipLaunchKernelGGL((attn_split_kernel<T, D, NR, 16, true>), dim3(grid), dim3(kThreads), 0, s, P);
   else if (P.bs == 16)
     hipLaunchKernelGGL((attn_split_kernel<T, D, NR, 16, false>), dim3(grid), dim3(kThreads), 0, s, P);
