@@ -846,17 +846,21 @@ bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_l
   if (nr > 16) return false;
   p->nr = nr;
   p->nr_tmpl = nr <= 1 ? 1 : nr <= 2 ? 2 : nr <= 4 ? 4 : nr <= 8 ? 8 : nr <= 12 ? 12 : 16;
-  // Split length: the largest power of two <= (expected token-heads / 512),
-  // clamped to [64, 1024] tokens, taking lengths to average half the maximum.
-  // Long splits cost less per token (fewer partial results, fewer pipeline
-  // restarts); short ones keep small batches spread over the CUs.  Measured
-  // on MI355X: 256 streams x log-uniform 64..8192 keys run 8% faster at 1024
-  // than at 256 tokens, 64 streams x 200..3000 keys 25% faster at 512-1024,
-  // and 16 streams x 100..1500 keys best at 128.  An item then spans at most
-  // 64 blocks of 16 tokens (one block id per lane).
+  // Split length: the largest power of two <= (expected token-heads / c),
+  // clamped to [64, 1024] tokens, taking lengths to average half the maximum;
+  // c = 512, or 256 for blocks of more than 2 query rows (the matrix-core
+  // kernel, whose tiles cost more per token).  Long splits cost less per
+  // token (fewer partial results, fewer pipeline restarts); short ones keep
+  // small batches spread over the CUs.  Measured on MI355X: 256 streams x
+  // log-uniform 64..8192 keys run 8% faster at 1024 than at 256 tokens, 64
+  // streams x 200..3000 keys 25% faster at 512-1024, 16 streams x 100..1500
+  // keys best at 128, and 32 streams x 6-query blocks over 300..2000 keys
+  // best at 512.  An item then spans at most 64 blocks of 16 tokens (one
+  // block id per lane).
   const double est = (double)B * H_kv * (max_kv_len > 1 ? max_kv_len / 2.0 : 1.0);
+  const double per = nr > 2 ? 256.0 : 512.0;
   long split = 64;
-  while (split < 1024 && (double)(split * 2) * 512.0 <= est) split *= 2;
+  while (split < 1024 && (double)(split * 2) * per <= est) split *= 2;
   p->split = (int)split;
   p->max_splits = (int)((max_kv_len + split - 1) / split);
   const size_t slots = (size_t)B * H_kv * p->max_splits * p->nr_tmpl;
