@@ -2,26 +2,21 @@
 // (TontaubeV1, audio head paragraph: a per-stage head onto that stage's
 // codebook; codec paragraph for the 16,384 / 4,096 entry codebooks).
 //
-// bf16: matrix-core kernel.  A workgroup owns VT*16 codebook entries of one
-// stage's W and up to 64 rows of that stage (rows are gathered by head id, in
-// batch order).  The products use v_mfma_f32_16x16x32_bf16 with W as the A
-// operand (16 codebook entries x 32 k) and h as B (32 k x 16 rows): the
-// accumulator lane l holds logits for row l%16 and 4 consecutive entries.
-// The four waves split the reduction (k) dimension; their partial tiles are
-// summed in LDS in wave order, so the result is deterministic.
-//
-// Operands come straight from global memory through a 3-deep register ring:
-// two k-steps of loads are in flight while one is multiplied, and the
-// steady-state loop has no branch at all (loads past the end re-read the last
-// k-step, which hits in cache; the last k-steps are multiplied after the
-// loop), so wait counts stay exact.  When a stage has several row chunks,
-// they read the same W tile: the 1-D grid is laid out so those workgroups sit
-// on one XCD (the hardware deals workgroup i to XCD i % 8) and are dispatched
-// together, so W comes from HBM once and from that XCD's L2 after.
-//
-// More than 64 rows per call: tiles of up to 128 codebook entries x 128 rows
-// are staged through LDS by the global-to-LDS DMA loads, so the operands never
-// pass through registers on their way in; the matrix cores read them from LDS.
+// bf16: matrix-core kernel with v_mfma_f32_16x16x32_bf16.  A workgroup owns
+// a tile of NV codebook entries of one stage's W and MR rows of that stage
+// (rows are gathered by head id, in batch order) and walks k in chunks of 64.
+// Each chunk of both operands goes from global memory straight into LDS with
+// the global-to-LDS DMA loads (every instruction moves 8 whole 128-byte row
+// pieces; pieces are XOR-swizzled by row so the matrix cores' 16-byte operand
+// reads are bank-conflict free), three chunks in flight while one is
+// multiplied.  The four waves are laid out 2 (entries) x 2 (rows) and write
+// their logits directly, 4 consecutive entries per lane.  MR in {32, 64, 128}
+// pads the fewest rows; NV in {128, 64, 32} is the widest that still gives
+// 256 workgroups.  When a stage has several row chunks they read the same W
+// tile: the 1-D grid is laid out so those workgroups sit on one XCD (the
+// hardware deals workgroup i to XCD i % 8) and run together, so W comes from
+// HBM once and from that XCD's L2 after.  W is read once per call for up to
+// 128 rows.
 //
 // fp32: a plain wave-per-row GEMV (used by the small fp32 workload).
 #include "clm_device.h"
@@ -30,11 +25,8 @@
 namespace clm {
 namespace {
 
-constexpr int kRowsPerWG = 64;
 constexpr int kXcds = 8;
-constexpr int kRing = 3;
-constexpr int kSplitK = 4;             // waves per workgroup, each 1/4 of k
-constexpr int kThreads = kSplitK * 64;
+constexpr int kHeadWGs = 256;           // workgroups the tile choice aims for
 
 struct HeadP {
   const uint16_t* h;
@@ -43,142 +35,6 @@ struct HeadP {
   float* logits;
   int G, M, d, V, row_chunks, nvt, nvt_pad;
 };
-
-template <int VT, int RT>
-__global__ __launch_bounds__(kThreads) void head_mfma_kernel(HeadP P) {
-  constexpr int NV = VT * 16;        // codebook entries per workgroup
-  constexpr int LDW = NV + 4;        // padded LDS row (floats)
-  __shared__ int s_rows[kRowsPerWG];
-  __shared__ int s_cnt[kSplitK];
-  __shared__ float s_red[kSplitK][kRowsPerWG][LDW];
-
-  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
-
-  // ---- (vocab tile, row chunk, stage) from the XCD-aware 1-D grid ---------
-  const int per_grp = P.nvt_pad * P.row_chunks;
-  const int grp = blockIdx.x / per_grp;
-  const int id = blockIdx.x - grp * per_grp;
-  const int super = id / (kXcds * P.row_chunks);
-  const int rem = id - super * kXcds * P.row_chunks;
-  const int rc = rem / kXcds;
-  const int vt = super * kXcds + (rem - rc * kXcds);
-  if (vt >= P.nvt) return;
-  const int v0 = vt * NV;
-
-  // ---- rows of this stage, chunk rc (batch order) ---------------------------
-  int n_rows;
-  if (P.G == 1) {
-    n_rows = min(kRowsPerWG, P.M - rc * kRowsPerWG);
-    if (tid < kRowsPerWG) s_rows[tid] = min(rc * kRowsPerWG + tid, P.M - 1);
-    __syncthreads();
-  } else {
-    const int per = (P.M + kThreads - 1) / kThreads;
-    const int r0 = tid * per;
-    int cnt = 0;
-    for (int k = 0; k < per; ++k) {
-      int r = r0 + k;
-      if (r < P.M && clampi(P.head_id[r], 0, P.G - 1) == grp) ++cnt;
-    }
-    int incl = wave_incl_scan_i(cnt, lane);
-    if (lane == 63) s_cnt[w] = incl;
-    __syncthreads();
-    int rank = incl - cnt;
-    int total = 0;
-    for (int i = 0; i < kSplitK; ++i) {
-      rank += i < w ? s_cnt[i] : 0;
-      total += s_cnt[i];
-    }
-    for (int k = 0; k < per; ++k) {
-      int r = r0 + k;
-      if (r < P.M && clampi(P.head_id[r], 0, P.G - 1) == grp) {
-        const int slot = rank - rc * kRowsPerWG;
-        if (slot >= 0 && slot < kRowsPerWG) s_rows[slot] = r;
-        ++rank;
-      }
-    }
-    n_rows = min(kRowsPerWG, total - rc * kRowsPerWG);
-    __syncthreads();
-    if (n_rows > 0 && tid >= n_rows && tid < kRowsPerWG) s_rows[tid] = s_rows[0];
-    __syncthreads();
-  }
-  n_rows = uniform(n_rows);
-  if (n_rows <= 0) return;
-  const int n_rt = (n_rows + 15) >> 4;
-
-  const uint16_t* __restrict__ Wg = P.W[grp];
-  const int kq = P.d / kSplitK;         // k range per wave
-  const int kb = w * kq;
-  const int nk = kq >> 5;               // k-steps of 32 per wave
-  const int l16 = lane & 15, lg = lane >> 4;
-
-  const uint16_t* aptr[VT];
-#pragma unroll
-  for (int vt_ = 0; vt_ < VT; ++vt_) {
-    const int v = min(v0 + vt_ * 16 + l16, P.V - 1);
-    aptr[vt_] = Wg + (size_t)v * P.d + kb + lg * 8;
-  }
-  // RT row tiles are loaded every k-step (rows past n_rows repeat a valid
-  // row); only the products are skipped for row tiles past n_rt.
-  const uint16_t* bptr[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) bptr[rt] = P.h + (size_t)s_rows[rt * 16 + l16] * P.d + kb + lg * 8;
-
-  f32x4_t acc[VT][RT];
-#pragma unroll
-  for (int vt_ = 0; vt_ < VT; ++vt_)
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) acc[vt_][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  bf16x8_t a[kRing][VT], bb[kRing][RT];
-  // loads of k-step ks (clamped to the last one) into ring slot s
-  auto issue = [&](int ks, int s) {
-    const int k = min(ks, nk - 1) << 5;
-#pragma unroll
-    for (int vt_ = 0; vt_ < VT; ++vt_) a[s][vt_] = *reinterpret_cast<const bf16x8_t*>(aptr[vt_] + k);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) bb[s][rt] = *reinterpret_cast<const bf16x8_t*>(bptr[rt] + k);
-  };
-  // all RT row tiles are multiplied (tiles past n_rt hold repeated rows
-  // whose results are never stored), so the steady-state loop is branch-free
-  auto mma = [&](int s) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int vt_ = 0; vt_ < VT; ++vt_)
-        acc[vt_][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][vt_], bb[s][rt], acc[vt_][rt], 0, 0, 0);
-  };
-
-  issue(0, 0);
-  issue(1, 1);
-  int ks = 0;
-  for (; ks + 3 <= nk; ks += 3) {
-    issue(ks + 2, 2);
-    mma(0);
-    issue(ks + 3, 0);
-    mma(1);
-    issue(ks + 4, 1);
-    mma(2);
-  }
-  // slots 0 and 1 now hold k-steps ks and ks+1 (clamped); finish the rest
-  if (ks < nk) mma(0);
-  if (ks + 1 < nk) mma(1);
-
-  // ---- sum the four k-slices in wave order and store ------------------------
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int vt_ = 0; vt_ < VT; ++vt_)
-      *reinterpret_cast<f32x4_t*>(&s_red[w][rt * 16 + l16][vt_ * 16 + lg * 4]) = acc[vt_][rt];
-  __syncthreads();
-  for (int e = tid; e < n_rows * NV; e += kThreads) {
-    const int rl = e / NV, vl = e - (e / NV) * NV;
-    const int v = v0 + vl;
-    if (v < P.V) {
-      const float s = ((s_red[0][rl][vl] + s_red[1][rl][vl]) + s_red[2][rl][vl]) + s_red[3][rl][vl];
-      P.logits[(size_t)s_rows[rl] * P.V + v] = s;
-    }
-  }
-}
 
 // Rows of stage grp that fall in row chunk rc (MR rows each, batch order) into
 // s_rows; slots past the last row repeat a valid row so loads stay in bounds.
@@ -238,7 +94,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Many rows, LDS fed by DMA: S LDS stages of one 64-k chunk each, holding NV
+// LDS fed by DMA: S LDS stages of one 64-k chunk each, holding NV
 // codebook rows then MR h rows (128 bytes per row, the 16-byte pieces
 // XOR-swizzled by row so the operand reads are bank-conflict free).  Each
 // wave's DMA instruction fills 8 whole rows (1 KiB), lane l taking the piece
@@ -409,39 +265,26 @@ hipError_t launch_codebook_head(const HeadArgs& a, hipStream_t s) {
     P.head_id = a.head_id;
     P.logits = a.logits;
     P.G = a.G; P.M = a.M; P.d = a.d; P.V = a.V;
-    if (a.M > kRowsPerWG) {
-      // many rows: LDS-staged tiles of 128 rows and 128 entries, or 64
-      // entries when 128 would leave CUs without a workgroup
-      P.row_chunks = (a.M + 127) / 128;
-      const bool wide = (long)((a.V + 127) / 128) * P.row_chunks * a.G >= 256;
-      const int nv = wide ? 128 : 64;
-      P.nvt = (a.V + nv - 1) / nv;
-      P.nvt_pad = (P.nvt + kXcds - 1) / kXcds * kXcds;
-      const dim3 g((unsigned)((long)P.nvt_pad * P.row_chunks * a.G));
-      if (wide) hipLaunchKernelGGL((head_dma_kernel<128, 128, 4>), g, dim3(256), 0, s, P);
-      else hipLaunchKernelGGL((head_dma_kernel<64, 128, 4>), g, dim3(256), 0, s, P);
-      return hipGetLastError();
-    }
-    P.row_chunks = 1;
-    // 64-entry tiles when that already gives >= 512 workgroups, else 32.
-    const bool wide = (long)((a.V + 63) / 64) * a.G >= 512;
-    const int nv = wide ? 64 : 32;
+    // LDS-staged tiles of NV codebook entries x MR rows: MR in {32, 64, 128}
+    // with the least row padding (the larger on ties), then the widest NV in
+    // {128, 64, 32} that still gives kHeadWGs workgroups (else 32)
+    int mr = 128;
+    for (int c : {64, 32})
+      if ((a.M + c - 1) / c * c < (a.M + mr - 1) / mr * mr) mr = c;
+    P.row_chunks = (a.M + mr - 1) / mr;
+    int nv = 32;
+    for (int c : {128, 64})
+      if ((long)((a.V + c - 1) / c) * P.row_chunks * a.G >= kHeadWGs) { nv = c; break; }
     P.nvt = (a.V + nv - 1) / nv;
     P.nvt_pad = (P.nvt + kXcds - 1) / kXcds * kXcds;
-    const long grid = (long)P.nvt_pad * P.row_chunks * a.G;
-    // row tiles per workgroup: enough for the rows (<= 64)
-    const int rt = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
-    const dim3 g((unsigned)grid), b(kThreads);
-    if (wide) {
-      if (rt == 1) hipLaunchKernelGGL((head_mfma_kernel<4, 1>), g, b, 0, s, P);
-      else if (rt == 2) hipLaunchKernelGGL((head_mfma_kernel<4, 2>), g, b, 0, s, P);
-      else hipLaunchKernelGGL((head_mfma_kernel<4, 4>), g, b, 0, s, P);
-    } else {
-      if (rt == 1) hipLaunchKernelGGL((head_mfma_kernel<2, 1>), g, b, 0, s, P);
-      else if (rt == 2) hipLaunchKernelGGL((head_mfma_kernel<2, 2>), g, b, 0, s, P);
-      else hipLaunchKernelGGL((head_mfma_kernel<2, 4>), g, b, 0, s, P);
-    }
-    return hipGetLastError();
+    const dim3 g((unsigned)((long)P.nvt_pad * P.row_chunks * a.G)), b(256);
+#define CLM_HEAD_DMA(NV_, MR_) \
+    if (nv == NV_ && mr == MR_) { hipLaunchKernelGGL((head_dma_kernel<NV_, MR_, 4>), g, b, 0, s, P); return hipGetLastError(); }
+    CLM_HEAD_DMA(128, 128) CLM_HEAD_DMA(128, 64) CLM_HEAD_DMA(128, 32)
+    CLM_HEAD_DMA(64, 128) CLM_HEAD_DMA(64, 64) CLM_HEAD_DMA(64, 32)
+    CLM_HEAD_DMA(32, 128) CLM_HEAD_DMA(32, 64) CLM_HEAD_DMA(32, 32)
+#undef CLM_HEAD_DMA
+    return hipErrorInvalidValue;
   }
   GemvP P;
   P.h = static_cast<const float*>(a.h);

@@ -161,9 +161,9 @@ int clm_decode_attention(const void* q, const void* k_cache, const void* v_cache
  *   W        host array of G device pointers, each [V, d] (element type dt)
  *   head_id  [M] int32 in [0, G), or NULL when G == 1
  *   logits   [M, V] float32           output
- * Each W_g is streamed from memory once per call for up to 64 rows of its
- * group; more rows are taken in chunks of 128 whose workgroups read the same
- * W tile close together in time, so it comes from memory about once.
+ * Each W_g is streamed from memory once per call for up to 128 rows of its
+ * group; more rows are taken in chunks whose workgroups read the same W tile
+ * close together in time, so it comes from memory about once.
  * Arithmetic: products of dt values accumulated in fp32.
  * Errors: INVALID_ARG (null, sizes < 1, G > 8, head_id NULL with G > 1,
  *   h or a W not 16-byte aligned), UNSUPPORTED (bf16 with d % 128 != 0, f32
