@@ -6,6 +6,10 @@
 A step is the whole hot path over one batch: kv_cache_append ->
 decode_attention -> codebook_head -> sample_or_argmax (spec_verify for the
 speculative workload), all through the C ABI, inputs resident in HBM.  The
+timed steps are eager calls; --graph on captures the step once as a HIP graph
+and times its replays instead (faster only where launches dominate, as in
+the one-stream fp32 workload).  Per-call durations always come from HIP
+events around eager calls.  The
 default workload is 256 streams with log-uniform KV lengths in [64, 8192],
 16 query / 8 KV heads of width 128, bf16 cache, a 2048 -> 16384 head and
 greedy decoding: the one that fills the GPU and exposes the attention
@@ -54,6 +58,8 @@ def parse():
                     help="streams in the oracle's timed sample (0 = the whole batch)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="the oracle is repeated over its sample until this much CPU time has passed")
+    ap.add_argument("--graph", choices=("on", "off"), default="off",
+                    help="time the step as replays of one captured HIP graph (on) or as eager calls (off)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -285,10 +291,29 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # The step as one HIP graph: every call only enqueues kernels on the
+    # current stream (no allocation, host sync or memset), so a fixed-shape
+    # step captures as is and replays without per-launch host overhead.
+    run = step
+    if args.graph == "on":
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+
     # whole-step throughput: K steps back to back, no events inside
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -349,6 +374,7 @@ def main():
             "streams": c.B, "queries_per_stream": c.Kq, "q_heads": c.H_q, "kv_heads": c.H_kv,
             "head_dim": c.D, "kv_len": "x".join(str(a) for a in c.kv_len_dist), "block_size": c.block_size,
             "d_model": c.d_model, "codebook": c.V, "heads": c.G, "decoding": c.mode,
+            "launch": "hip_graph" if args.graph == "on" else "eager",
         },
         "roofline": {
             "bound": "hbm",

@@ -14,7 +14,14 @@ order:
       accept -> emit x and go on
       reject -> emit a draw from max(p - draft_probs[i], 0), normalised,
                 and stop
-Readings where the pages leave a step open: no bonus token after K accepts;
+Bonus-token variant (``bonus=True``): the target pass also scores the
+position after the last draft, so K+1 target distributions are given; when
+all K drafts are accepted, one more token is drawn from the (K+1)-th target
+distribution with u_resample (only one of the residual and bonus draws can
+happen).  The blog's 0.28 forward passes per token (section 'Latency
+Benchmark Analysis') matches this variant at its alpha = 0.82, K = 4.
+Readings where the pages leave a step open: no bonus token after K accepts
+in the default form;
 the random numbers are supplied (u_accept [B,K], u_resample [B]) and the
 residual draw is by inverse CDF in ascending token order; if the residual has
 zero mass (only possible when p equals the draft distribution) the draw is
@@ -41,8 +48,11 @@ def target_probs(logits_row, temperature):
     return e / total
 
 
-def spec_verify_stream(target_logits, draft_probs, draft_tokens, u_accept, u_resample, temperature):
-    K = target_logits.shape[0]
+def spec_verify_stream(target_logits, draft_probs, draft_tokens, u_accept, u_resample, temperature,
+                       bonus=False):
+    K = len(draft_tokens)
+    if target_logits.shape[0] != K + (1 if bonus else 0):
+        raise ValueError("target rows must be K (K + 1 with a bonus token)")
     out = []
     for i in range(K):
         p = target_probs(target_logits[i], temperature)
@@ -58,19 +68,23 @@ def spec_verify_stream(target_logits, draft_probs, draft_tokens, u_accept, u_res
             resid = p
         out.append(inverse_cdf(resid, u_resample))
         break
+    else:
+        if bonus:
+            out.append(inverse_cdf(target_probs(target_logits[K], temperature), u_resample))
     return out
 
 
 def spec_verify(target_logits, draft_probs, draft_tokens, u_accept, u_resample, temperature,
-                streams=None):
-    """Batched form: target_logits, draft_probs [B,K,V]; returns
-    (out_tokens [B,K] int32 padded with -1, num_emitted [B] int32)."""
+                streams=None, bonus=False):
+    """Batched form: target_logits [B,K,V] ([B,K+1,V] with bonus), draft_probs
+    [B,K,V]; returns (out_tokens [B,K] ([B,K+1] with bonus) int32 padded with
+    -1, num_emitted [B] int32)."""
     B, K = draft_tokens.shape
-    out = np.full((B, K), -1, np.int32)
+    out = np.full((B, K + (1 if bonus else 0)), -1, np.int32)
     num = np.zeros(B, np.int32)
     for b in (range(B) if streams is None else streams):
         toks = spec_verify_stream(target_logits[b], draft_probs[b], draft_tokens[b],
-                                  u_accept[b], u_resample[b], temperature)
+                                  u_accept[b], u_resample[b], temperature, bonus=bonus)
         out[b, :len(toks)] = toks
         num[b] = len(toks)
     return out, num

@@ -2,8 +2,10 @@
 
 Closed forms, brute force on tiny vocabularies, the speculative-sampling
 theorem (emitted tokens follow the target distribution; acceptance rate
-sum_x min(p, q)), and the acceptance figure the speculative-decoding blog
-prints (tests/golden/spec_acceptance_blog.json).
+sum_x min(p, q)), the acceptance figure the speculative-decoding blog
+prints (tests/golden/spec_acceptance_blog.json), and, for the bonus-token
+variant, the blog's passes-per-token figure
+(tests/golden/spec_passes_per_token_blog.json).
 """
 
 import json
@@ -131,7 +133,7 @@ def test_greedy_verification_at_zero_temperature():
         assert out == expect
 
 
-def _run_trials(p_logits, q, T, n, rng):
+def _run_trials(p_logits, q, T, n, rng, bonus=False):
     """Draw drafts from q and run n verifications; returns emitted lists."""
     K, V = q.shape
     cdf = np.cumsum(q.astype(np.float64), axis=1)
@@ -140,7 +142,7 @@ def _run_trials(p_logits, q, T, n, rng):
         drafts = np.array([min(int(np.searchsorted(cdf[i], rng.random(), side="right")), V - 1)
                            for i in range(K)])
         outs.append(oracle.spec_verify_stream(p_logits, q, drafts, rng.random(K, dtype=np.float32),
-                                              rng.random(dtype=np.float32), T))
+                                              rng.random(dtype=np.float32), T, bonus=bonus))
     return outs
 
 
@@ -201,6 +203,59 @@ def test_acceptance_figure_from_the_blog():
     assert abs(mean_emitted - closed) < 0.03
     assert abs(closed - g["reported_speedup"]) < g["tolerance"]
     assert abs((1 - alpha ** (K + 1)) / (1 - alpha) - g["reported_speedup"]) > g["tolerance"]
+
+
+def test_bonus_variant_matches_the_blogs_passes_per_token():
+    g = json.load(open(os.path.join(GOLDEN, "spec_passes_per_token_blog.json")))
+    alpha, K = g["alpha"], g["K"]
+    # acceptance probability exactly alpha at every position (target [1, 0],
+    # draft [alpha, 1 - alpha]); the bonus row's target is also [1, 0]
+    logits = np.tile(np.array([0.0, -1e30], np.float32), (K + 1, 1))
+    q = np.tile(np.array([alpha, 1 - alpha], np.float32), (K, 1))
+    rng = np.random.default_rng(61)
+    outs = _run_trials(logits, q, 0.7, 20000, rng, bonus=True)
+    mean_emitted = np.mean([len(o) for o in outs])
+    closed = (1 - alpha ** (K + 1)) / (1 - alpha)
+    assert abs(mean_emitted - closed) < 0.03
+    assert all(1 <= len(o) <= K + 1 for o in outs)
+    assert abs(1 / closed - g["reported_passes_per_token"]) < g["tolerance"]
+    # the variant without a bonus token does not reproduce the figure
+    assert abs((1 - alpha) / (1 - alpha ** K) - g["reported_passes_per_token"]) > g["tolerance"]
+
+
+@pytest.mark.parametrize("V,K", [(3, 1), (5, 2)])
+def test_bonus_token_follows_the_last_target_distribution(V, K):
+    # drafts equal to the target distribution are always accepted (u < 1), so
+    # every run ends with a bonus draw from the (K+1)-th target row
+    rng = np.random.default_rng(70 + V)
+    T = 0.7
+    logits = rng.standard_normal((K + 1, V)).astype(np.float32) * 1.5
+    q = np.stack([oracle.target_probs(logits[i], T) for i in range(K)])
+    n = 20000
+    outs = _run_trials(logits, q, T, n, rng, bonus=True)
+    assert all(len(o) == K + 1 for o in outs)
+    p_last = oracle.target_probs(logits[K], T).astype(np.float64)
+    cnt = np.bincount([o[K] for o in outs], minlength=V)
+    assert stats.chisquare(cnt, p_last / p_last.sum() * n).pvalue > 1e-4
+
+
+def test_bonus_greedy_verification():
+    # T = 0: accepted drafts equal each row's argmax; all accepted -> the
+    # bonus token is the argmax of the last row; a mismatch stops without one
+    rng = np.random.default_rng(80)
+    K, V = 3, 6
+    logits = rng.standard_normal((K + 1, V)).astype(np.float32)
+    amax = [oracle.argmax_token(logits[i]) for i in range(K + 1)]
+    q = np.full((K, V), 1.0 / V, np.float32)
+    u = np.full(K, 0.5, np.float32)
+    out = oracle.spec_verify_stream(logits, q, np.array(amax[:K]), u, 0.3, 0.0, bonus=True)
+    assert out == amax
+    drafts = np.array(amax[:K])
+    drafts[1] = (drafts[1] + 1) % V
+    out = oracle.spec_verify_stream(logits, q, drafts, u, 0.3, 0.0, bonus=True)
+    assert out == [amax[0], amax[1]]
+    with pytest.raises(ValueError):
+        oracle.spec_verify_stream(logits[:K], q, drafts, u, 0.3, 0.0, bonus=True)
 
 
 def test_batched_verify_pads_with_minus_one():
