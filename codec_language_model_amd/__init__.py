@@ -22,7 +22,7 @@ from ._lib import CLM_BF16, CLM_F32, STATUS
 
 __all__ = [
     "ClmError", "load", "kv_cache_append", "decode_attention", "decode_attention_workspace_size",
-    "codebook_head", "sample_or_argmax", "spec_verify", "Workspace",
+    "codebook_head", "sample_or_argmax", "spec_verify", "spec_verify_bonus", "Workspace",
 ]
 
 
@@ -223,6 +223,31 @@ def spec_verify(target_logits, draft_probs, draft_tokens, u_accept, u_resample, 
     if num_emitted is None:
         num_emitted = torch.empty(B, dtype=torch.int32, device=target_logits.device)
     _check("clm_spec_verify", lib.clm_spec_verify(
+        _ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resample),
+        C.c_float(temperature), B, K, V, _ptr(out_tokens), _ptr(num_emitted), _stream()))
+    return out_tokens, num_emitted
+
+
+def spec_verify_bonus(target_logits, draft_probs, draft_tokens, u_accept, u_resample, temperature,
+                      out_tokens=None, num_emitted=None):
+    """target_logits [B,K+1,V], draft_probs [B,K,V] float32; draft_tokens
+    [B,K] int32; u_accept [B,K], u_resample [B] float32.  Returns (out_tokens
+    [B,K+1] int32 padded with -1, num_emitted [B] int32 in [1, K+1])."""
+    torch = _torch()
+    lib = load()
+    _cuda("target_logits", target_logits, torch.float32, 3)
+    _cuda("draft_probs", draft_probs, torch.float32, 3)
+    _cuda("draft_tokens", draft_tokens, torch.int32, 2)
+    _cuda("u_accept", u_accept, torch.float32, 2)
+    _cuda("u_resample", u_resample, torch.float32, 1)
+    B, K, V = draft_probs.shape
+    if tuple(target_logits.shape) != (B, K + 1, V) or tuple(draft_tokens.shape) != (B, K):
+        raise ValueError("spec_verify_bonus: shape mismatch")
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=target_logits.device)
+    if num_emitted is None:
+        num_emitted = torch.empty(B, dtype=torch.int32, device=target_logits.device)
+    _check("clm_spec_verify_bonus", lib.clm_spec_verify_bonus(
         _ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resample),
         C.c_float(temperature), B, K, V, _ptr(out_tokens), _ptr(num_emitted), _stream()))
     return out_tokens, num_emitted

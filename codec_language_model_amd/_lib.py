@@ -36,6 +36,7 @@ SIGNATURES = {
     "clm_codebook_head": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _vp]),
     "clm_sample_or_argmax": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "clm_spec_verify": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _vp, _vp, _vp]),
+    "clm_spec_verify_bonus": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _vp, _vp, _vp]),
 }
 
 _lib = None

@@ -175,15 +175,15 @@ int clm_sample_or_argmax(const float* logits, int M, int V, int ld, const float*
   return hip_status(clm::launch_sample_or_argmax(a, stream));
 }
 
-int clm_spec_verify(const float* target_logits, const float* draft_probs,
-                    const int32_t* draft_tokens, const float* u_accept, const float* u_resample,
-                    float temperature, int B, int K, int V, int32_t* out_tokens,
-                    int32_t* num_emitted, hipStream_t stream) {
+static int spec_verify_impl(const float* target_logits, const float* draft_probs,
+                            const int32_t* draft_tokens, const float* u_accept, const float* u_resample,
+                            float temperature, int B, int K, int V, int32_t* out_tokens,
+                            int32_t* num_emitted, int bonus, hipStream_t stream) {
   if (!target_logits || !draft_probs || !draft_tokens || !u_accept || !u_resample || !out_tokens ||
       !num_emitted)
     return CLM_ERR_INVALID_ARG;
   if (B < 1 || K < 1 || V < 1 || !std::isfinite(temperature) || temperature < 0.f) return CLM_ERR_INVALID_ARG;
-  if (K > 16 || V > (1 << 20)) return CLM_ERR_UNSUPPORTED;
+  if (K + bonus > 16 || V > (1 << 20)) return CLM_ERR_UNSUPPORTED;
   if (g_checked) {
     int st = run_checks(stream, [&](int* bad) {
       hipError_t e = clm::launch_check_ints(draft_tokens, B * K, 0, V - 1, bad, stream);
@@ -194,8 +194,24 @@ int clm_spec_verify(const float* target_logits, const float* draft_probs,
     if (st != CLM_OK) return st;
   }
   clm::VerifyArgs a{target_logits, draft_probs, draft_tokens, u_accept, u_resample, temperature,
-                    B, K, V, out_tokens, num_emitted};
+                    B, K, V, out_tokens, num_emitted, bonus};
   return hip_status(clm::launch_spec_verify(a, stream));
+}
+
+int clm_spec_verify(const float* target_logits, const float* draft_probs,
+                    const int32_t* draft_tokens, const float* u_accept, const float* u_resample,
+                    float temperature, int B, int K, int V, int32_t* out_tokens,
+                    int32_t* num_emitted, hipStream_t stream) {
+  return spec_verify_impl(target_logits, draft_probs, draft_tokens, u_accept, u_resample, temperature,
+                          B, K, V, out_tokens, num_emitted, 0, stream);
+}
+
+int clm_spec_verify_bonus(const float* target_logits, const float* draft_probs,
+                          const int32_t* draft_tokens, const float* u_accept, const float* u_resample,
+                          float temperature, int B, int K, int V, int32_t* out_tokens,
+                          int32_t* num_emitted, hipStream_t stream) {
+  return spec_verify_impl(target_logits, draft_probs, draft_tokens, u_accept, u_resample, temperature,
+                          B, K, V, out_tokens, num_emitted, 1, stream);
 }
 
 }  // extern "C"

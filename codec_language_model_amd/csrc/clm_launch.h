@@ -75,6 +75,7 @@ struct VerifyArgs {
   int B, K, V;
   int32_t* out_tokens;
   int32_t* num_emitted;
+  int bonus;   // 1: K+1 target rows and out rows, a bonus draw after K accepts
 };
 hipError_t launch_spec_verify(const VerifyArgs& a, hipStream_t s);
 

@@ -314,7 +314,8 @@ __device__ RowStat wave_row_stat(const float* __restrict__ x, int n, float T) {
 // one wave per row, while the drafted token of each row is looked up.  (2)
 // The accept chain, which needs only p[x] = exp(x[x]/T - m)/S for the
 // drafted token of each row, walked in order by one lane.  (3) On the first
-// rejection, the residual draw over that one row.
+// rejection, the residual draw over that one row; with the bonus variant,
+// when every draft is accepted, a draw from the target row after them.
 __global__ __launch_bounds__(kT) void verify_kernel(VerifyArgs P) {
   __shared__ Scratch sc;
   __shared__ float s_m[kMaxDraft], s_sum[kMaxDraft];
@@ -326,26 +327,23 @@ __global__ __launch_bounds__(kT) void verify_kernel(VerifyArgs P) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const float T = P.temperature;
   const int V = P.V, K = P.K;
+  const int TK = K + P.bonus;            // target rows (and output rows) per stream
 
-  if (w < K) {
-    const RowStat st = wave_row_stat(P.target_logits + ((size_t)b * K + w) * V, V, T);
+  auto lookup = [&]() {                  // the drafted token of each row and its numbers
+    const size_t row = (size_t)b * K + lane;
+    const int xt = clampi(P.draft_tokens[row], 0, V - 1);
+    s_xt[lane] = xt;
+    s_qx[lane] = P.draft_probs[row * V + xt];
+    s_xx[lane] = P.target_logits[((size_t)b * TK + lane) * V + xt];
+    s_ua[lane] = P.u_accept[row];
+  };
+  if (w < TK) {
+    const RowStat st = wave_row_stat(P.target_logits + ((size_t)b * TK + w) * V, V, T);
     if (lane == 0) { s_m[w] = st.m; s_sum[w] = st.sum; s_amax[w] = st.amax; }
   } else if (w == kW - 1 && lane < K) {
-    const size_t row = (size_t)b * K + lane;
-    const int xt = clampi(P.draft_tokens[row], 0, V - 1);
-    s_xt[lane] = xt;
-    s_qx[lane] = P.draft_probs[row * V + xt];
-    s_xx[lane] = P.target_logits[row * V + xt];
-    s_ua[lane] = P.u_accept[row];
+    lookup();
   }
-  if (K == kMaxDraft && w == 0 && lane < K) {   // every wave holds a row: wave 0 looks up after
-    const size_t row = (size_t)b * K + lane;
-    const int xt = clampi(P.draft_tokens[row], 0, V - 1);
-    s_xt[lane] = xt;
-    s_qx[lane] = P.draft_probs[row * V + xt];
-    s_xx[lane] = P.target_logits[row * V + xt];
-    s_ua[lane] = P.u_accept[row];
-  }
+  if (TK >= kW && w == 0 && lane < K) lookup();   // every wave held a row: wave 0 looks up after
   __syncthreads();
 
   if (threadIdx.x == 0) {
@@ -362,19 +360,20 @@ __global__ __launch_bounds__(kT) void verify_kernel(VerifyArgs P) {
         accept = qx > 0.f && xt == s_amax[i];
       }
       if (!accept) { rej = i; break; }
-      P.out_tokens[(size_t)b * K + i] = xt;
+      P.out_tokens[(size_t)b * TK + i] = xt;
     }
     s_first_reject = rej;
-    s_emitted = rej < 0 ? K : rej + 1;
+    s_emitted = rej < 0 ? TK : rej + 1;
   }
   __syncthreads();
   const int rej = s_first_reject, emitted = s_emitted;
 
   if (rej >= 0) {
-    const size_t row = (size_t)b * K + rej;
+    const size_t row = (size_t)b * K + rej;            // draft row
+    const size_t trow = (size_t)b * TK + rej;          // target row
     int tok;
     if (T > 0.f) {
-      const float* __restrict__ x = P.target_logits + row * V;
+      const float* __restrict__ x = P.target_logits + trow * V;
       const float* __restrict__ q = P.draft_probs + row * V;
       const float m = s_m[rej] / T, S = s_sum[rej];
       const float ur = P.u_resample[b];
@@ -402,9 +401,29 @@ __global__ __launch_bounds__(kT) void verify_kernel(VerifyArgs P) {
       // zero everywhere, then the draw is from the one-hot target): amax
       tok = s_amax[rej];
     }
-    if (threadIdx.x == 0) P.out_tokens[row] = tok;
+    if (threadIdx.x == 0) P.out_tokens[trow] = tok;
+  } else if (P.bonus) {
+    // every draft accepted: one more token from the target row after them
+    const size_t trow = (size_t)b * TK + K;
+    int tok;
+    if (T > 0.f) {
+      const float* __restrict__ x = P.target_logits + trow * V;
+      const float m = s_m[K] / T, S = s_sum[K];
+      float e[kCH];
+      auto target = [&](int i0, float (&wgt)[kCH]) {
+        float y[kCH];
+        load16(x, i0, V, y, 0.f);
+#pragma unroll
+        for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? expf(y[k] / T - m) / S : 0.f;
+      };
+      tok = block_draw(V, P.u_resample[b], target, e, false, sc);
+      if (tok < 0) tok = 0;
+    } else {
+      tok = s_amax[K];
+    }
+    if (threadIdx.x == 0) P.out_tokens[trow] = tok;
   }
-  for (int i = emitted + threadIdx.x; i < K; i += kT) P.out_tokens[(size_t)b * K + i] = -1;
+  for (int i = emitted + threadIdx.x; i < TK; i += kT) P.out_tokens[(size_t)b * TK + i] = -1;
   if (threadIdx.x == 0) P.num_emitted[b] = emitted;
 }
 

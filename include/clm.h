@@ -14,6 +14,7 @@
  *                          stage (one weight matrix per stage)
  *   clm_sample_or_argmax   greedy argmax or temperature sampling per row
  *   clm_spec_verify        speculative accept/reject of K drafted tokens
+ *   clm_spec_verify_bonus  the same with a bonus token after K accepts
  *
  * Conventions shared by every call
  * --------------------------------
@@ -215,6 +216,30 @@ int clm_spec_verify(const float* target_logits, const float* draft_probs,
                     const int32_t* draft_tokens, const float* u_accept, const float* u_resample,
                     float temperature, int B, int K, int V, int32_t* out_tokens,
                     int32_t* num_emitted, hipStream_t stream);
+
+/*
+ * Speculative verification with a bonus token (Optimizing Streaming
+ * Text-to-Speech Models ..., "Latency Benchmark Analysis": 0.28 target passes
+ * per token at the acceptance rate 0.82 and K = 4 of "Speculative Decoding
+ * for Acoustic Tokens", i.e. (1 - 0.82^5) / (1 - 0.82) = 3.50 tokens per
+ * pass).  The target pass scores K + 1 positions: the K drafts and the one
+ * after them.  Decisions for i = 0..K-1 are those of clm_spec_verify; if all
+ * K drafts are accepted, one more token is drawn by inverse CDF at
+ * u_resample[b] from softmax(target_logits[b,K,:] / T) (T = 0: its argmax).
+ * At most one of the residual and bonus draws happens, so one uniform per
+ * stream serves both.
+ *   target_logits [B, K+1, V] float32,  draft_probs [B, K, V] float32
+ *   draft_tokens  [B, K] int32 in [0, V)
+ *   u_accept      [B, K] float32 in [0,1),  u_resample [B] float32 in [0,1)
+ *   temperature   host float >= 0
+ *   out_tokens    [B, K+1] int32 output: emitted tokens, then -1 padding
+ *   num_emitted   [B] int32 output in [1, K+1]
+ * Errors: as clm_spec_verify, with UNSUPPORTED for K + 1 > 16.
+ */
+int clm_spec_verify_bonus(const float* target_logits, const float* draft_probs,
+                          const int32_t* draft_tokens, const float* u_accept, const float* u_resample,
+                          float temperature, int B, int K, int V, int32_t* out_tokens,
+                          int32_t* num_emitted, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ _STREAMS = {
     "kv_len": 1, "stage": 2, "blocks": 3, "k_hist": 4, "v_hist": 5, "k_new": 6,
     "v_new": 7, "q": 8, "w": 9, "h_iso": 10, "uniforms": 11, "draft_logits": 12,
     "draft_tokens": 13, "u_accept": 14, "u_resample": 15, "logits_iso": 16,
-    "target_logits_iso": 17,
+    "target_logits_iso": 17, "target_logits_bonus_row": 18,
 }
 
 BF16_NAN = np.uint16(0x7FC0)
@@ -160,7 +160,8 @@ class StepInputs:
     def spec_inputs(self):
         """Draft side of speculative verification: draft_probs [B,K,V] f32 (softmax
         of N(0, draft_logit_std) logits), draft_tokens [B,K] drawn from them,
-        u_accept [B,K], u_resample [B], and isolated target logits [B,K,V]."""
+        u_accept [B,K], u_resample [B], isolated target logits [B,K,V], and the
+        same with one more row [B,K+1,V] for the bonus-token variant."""
         cfg = self.cfg
         B, K, V = cfg.B, cfg.Kq, cfg.V
         z = _rng(cfg.seed, "draft_logits").standard_normal((B, K, V)) * cfg.draft_logit_std
@@ -178,8 +179,10 @@ class StepInputs:
         u_accept = _rng(cfg.seed, "u_accept").random((B, K), dtype=np.float32)
         u_resample = _rng(cfg.seed, "u_resample").random(B, dtype=np.float32)
         tl = _rng(cfg.seed, "target_logits_iso").standard_normal((B, K, V), dtype=np.float32) * np.float32(0.9)
+        extra = _rng(cfg.seed, "target_logits_bonus_row").standard_normal((B, 1, V), dtype=np.float32) * np.float32(0.9)
         return dict(draft_probs=draft_probs, draft_tokens=draft_tokens, u_accept=u_accept,
-                    u_resample=u_resample, target_logits_iso=tl)
+                    u_resample=u_resample, target_logits_iso=tl,
+                    target_logits_bonus_iso=np.concatenate([tl, extra], axis=1))
 
 
 def make_inputs(cfg, B: Optional[int] = None, spare_blocks: int = 4) -> StepInputs:

@@ -103,15 +103,18 @@ def check_sampled(gpu_tok, ref_logits, temperature, uniforms, what, vocab_valid=
     return exempt
 
 
-def check_verify(gpu_toks, gpu_num, ref_logits, draft_probs, draft_tokens, u_acc, u_res, T, what):
+def check_verify(gpu_toks, gpu_num, ref_logits, draft_probs, draft_tokens, u_acc, u_res, T, what,
+                 bonus=False):
     """Walks each stream's decisions against the oracle's.  Returns the
-    number of exempt streams."""
+    number of exempt streams.  With bonus, ref_logits has K+1 rows and a
+    stream whose K drafts are all accepted emits one more token."""
     B, K = draft_tokens.shape
     exempt = 0
     for b in range(B):
-        ref = oracle.spec_verify_stream(ref_logits[b], draft_probs[b], draft_tokens[b], u_acc[b], u_res[b], T)
+        ref = oracle.spec_verify_stream(ref_logits[b], draft_probs[b], draft_tokens[b], u_acc[b], u_res[b], T,
+                                        bonus=bonus)
         got = list(np.asarray(gpu_toks[b][:int(gpu_num[b])]))
-        assert 1 <= int(gpu_num[b]) <= K, f"{what} stream {b}: num_emitted {gpu_num[b]}"
+        assert 1 <= int(gpu_num[b]) <= K + (1 if bonus else 0), f"{what} stream {b}: num_emitted {gpu_num[b]}"
         assert np.all(np.asarray(gpu_toks[b][int(gpu_num[b]):]) == -1), f"{what} stream {b}: padding"
         if got == ref:
             continue
@@ -143,6 +146,17 @@ def check_verify(gpu_toks, gpu_num, ref_logits, draft_probs, draft_tokens, u_acc
             assert lo[g] <= u + UEPS and hi[g] >= u - UEPS
             stream_exempt = True
             break
+        else:
+            if bonus:
+                # every draft accepted in the reference: the bonus draw differs
+                assert len(got) == K + 1, f"{what} stream {b}: no bonus token after K accepts"
+                lo, hi = _cdf_bounds(oracle.target_probs(ref_logits[b][K], T))
+                u = float(u_res[b])
+                g, rt = got[K], ref[K]
+                assert abs(u - lo[rt]) < UEPS or abs(u - hi[rt]) < UEPS, \
+                    f"{what} stream {b}: bonus gpu {g} != ref {rt}"
+                assert lo[g] <= u + UEPS and hi[g] >= u - UEPS
+                stream_exempt = True
         assert stream_exempt, f"{what} stream {b}: {got} vs {ref}"
         exempt += 1
     return exempt

@@ -280,6 +280,42 @@ def test_spec_verify_accepts_when_draft_equals_target(clm_gpu):
     assert np.array_equal(toks.cpu().numpy(), s["draft_tokens"])
 
 
+@pytest.mark.parametrize("T", [0.7, 0.0])
+def test_spec_verify_bonus_isolated(clm_gpu, T):
+    x = inputs(4)
+    s = x.spec_inputs()
+    tl = s["target_logits_bonus_iso"]
+    dp, dtok, ua, ur = _spec_inputs_torch(s)
+    toks, num = clm_gpu.spec_verify_bonus(to_torch(tl), dp, dtok, ua, ur, T)
+    ex = check_verify(toks.cpu().numpy(), num.cpu().numpy(), tl, s["draft_probs"], s["draft_tokens"],
+                      s["u_accept"], s["u_resample"], T, f"verify bonus T={T}", bonus=True)
+    print(f"verify bonus T={T}: exempt {ex}/{x.cfg.B}, mean emitted {num.float().mean().item():.3f}")
+
+
+@pytest.mark.parametrize("T", [0.7, 0.0])
+def test_spec_verify_bonus_after_all_accepts(clm_gpu, T):
+    """Drafts equal to the target distribution (T > 0) or to each row's argmax
+    (T = 0) are all accepted, so every stream ends with a bonus draw."""
+    x = inputs(4)
+    s = x.spec_inputs()
+    tl = s["target_logits_bonus_iso"]
+    K = x.cfg.Kq
+    if T > 0:
+        q = np.stack([[oracle.target_probs(tl[b, i], T) for i in range(K)] for b in range(x.cfg.B)])
+        drafts = s["draft_tokens"]
+    else:
+        q = np.full((x.cfg.B, K, x.cfg.V), 1.0 / x.cfg.V, np.float32)
+        drafts = np.array([[oracle.argmax_token(tl[b, i]) for i in range(K)] for b in range(x.cfg.B)], np.int32)
+    ua = (s["u_accept"] * np.float32(0.999)).astype(np.float32)
+    toks, num = clm_gpu.spec_verify_bonus(to_torch(tl), to_torch(q.astype(np.float32)), to_torch(drafts),
+                                          to_torch(ua), to_torch(s["u_resample"]), T)
+    num = num.cpu().numpy()
+    assert (num == K + 1).all()
+    ex = check_verify(toks.cpu().numpy(), num, tl, q.astype(np.float32), drafts, ua, s["u_resample"], T,
+                      f"bonus all-accept T={T}", bonus=True)
+    print(f"bonus all-accept T={T}: exempt {ex}/{x.cfg.B}")
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_chained_step(clm_gpu, cfg):
     """append -> attention -> head -> sample/argmax/verify on the GPU, against
