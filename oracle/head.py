@@ -10,6 +10,19 @@ paragraph).  The workloads here use a single bias-free linear map per stage:
   logits[r, v] = sum_k h[r, k] * W[g(r)][v, k]
 
 with g(r) = head_id[r] (the stage of row r's stream), W[g] row-major [V, d].
+
+The audio head TontaubeV1 actually describes (audio head paragraph) has two
+layers: it widens the state to 4,096, applies Mish, and projects to the
+stage's vocabulary.  ``codebook_head_mlp`` computes that head:
+
+  z[r, f]      = sum_k h[r, k] * W1[g(r)][f, k]            (W1[g] [F, d])
+  a[r, f]      = bf16( Mish(z[r, f]) ),  Mish(x) = x * tanh(softplus(x))
+  logits[r, v] = sum_f a[r, f] * W2[g(r)][v, f]            (W2[g] [V, F])
+
+Readings where the page leaves a step open: no biases (as for the one-layer
+head); Mish as Misra (2019) defines it; the widened activation is stored in
+the step's element type (bf16) between the two products, rounded to nearest
+even (fp32 workloads keep it in float64).
 """
 
 from __future__ import annotations
@@ -39,3 +52,34 @@ def codebook_head(h, W, head_id=None, rows=None):
             Wf[g] = np.asarray(W[g], np.float64)
         out[r] = Wf[g] @ h[r]
     return out
+
+
+def mish(x):
+    """x * tanh(softplus(x)) in float64; softplus(x) = log(1 + e^x) evaluated
+    as logaddexp(0, x) so that it neither overflows nor loses small values."""
+    x = np.asarray(x, np.float64)
+    return x * np.tanh(np.logaddexp(0.0, x))
+
+
+def round_to_bf16_f64(x):
+    """Round float64 values to the nearest bfloat16 (ties to even), via float32
+    (the kernel rounds its float32 activation), returned as float64."""
+    f = np.asarray(x, np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def codebook_head_mlp(h, W1, W2, head_id=None, act_bf16=True):
+    """h [M, d]; W1 [G, F, d]; W2 [G, V, F]; head_id [M] (None = all zero).
+    Returns (act [M, F] float64 after Mish and, with act_bf16, bf16 rounding;
+    logits [M, V] float64)."""
+    W1 = np.asarray(W1)
+    W2 = np.asarray(W2)
+    if W1.ndim == 2:
+        W1, W2 = W1[None], W2[None]
+    z = codebook_head(h, W1, head_id)
+    a = mish(z)
+    if act_bf16:
+        a = round_to_bf16_f64(a)
+    return a, codebook_head(a, W2, head_id)

@@ -1,4 +1,10 @@
-"""Pins for the head and paged-append oracles (CPU only)."""
+"""Pins for the head and paged-append oracles (CPU only).
+
+The two-layer head's Mish is pinned by the algebraic form
+x * ((1+e^x)^2 - 1) / ((1+e^x)^2 + 1) (tanh(log y) = (y^2-1)/(y^2+1)), its
+slope tanh(log 2) = 3/5 at zero, its asymptotes, and its minimum -0.30884
+reported by Misra (2019); the layer structure by unit-vector and rank-one
+weights."""
 
 import numpy as np
 import pytest
@@ -42,6 +48,68 @@ def test_grouped_heads_equal_separate_dense_calls():
             np.testing.assert_array_equal(out[rows], oracle.codebook_head(h[rows], W[g:g + 1]))
     with pytest.raises(ValueError):
         oracle.codebook_head(h, W, np.full(M, G))
+
+
+def _mish_algebraic(x):
+    # tanh(log y) = (y^2 - 1) / (y^2 + 1) with y = 1 + e^x: no tanh, no log
+    y = 1.0 + np.exp(np.asarray(x, np.float64))
+    return x * (y * y - 1.0) / (y * y + 1.0)
+
+
+def test_mish_closed_forms():
+    x = np.linspace(-8.0, 8.0, 161)
+    np.testing.assert_allclose(oracle.mish(x), _mish_algebraic(x), rtol=1e-12, atol=1e-15)
+    assert oracle.mish(0.0) == 0.0
+    eps = 1e-8
+    assert abs(oracle.mish(eps) / eps - 0.6) < 1e-7          # slope tanh(log 2) = 3/5
+    assert abs(oracle.mish(40.0) - 40.0) < 1e-12             # ~ x for large x
+    assert abs(oracle.mish(-40.0) - (-40.0 * np.exp(-40.0))) < 1e-25   # ~ x e^x for very negative x
+    grid = np.linspace(-3.0, 0.0, 300001)
+    m = oracle.mish(grid)
+    assert abs(m.min() - (-0.30884)) < 1e-5 and abs(grid[np.argmin(m)] - (-1.1924)) < 1e-3
+
+
+def test_bf16_rounding_of_the_activation():
+    from oracle.head import round_to_bf16_f64
+    vals = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -3.14159, 1e-30, 65504.5])
+    r = round_to_bf16_f64(vals)
+    # exactly representable: the low 16 bits of the float32 are zero
+    assert np.all((r.astype(np.float32).view(np.uint32) & 0xFFFF) == 0)
+    # ties go to the even mantissa: 1 + 2^-8 -> 1, 1 + 3*2^-8 -> 1 + 2^-6
+    assert r[0] == 1.0 and r[1] == 1.0 + 2 ** -6 and r[2] == 1.0
+    assert abs(r[3] - -3.140625) == 0
+
+
+def test_two_layer_head_structure():
+    # W1 rows = c_f e_{j(f)}: z[r, f] = c_f h[r, j(f)];  W2 = a b^T: logits = (act . b) a
+    rng = np.random.default_rng(13)
+    M, d, F, V = 6, 16, 24, 30
+    h = rng.standard_normal((M, d))
+    cols, c = rng.integers(0, d, size=F), rng.uniform(-3, 3, size=F)
+    W1 = np.zeros((F, d))
+    W1[np.arange(F), cols] = c
+    a, bvec = rng.standard_normal(V), rng.standard_normal(F)
+    act, logits = oracle.codebook_head_mlp(h, W1, np.outer(a, bvec), act_bf16=False)
+    np.testing.assert_allclose(act, _mish_algebraic(c * h[:, cols]), rtol=1e-12, atol=1e-15)
+    for r in range(M):
+        np.testing.assert_allclose(logits[r], (act[r] @ bvec) * a, rtol=1e-12, atol=1e-12)
+    act16, _ = oracle.codebook_head_mlp(h, W1, np.outer(a, bvec))
+    assert np.all(np.abs(act16 - act) <= np.abs(act) * 2 ** -8 + 1e-38)   # half a bf16 ulp
+
+
+def test_two_layer_grouped_heads_equal_separate_calls():
+    rng = np.random.default_rng(14)
+    M, d, F, V, G = 10, 8, 12, 9, 3
+    W1, W2 = rng.standard_normal((G, F, d)), rng.standard_normal((G, V, F))
+    h = rng.standard_normal((M, d))
+    hid = rng.integers(0, G, size=M)
+    act, logits = oracle.codebook_head_mlp(h, W1, W2, hid)
+    for g in range(G):
+        rows = np.nonzero(hid == g)[0]
+        if rows.size:
+            a_g, l_g = oracle.codebook_head_mlp(h[rows], W1[g], W2[g])
+            np.testing.assert_array_equal(act[rows], a_g)
+            np.testing.assert_array_equal(logits[rows], l_g)
 
 
 def _small_step(cfg_index=3, B=6):
