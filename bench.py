@@ -58,6 +58,9 @@ def parse():
                     help="streams in the oracle's timed sample (0 = the whole batch)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="the oracle is repeated over its sample until this much CPU time has passed")
+    ap.add_argument("--head", choices=("linear", "mlp"), default="linear",
+                    help="codebook head: one linear map per stage (the workloads' head) or TontaubeV1's "
+                         "two-layer d -> 4096 -> Mish -> V head (random N(0, 0.02) weights)")
     ap.add_argument("--graph", choices=("on", "off"), default="off",
                     help="time the step as replays of one captured HIP graph (on) or as eager calls (off)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -249,6 +252,17 @@ def main():
     k_new, v_new, q = dev_t(x.k_new, bf), dev_t(x.v_new, bf), dev_t(x.q, bf)
     W = dev_t(x.W, bf)
     head_id = dev_t(x.head_id, False) if c.G > 1 else None
+    mlp = None
+    if args.head == "mlp":
+        if not bf:
+            print("--head mlp needs a bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        F = 4096
+        gen = torch.Generator(device=dev).manual_seed(1234)
+        W1 = (torch.randn((c.G, F, c.d_model), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        W2 = (torch.randn((c.G, c.V, F), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        act = torch.empty((c.M, F), dtype=torch.bfloat16, device=dev)
+        mlp = (W1, W2, act, F)
     max_kv = int(x.kv_len.max())
     scale = 1.0 / math.sqrt(c.D)
     o = torch.empty_like(q)
@@ -276,7 +290,10 @@ def main():
         clm.decode_attention(q, k_cache, v_cache, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
         if ev is not None:
             ev[2].record()
-        clm.codebook_head(o.view(c.M, c.d_model), W, head_id, out=logits)
+        if mlp is None:
+            clm.codebook_head(o.view(c.M, c.d_model), W, head_id, out=logits)
+        else:
+            clm.codebook_head_mlp(o.view(c.M, c.d_model), mlp[0], mlp[1], head_id, act=mlp[2], out=logits)
         if ev is not None:
             ev[3].record()
         if spec is not None:
@@ -355,7 +372,7 @@ def main():
         cpu = cpu_baseline(x, args.cpu_streams, args.cpu_seconds)
         log(f"[bench] cpu oracle: {cpu['value']:.2f} {cpu['unit']} ({cpu['sample']})")
 
-    head_flops = 2.0 * c.M * c.d_model * c.V
+    head_flops = 2.0 * c.M * c.d_model * c.V if mlp is None else 2.0 * c.M * mlp[3] * (c.d_model + c.V)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -375,6 +392,7 @@ def main():
             "head_dim": c.D, "kv_len": "x".join(str(a) for a in c.kv_len_dist), "block_size": c.block_size,
             "d_model": c.d_model, "codebook": c.V, "heads": c.G, "decoding": c.mode,
             "launch": "hip_graph" if args.graph == "on" else "eager",
+            "head": "linear" if mlp is None else "two-layer d->4096->Mish->V",
         },
         "roofline": {
             "bound": "hbm",
@@ -387,7 +405,7 @@ def main():
             "algorithmic_bytes_per_launch": attn_bytes,
         },
         "per_call_us": {"kv_cache_append": round(per_us[0], 2), "decode_attention": round(per_us[1], 2),
-                        "codebook_head": round(per_us[2], 2),
+                        ("codebook_head" if mlp is None else "codebook_head_mlp"): round(per_us[2], 2),
                         ("spec_verify" if spec is not None else "sample_or_argmax"): round(per_us[3], 2)},
         "codebook_head_tflops": round(head_flops / (per_us[2] * 1e-6) / 1e12, 2),
         "cpu_baseline": cpu,

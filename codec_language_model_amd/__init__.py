@@ -22,7 +22,8 @@ from ._lib import CLM_BF16, CLM_F32, STATUS
 
 __all__ = [
     "ClmError", "load", "kv_cache_append", "decode_attention", "decode_attention_workspace_size",
-    "codebook_head", "sample_or_argmax", "spec_verify", "spec_verify_bonus", "Workspace",
+    "codebook_head", "codebook_head_mlp", "sample_or_argmax", "spec_verify", "spec_verify_bonus",
+    "Workspace",
 ]
 
 
@@ -181,6 +182,46 @@ def codebook_head(h, W, head_id=None, out=None):
     _check("clm_codebook_head", lib.clm_codebook_head(
         _ptr(h), arr, G, _ptr(head_id), _ptr(out), M, d, V, _dt(h), _stream()))
     return out
+
+
+def codebook_head_mlp(h, W1, W2, head_id=None, act=None, out=None):
+    """Two-layer head: h [M,d] bf16; W1 a [G,F,d] tensor or list of G [F,d];
+    W2 a [G,V,F] tensor or list of G [V,F]; head_id [M] int32 (required when
+    G > 1); act [M,F] bf16 scratch for the widened activation (allocated when
+    None).  Returns (logits [M,V] float32, act)."""
+    torch = _torch()
+    lib = load()
+    _cuda("h", h, torch.bfloat16, 2)
+
+    def as_list(W):
+        return [W[g] for g in range(W.shape[0])] if isinstance(W, torch.Tensor) and W.dim() == 3 else list(W)
+    W1s, W2s = as_list(W1), as_list(W2)
+    if len(W1s) != len(W2s):
+        raise ValueError("codebook_head_mlp: W1 and W2 need one matrix per stage each")
+    for i, (a, b) in enumerate(zip(W1s, W2s)):
+        _cuda(f"W1[{i}]", a, torch.bfloat16, 2)
+        _cuda(f"W2[{i}]", b, torch.bfloat16, 2)
+    G = len(W1s)
+    F, d = W1s[0].shape
+    V = W2s[0].shape[0]
+    M = h.shape[0]
+    if h.shape[1] != d or any(tuple(w.shape) != (F, d) for w in W1s) or any(tuple(w.shape) != (V, F) for w in W2s):
+        raise ValueError("codebook_head_mlp: shape mismatch")
+    if head_id is not None:
+        _cuda("head_id", head_id, torch.int32, 1)
+    if act is None:
+        act = torch.empty((M, F), dtype=torch.bfloat16, device=h.device)
+    else:
+        _cuda("act", act, torch.bfloat16, 2)
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.float32, device=h.device)
+    else:
+        _cuda("out", out, torch.float32, 2)
+    a1 = (C.c_void_p * G)(*[w.data_ptr() for w in W1s])
+    a2 = (C.c_void_p * G)(*[w.data_ptr() for w in W2s])
+    _check("clm_codebook_head_mlp", lib.clm_codebook_head_mlp(
+        _ptr(h), a1, a2, G, _ptr(head_id), _ptr(act), _ptr(out), M, d, F, V, _dt(h), _stream()))
+    return out, act
 
 
 def sample_or_argmax(logits, temperature=None, uniforms=None, vocab_valid=None, out=None):

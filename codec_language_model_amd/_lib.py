@@ -34,6 +34,7 @@ SIGNATURES = {
     "clm_decode_attention": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
                                   _f, _i, _vp, _sz, _vp]),
     "clm_codebook_head": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "clm_codebook_head_mlp": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "clm_sample_or_argmax": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "clm_spec_verify": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _vp, _vp, _vp]),
     "clm_spec_verify_bonus": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _vp, _vp, _vp]),

@@ -153,6 +153,36 @@ int clm_codebook_head(const void* h, const void* const* W, int G, const int32_t*
   for (int g = 0; g < 8; ++g) a.W[g] = g < G ? W[g] : W[0];
   a.G = G; a.head_id = head_id; a.logits = logits; a.M = M; a.d = d; a.V = V;
   a.bf16 = dt == CLM_BF16;
+  a.act = nullptr;
+  return hip_status(clm::launch_codebook_head(a, stream));
+}
+
+int clm_codebook_head_mlp(const void* h, const void* const* W1, const void* const* W2, int G,
+                          const int32_t* head_id, void* act, float* logits, int M, int d, int F, int V,
+                          clm_dtype dt, hipStream_t stream) {
+  if (!h || !W1 || !W2 || !act || !logits) return CLM_ERR_INVALID_ARG;
+  if (M < 1 || d < 1 || F < 1 || V < 1 || G < 1 || G > 8) return CLM_ERR_INVALID_ARG;
+  if (G > 1 && !head_id) return CLM_ERR_INVALID_ARG;
+  for (int g = 0; g < G; ++g)
+    if (!W1[g] || !W2[g] || !aligned(W1[g], 16) || !aligned(W2[g], 16)) return CLM_ERR_INVALID_ARG;
+  if (!aligned(h, 16) || !aligned(act, 16)) return CLM_ERR_INVALID_ARG;
+  if (dt != CLM_BF16) return CLM_ERR_UNSUPPORTED;
+  if (M > 65536 || d % 128 != 0 || F % 128 != 0) return CLM_ERR_UNSUPPORTED;
+  if (g_checked && G > 1) {
+    int st = run_checks(stream, [&](int* bad) { return clm::launch_check_ints(head_id, M, 0, G - 1, bad, stream); });
+    if (st != CLM_OK) return st;
+  }
+  clm::HeadArgs a;
+  a.h = h;
+  for (int g = 0; g < 8; ++g) a.W[g] = g < G ? W1[g] : W1[0];
+  a.G = G; a.head_id = head_id; a.logits = nullptr; a.M = M; a.d = d; a.V = F;
+  a.bf16 = true;
+  a.act = static_cast<uint16_t*>(act);
+  hipError_t e = clm::launch_codebook_head(a, stream);
+  if (e != hipSuccess) return hip_status(e);
+  a.h = act;
+  for (int g = 0; g < 8; ++g) a.W[g] = g < G ? W2[g] : W2[0];
+  a.logits = logits; a.d = F; a.V = V; a.act = nullptr;
   return hip_status(clm::launch_codebook_head(a, stream));
 }
 

@@ -52,6 +52,7 @@ struct HeadArgs {
   float* logits;
   int M, d, V;
   bool bf16;
+  uint16_t* act;   // non-null: write bf16(Mish(h W^T)) here ([M, V]) instead of logits
 };
 hipError_t launch_codebook_head(const HeadArgs& a, hipStream_t s);
 

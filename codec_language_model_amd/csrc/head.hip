@@ -18,6 +18,10 @@
 // HBM once and from that XCD's L2 after.  W is read once per call for up to
 // 128 rows.
 //
+// Two-layer head (TontaubeV1, audio head paragraph: widen to 4,096, Mish,
+// project): the same kernel with a Mish epilogue that stores the bf16
+// activation, then the plain kernel on that activation.
+//
 // fp32: a plain wave-per-row GEMV (used by the small fp32 workload).
 #include "clm_device.h"
 #include "clm_launch.h"
@@ -33,6 +37,7 @@ struct HeadP {
   const uint16_t* W[8];
   const int32_t* head_id;
   float* logits;
+  uint16_t* act;    // MISH epilogue: bf16 activations [M, V]
   int G, M, d, V, row_chunks, nvt, nvt_pad;
 };
 
@@ -101,7 +106,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // that belongs in slot l % 8.  S - 1 chunks are in flight while one is
 // multiplied; one barrier per chunk.  Waves are laid out 2 (entries) x 2
 // (rows); each owns NV/2 entries x MR/2 rows and writes its logits directly.
-template <int NV, int MR, int S>
+// Mish(x) = x * tanh(softplus(x)), written with y = 1 + e^x as
+// x * (y^2 - 1) / (y^2 + 1) = x * n (n + 2) / (n (n + 2) + 2), n = e^x; for
+// x > 20 the ratio is 1 in fp32 (and n^2 would overflow past x = 44).
+__device__ __forceinline__ float mish_f(float x) {
+  if (x > 20.f) return x;
+  const float n = expf(x);
+  const float t = n * (n + 2.f);
+  return x * t / (t + 2.f);
+}
+
+template <int NV, int MR, int S, bool MISH>
 __global__ __launch_bounds__(256) void head_dma_kernel(HeadP P) {
   constexpr int KC = 64;                      // k per chunk
   constexpr int ROWS = NV + MR;               // LDS rows per stage
@@ -208,16 +223,33 @@ __global__ __launch_bounds__(256) void head_dma_kernel(HeadP P) {
   for (int t = 0; t < RTW; ++t) {
     const int R = wr * (MR / 2) + 16 * t + l16;
     if (R < n_rows) {
-      float* orow = P.logits + (size_t)s_rows[R] * P.V;
+      if constexpr (MISH) {
+        uint16_t* orow = P.act + (size_t)s_rows[R] * P.V;
 #pragma unroll
-      for (int a = 0; a < VTW; ++a) {
-        const int v = v0 + (NV / 2) * wv + 16 * a + 4 * lg;
-        if (v + 3 < P.V) {
-          *reinterpret_cast<f32x4_t*>(orow + v) = acc[a][t];
-        } else {
+        for (int a = 0; a < VTW; ++a) {
+          const int v = v0 + (NV / 2) * wv + 16 * a + 4 * lg;
+          const f32x4_t y = {mish_f(acc[a][t][0]), mish_f(acc[a][t][1]), mish_f(acc[a][t][2]),
+                             mish_f(acc[a][t][3])};
+          if (v + 3 < P.V) {
+            *reinterpret_cast<uint2*>(orow + v) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+          } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (v + e < P.V) orow[v + e] = acc[a][t][e];
+            for (int e = 0; e < 4; ++e)
+              if (v + e < P.V) orow[v + e] = f32_to_bf16(y[e]);
+          }
+        }
+      } else {
+        float* orow = P.logits + (size_t)s_rows[R] * P.V;
+#pragma unroll
+        for (int a = 0; a < VTW; ++a) {
+          const int v = v0 + (NV / 2) * wv + 16 * a + 4 * lg;
+          if (v + 3 < P.V) {
+            *reinterpret_cast<f32x4_t*>(orow + v) = acc[a][t];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (v + e < P.V) orow[v + e] = acc[a][t][e];
+          }
         }
       }
     }
@@ -264,6 +296,7 @@ hipError_t launch_codebook_head(const HeadArgs& a, hipStream_t s) {
     for (int g = 0; g < 8; ++g) P.W[g] = static_cast<const uint16_t*>(g < a.G ? a.W[g] : a.W[0]);
     P.head_id = a.head_id;
     P.logits = a.logits;
+    P.act = a.act;
     P.G = a.G; P.M = a.M; P.d = a.d; P.V = a.V;
     // LDS-staged tiles of NV codebook entries x MR rows: MR in {32, 64, 128}
     // with the least row padding (the larger on ties), then the widest NV in
@@ -278,8 +311,12 @@ hipError_t launch_codebook_head(const HeadArgs& a, hipStream_t s) {
     P.nvt = (a.V + nv - 1) / nv;
     P.nvt_pad = (P.nvt + kXcds - 1) / kXcds * kXcds;
     const dim3 g((unsigned)((long)P.nvt_pad * P.row_chunks * a.G)), b(256);
-#define CLM_HEAD_DMA(NV_, MR_) \
-    if (nv == NV_ && mr == MR_) { hipLaunchKernelGGL((head_dma_kernel<NV_, MR_, 4>), g, b, 0, s, P); return hipGetLastError(); }
+#define CLM_HEAD_DMA(NV_, MR_)                                                                    \
+    if (nv == NV_ && mr == MR_) {                                                                 \
+      if (a.act) hipLaunchKernelGGL((head_dma_kernel<NV_, MR_, 4, true>), g, b, 0, s, P);         \
+      else hipLaunchKernelGGL((head_dma_kernel<NV_, MR_, 4, false>), g, b, 0, s, P);              \
+      return hipGetLastError();                                                                   \
+    }
     CLM_HEAD_DMA(128, 128) CLM_HEAD_DMA(128, 64) CLM_HEAD_DMA(128, 32)
     CLM_HEAD_DMA(64, 128) CLM_HEAD_DMA(64, 64) CLM_HEAD_DMA(64, 32)
     CLM_HEAD_DMA(32, 128) CLM_HEAD_DMA(32, 64) CLM_HEAD_DMA(32, 32)

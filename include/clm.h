@@ -12,6 +12,7 @@
  *                          ragged cache (split-KV flash decoding)
  *   clm_codebook_head      codebook logit projection, optionally grouped by
  *                          stage (one weight matrix per stage)
+ *   clm_codebook_head_mlp  the two-layer (d -> F -> Mish -> V) form of that head
  *   clm_sample_or_argmax   greedy argmax or temperature sampling per row
  *   clm_spec_verify        speculative accept/reject of K drafted tokens
  *   clm_spec_verify_bonus  the same with a bonus token after K accepts
@@ -172,6 +173,30 @@ int clm_decode_attention(const void* q, const void* k_cache, const void* v_cache
  */
 int clm_codebook_head(const void* h, const void* const* W, int G, const int32_t* head_id,
                       float* logits, int M, int d, int V, clm_dtype dt, hipStream_t stream);
+
+/*
+ * Two-layer audio head (TontaubeV1, audio head paragraph: each stage's head
+ * widens the transformer state to 4,096, applies a Mish nonlinearity and
+ * projects to that stage's audio vocabulary).  No biases.
+ *     act[r, f]    = bf16( Mish( sum_k h[r, k] * W1_{g(r)}[f, k] ) )
+ *     logits[r, v] = sum_f act[r, f] * W2_{g(r)}[v, f]
+ *     Mish(x) = x * tanh(softplus(x)),  g(r) = head_id[r] (or 0)
+ *   h        [M, d] bf16
+ *   W1, W2   host arrays of G device pointers: W1_g [F, d], W2_g [V, F], bf16
+ *   head_id  [M] int32 in [0, G), or NULL when G == 1
+ *   act      [M, F] bf16, caller-owned: written with the widened activation
+ *            (rounded to nearest even), then read by the second product
+ *   logits   [M, V] float32 output
+ * Two kernel launches on `stream`: the first product with Mish fused into its
+ * epilogue, then the second.  Arithmetic: products of bf16 accumulated in
+ * fp32; Mish in fp32.
+ * Errors: INVALID_ARG (null, sizes < 1, G > 8, head_id NULL with G > 1, h, act
+ *   or a weight not 16-byte aligned), UNSUPPORTED (dt not bf16, d or F not a
+ *   multiple of 128, M > 65536).
+ */
+int clm_codebook_head_mlp(const void* h, const void* const* W1, const void* const* W2, int G,
+                          const int32_t* head_id, void* act, float* logits, int M, int d, int F, int V,
+                          clm_dtype dt, hipStream_t stream);
 
 /*
  * One token per row (TontaubeV1 decodes later stages greedily; Section 3.3

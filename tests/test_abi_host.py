@@ -119,6 +119,16 @@ def test_workspace_size_query(lib):
     assert f(4096, 1, 16, 32, 128, 100) == 0            # more than 65536 (stream, KV head) pairs
 
 
+def test_two_layer_head_argument_errors(lib):
+    W = (C.c_void_p * 2)(0x100000, 0x200000)
+    f = lib.clm_codebook_head_mlp
+    assert f(P, W, W, 2, N, P, P, 16, 2048, 4096, 4096, 1, S) == INVALID      # G > 1 needs head_id
+    assert f(P, W, W, 1, N, N, P, 16, 2048, 4096, 4096, 1, S) == INVALID      # act missing
+    assert f(P, W, W, 1, N, P, P, 16, 2048, 4000, 4096, 1, S) == UNSUPPORTED  # F % 128
+    assert f(P, W, W, 1, N, P, P, 16, 2000, 4096, 4096, 1, S) == UNSUPPORTED  # d % 128
+    assert f(P, W, W, 1, N, P, P, 16, 2048, 4096, 4096, 0, S) == UNSUPPORTED  # fp32 not supported
+
+
 def test_head_sampler_verify_argument_errors(lib):
     Ws = (C.c_void_p * 3)(0x100000, 0x200000, 0x300000)
     assert lib.clm_codebook_head(P, Ws, 3, N, P, 64, 2048, 4096, 1, S) == INVALID   # G > 1 needs head_id

@@ -174,6 +174,26 @@ def test_codebook_head_ragged_rows(clm_gpu):
         check_close(logits.cpu().numpy(), ref, f"head M={M} V={V} G={G} d={d}")
 
 
+@pytest.mark.parametrize("M,G,V,d,F", [(16, 1, 16384, 2048, 4096), (64, 3, 4096, 2048, 4096),
+                                        (70, 2, 1000, 256, 384), (192, 1, 4096, 2048, 4096)])
+def test_codebook_head_mlp(clm_gpu, M, G, V, d, F):
+    """TontaubeV1's two-layer head (d -> F -> Mish -> V per stage): the bf16
+    activation and the logits against the oracle, including ragged row and
+    vocabulary counts and rows of three stages."""
+    rng = np.random.default_rng(M + V)
+    h = synth.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32))
+    W1 = synth.f32_to_bf16_bits((rng.standard_normal((G, F, d)) * 0.02).astype(np.float32))
+    W2 = synth.f32_to_bf16_bits((rng.standard_normal((G, V, F)) * 0.02).astype(np.float32))
+    hid = rng.integers(0, G, size=M).astype(np.int32)
+    logits, act = clm_gpu.codebook_head_mlp(to_torch(h, bf16=True), to_torch(W1, bf16=True),
+                                            to_torch(W2, bf16=True), to_torch(hid) if G > 1 else None)
+    ref_act, ref = oracle.codebook_head_mlp(synth.bf16_bits_to_f32(h), synth.bf16_bits_to_f32(W1),
+                                            synth.bf16_bits_to_f32(W2), hid)
+    check_close(bf16_tensor_to_f32(act), ref_act, f"mlp act M={M} G={G} V={V}")
+    err = check_close(logits.cpu().numpy(), ref, f"mlp logits M={M} G={G} V={V}")
+    print(f"mlp head M={M} G={G} V={V}: max abs err {err:.3g}")
+
+
 @pytest.mark.parametrize("cfg,scale", [(2, 1.0), (2, 4.0), (5, 1.0), (3, 1.0)])
 def test_sampler_isolated(clm_gpu, cfg, scale):
     import torch
