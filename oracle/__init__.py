@@ -35,6 +35,7 @@ float32, the precision the GPU kernels decide in.
 from .attention import attend, attention_weights, decode_attention
 from .head import codebook_head, codebook_head_mlp, mish
 from .kv import gather_logical, kv_cache_append
+from .rope import rope, rope_kv_cache_append
 from .sampling import argmax_token, inverse_cdf, sample_or_argmax, sample_token
 from .verify import spec_verify, spec_verify_stream, target_probs
 from .step import decode_step, round_to_bf16
@@ -43,6 +44,6 @@ __all__ = [
     "attend", "attention_weights", "decode_attention", "codebook_head",
     "gather_logical", "kv_cache_append", "argmax_token", "inverse_cdf",
     "sample_or_argmax", "sample_token", "spec_verify", "spec_verify_stream",
-    "codebook_head_mlp", "mish",
+    "codebook_head_mlp", "mish", "rope", "rope_kv_cache_append",
     "target_probs", "decode_step", "round_to_bf16",
 ]
