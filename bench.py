@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--head", choices=("linear", "mlp"), default="linear",
                     help="codebook head: one linear map per stage (the workloads' head) or TontaubeV1's "
                          "two-layer d -> 4096 -> Mish -> V head (random N(0, 0.02) weights)")
+    ap.add_argument("--append", choices=("plain", "rope"), default="plain",
+                    help="plain KV append, or the append with rotary embedding at logical positions "
+                         "(len_before + 1000 + t, base 1e6) applied to the new keys and the queries")
     ap.add_argument("--graph", choices=("on", "off"), default="off",
                     help="time the step as replays of one captured HIP graph (on) or as eager calls (off)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -264,6 +267,9 @@ def main():
         act = torch.empty((c.M, F), dtype=torch.bfloat16, device=dev)
         mlp = (W1, W2, act, F)
     max_kv = int(x.kv_len.max())
+    rope_pos = None
+    if args.append == "rope":
+        rope_pos = dev_t((x.len_before[:, None] + 1000 + np.arange(c.Kq)[None, :]).astype(np.int32), False)
     scale = 1.0 / math.sqrt(c.D)
     o = torch.empty_like(q)
     logits = torch.empty((c.M, c.V), dtype=torch.float32, device=dev)
@@ -284,7 +290,11 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        clm.kv_cache_append(k_new, v_new, k_cache, v_cache, bt, len_before, block_size=c.block_size)
+        if rope_pos is None:
+            clm.kv_cache_append(k_new, v_new, k_cache, v_cache, bt, len_before, block_size=c.block_size)
+        else:
+            clm.rope_kv_cache_append(q, k_new, v_new, k_cache, v_cache, bt, len_before, rope_pos, 1.0e6,
+                                     block_size=c.block_size)
         if ev is not None:
             ev[1].record()
         clm.decode_attention(q, k_cache, v_cache, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
@@ -393,6 +403,7 @@ def main():
             "d_model": c.d_model, "codebook": c.V, "heads": c.G, "decoding": c.mode,
             "launch": "hip_graph" if args.graph == "on" else "eager",
             "head": "linear" if mlp is None else "two-layer d->4096->Mish->V",
+            "append": "plain" if rope_pos is None else "rope at logical positions",
         },
         "roofline": {
             "bound": "hbm",
@@ -404,7 +415,7 @@ def main():
             "kernel": "decode_attention",
             "algorithmic_bytes_per_launch": attn_bytes,
         },
-        "per_call_us": {"kv_cache_append": round(per_us[0], 2), "decode_attention": round(per_us[1], 2),
+        "per_call_us": {("kv_cache_append" if rope_pos is None else "rope_kv_cache_append"): round(per_us[0], 2), "decode_attention": round(per_us[1], 2),
                         ("codebook_head" if mlp is None else "codebook_head_mlp"): round(per_us[2], 2),
                         ("spec_verify" if spec is not None else "sample_or_argmax"): round(per_us[3], 2)},
         "codebook_head_tflops": round(head_flops / (per_us[2] * 1e-6) / 1e12, 2),

@@ -21,7 +21,7 @@ from . import _lib
 from ._lib import CLM_BF16, CLM_F32, STATUS
 
 __all__ = [
-    "ClmError", "load", "kv_cache_append", "decode_attention", "decode_attention_workspace_size",
+    "ClmError", "load", "kv_cache_append", "rope_kv_cache_append", "decode_attention", "decode_attention_workspace_size",
     "codebook_head", "codebook_head_mlp", "sample_or_argmax", "spec_verify", "spec_verify_bonus",
     "Workspace",
 ]
@@ -119,6 +119,35 @@ def kv_cache_append(k_new, v_new, k_cache, v_cache, block_table, len_before, blo
     _check("clm_kv_cache_append", lib.clm_kv_cache_append(
         _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         block_table.shape[1], _ptr(len_before), B, T, H, D, block_size, nb, _dt(k_new), _stream()))
+
+
+def rope_kv_cache_append(q, k_new, v_new, k_cache, v_cache, block_table, len_before, positions,
+                         rope_base, block_size=16):
+    """kv_cache_append with rotary embedding at logical positions [B,T] int32
+    applied to the new keys (as written) and to q [B,T,H_q,D] (in place)."""
+    torch = _torch()
+    lib = load()
+    _cuda("q", q, ndim=4)
+    _cuda("k_new", k_new, q.dtype, 4)
+    _cuda("v_new", v_new, q.dtype, 4)
+    _cuda("k_cache", k_cache, q.dtype, 4)
+    _cuda("v_cache", v_cache, q.dtype, 4)
+    _cuda("block_table", block_table, torch.int32, 2)
+    _cuda("len_before", len_before, torch.int32, 1)
+    _cuda("positions", positions, torch.int32, 2)
+    B, T, H, D = k_new.shape
+    H_q = q.shape[2]
+    nb = k_cache.shape[0]
+    if tuple(q.shape) != (B, T, H_q, D) or tuple(v_new.shape) != (B, T, H, D) \
+            or tuple(k_cache.shape) != (nb, H, block_size, D) or tuple(v_cache.shape) != (nb, H, D, block_size) \
+            or tuple(positions.shape) != (B, T):
+        raise ValueError("rope_kv_cache_append: shape mismatch")
+    if block_table.shape[0] != B or len_before.shape[0] != B:
+        raise ValueError("rope_kv_cache_append: batch mismatch")
+    _check("clm_rope_kv_cache_append", lib.clm_rope_kv_cache_append(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        block_table.shape[1], _ptr(len_before), _ptr(positions), C.c_float(rope_base), B, T, H_q, H, D,
+        block_size, nb, _dt(k_new), _stream()))
 
 
 def decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len) -> int:

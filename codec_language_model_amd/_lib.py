@@ -30,6 +30,7 @@ SIGNATURES = {
     "clm_status_string": (C.c_char_p, [_i]),
     "clm_version": (_i, []),
     "clm_kv_cache_append": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "clm_rope_kv_cache_append": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _f, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "clm_decode_attention_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "clm_decode_attention": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
                                   _f, _i, _vp, _sz, _vp]),

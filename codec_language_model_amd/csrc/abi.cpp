@@ -94,6 +94,36 @@ int clm_kv_cache_append(const void* k_new, const void* v_new, void* k_cache, voi
   return hip_status(clm::launch_kv_append(a, stream));
 }
 
+int clm_rope_kv_cache_append(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* block_table, int max_blocks, const int32_t* len_before,
+                             const int32_t* positions, float rope_base, int B, int T_new, int H_q,
+                             int H_kv, int D, int block_size, int num_blocks, clm_dtype dt,
+                             hipStream_t stream) {
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !block_table || !len_before || !positions)
+    return CLM_ERR_INVALID_ARG;
+  if (B < 1 || T_new < 1 || H_q < 1 || H_kv < 1 || D < 1 || max_blocks < 1 || num_blocks < 1 ||
+      block_size < 1 || H_q % H_kv != 0)
+    return CLM_ERR_INVALID_ARG;
+  if (!std::isfinite(rope_base) || !(rope_base > 1.f)) return CLM_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(k_cache, 16)) return CLM_ERR_INVALID_ARG;
+  if (!dt_ok(dt) || (D != 64 && D != 128) || !bs_ok(block_size)) return CLM_ERR_UNSUPPORTED;
+  if ((long)T_new > (long)max_blocks * block_size) return CLM_ERR_CAPACITY;
+  if ((long)B * H_kv > (1L << 31) - 1) return CLM_ERR_UNSUPPORTED;
+  if (g_checked) {
+    const long lim = (long)max_blocks * block_size - T_new;
+    int st = run_checks(stream, [&](int* bad) {
+      hipError_t e = clm::launch_check_lengths(len_before, B, 0, (int)(lim > 0x7fffffff ? 0x7fffffff : lim), bad, stream);
+      if (e != hipSuccess) return e;
+      return clm::launch_check_block_table(block_table, len_before, B, max_blocks, T_new, block_size,
+                                           num_blocks, bad, stream);
+    });
+    if (st != CLM_OK) return st;
+  }
+  clm::RopeAppendArgs a{q, k_new, v_new, k_cache, v_cache, block_table, max_blocks, len_before, positions,
+                        rope_base, B, T_new, H_q, H_kv, D, block_size, num_blocks, dt == CLM_BF16};
+  return hip_status(clm::launch_rope_kv_append(a, stream));
+}
+
 size_t clm_decode_attention_workspace_size(int B, int Kq, int H_q, int H_kv, int D, int max_kv_len) {
   if (B < 1 || Kq < 1 || H_q < 1 || H_kv < 1 || (D != 64 && D != 128) || max_kv_len < Kq) return 0;
   clm::AttnPlan p;

@@ -20,6 +20,22 @@ struct AppendArgs {
 };
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 
+struct RopeAppendArgs {
+  void* q;                     // [B, T_new, H_q, D], rotated in place
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* len_before;
+  const int32_t* positions;    // [B, T_new] logical positions
+  float rope_base;
+  int B, T_new, H_q, H_kv, D, block_size, num_blocks;
+  bool bf16;
+};
+hipError_t launch_rope_kv_append(const RopeAppendArgs& a, hipStream_t s);
+
 struct AttnPlan {
   int split;        // tokens per work item (multiple of 64)
   int max_splits;   // ceil(max_kv_len / split)

@@ -59,6 +59,86 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendP P) {
   }
 }
 
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(uint16_t x) { return bf16_to_f32(x); }
+__device__ __forceinline__ void from_f(float x, float* p) { *p = x; }
+__device__ __forceinline__ void from_f(float x, uint16_t* p) { *p = f32_to_bf16(x); }
+
+// Rotary embedding at logical positions fused with the append (TontaubeV1:
+// positions are logical coordinates and only their differences matter; the
+// speculative-decoding blog's engine fuses the rotary embedding with the KV
+// cache write).  Per (stream, KV head) and new token t at logical position
+// p = positions[b, t]: angles a_i = p * base^(-2i/D) in fp64 (p * theta in
+// fp32 would be off by ~1e-3 rad at positions of 10^4), then pairs (i, i+D/2)
+// of the key row are rotated on their way into the cache, the value row is
+// copied as in the plain append, and the G query heads of this KV head are
+// rotated in place.
+struct RopeP {
+  AppendP a;
+  void* q;
+  const int32_t* positions;
+  int H_q, G;
+  double log_base;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_append_kernel(RopeP R) {
+  constexpr int HALF = D / 2;
+  const AppendP& P = R.a;
+  __shared__ float s_cos[HALF], s_sin[HALF];
+  const int b = blockIdx.x / P.H_kv;
+  const int h = blockIdx.x - b * P.H_kv;
+  const int lb = P.len_before[b];
+  const int32_t* bt_row = P.bt + (size_t)b * P.max_blocks;
+  const T* kn = static_cast<const T*>(P.k_new);
+  const T* vn = static_cast<const T*>(P.v_new);
+  T* kc = static_cast<T*>(P.k_cache);
+  T* vc = static_cast<T*>(P.v_cache);
+  T* qp = static_cast<T*>(R.q);
+
+  for (int t = 0; t < P.T_new; ++t) {
+    const int p = R.positions[b * P.T_new + t];
+    __syncthreads();                       // previous token's readers are done
+    if (threadIdx.x < HALF) {
+      const double th = exp(-2.0 * (double)threadIdx.x / (double)D * R.log_base);
+      const double ang = (double)p * th;
+      s_cos[threadIdx.x] = (float)cos(ang);
+      s_sin[threadIdx.x] = (float)sin(ang);
+    }
+    __syncthreads();
+    // the G query heads of this KV head, rotated in place
+    for (int e = threadIdx.x; e < R.G * HALF; e += blockDim.x) {
+      const int gi = e / HALF, i = e - (e / HALF) * HALF;
+      T* qrow = qp + ((size_t)(b * P.T_new + t) * R.H_q + h * R.G + gi) * D;
+      const float x0 = to_f(qrow[i]), x1 = to_f(qrow[i + HALF]);
+      from_f(x0 * s_cos[i] - x1 * s_sin[i], qrow + i);
+      from_f(x0 * s_sin[i] + x1 * s_cos[i], qrow + i + HALF);
+    }
+    const int pos = lb + t;
+    if (pos < 0) continue;
+    const int page = pos / P.bs;
+    if (page >= P.max_blocks) continue;
+    const int blk = bt_row[page];
+    if (blk < 0 || blk >= P.num_blocks) continue;
+    const int slot = pos - page * P.bs;
+    const T* krow = kn + ((size_t)(b * P.T_new + t) * P.H_kv + h) * D;
+    T* kdst = kc + (((size_t)blk * P.H_kv + h) * P.bs + slot) * D;
+    for (int i = threadIdx.x; i < HALF; i += blockDim.x) {
+      const float x0 = to_f(krow[i]), x1 = to_f(krow[i + HALF]);
+      from_f(x0 * s_cos[i] - x1 * s_sin[i], kdst + i);
+      from_f(x0 * s_sin[i] + x1 * s_cos[i], kdst + i + HALF);
+    }
+    for (int d = threadIdx.x; d < D; d += blockDim.x)
+      vc[(((size_t)blk * P.H_kv + h) * D + d) * P.bs + slot] = vn[((size_t)(b * P.T_new + t) * P.H_kv + h) * D + d];
+  }
+}
+
+template <typename T, int D>
+hipError_t go_rope(const RopeP& R, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((rope_append_kernel<T, D>), dim3(grid), dim3(256), 0, s, R);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t go(const AppendP& P, int grid, hipStream_t s) {
   hipLaunchKernelGGL((kv_append_kernel<T, D>), dim3(grid), dim3(256), 0, s, P);
@@ -77,6 +157,30 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s) {
   } else {
     if (a.D == 128) return go<float, 128>(P, grid, s);
     if (a.D == 64) return go<float, 64>(P, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace clm
+
+namespace clm {
+
+hipError_t launch_rope_kv_append(const RopeAppendArgs& a, hipStream_t s) {
+  RopeP R;
+  R.a = AppendP{a.k_new, a.v_new, a.k_cache, a.v_cache, a.block_table, a.len_before,
+                a.max_blocks, a.T_new, a.H_kv, a.block_size, a.num_blocks};
+  R.q = a.q;
+  R.positions = a.positions;
+  R.H_q = a.H_q;
+  R.G = a.H_q / a.H_kv;
+  R.log_base = log((double)a.rope_base);
+  const int grid = a.B * a.H_kv;
+  if (a.bf16) {
+    if (a.D == 128) return go_rope<uint16_t, 128>(R, grid, s);
+    if (a.D == 64) return go_rope<uint16_t, 64>(R, grid, s);
+  } else {
+    if (a.D == 128) return go_rope<float, 128>(R, grid, s);
+    if (a.D == 64) return go_rope<float, 64>(R, grid, s);
   }
   return hipErrorInvalidValue;
 }

@@ -8,6 +8,8 @@
  * step reads the KV cache; continuous batching over a paged cache):
  *
  *   clm_kv_cache_append    write the step's new K/V rows into the paged cache
+ *   clm_rope_kv_cache_append  the same with rotary position embedding at
+ *                          logical positions applied to the new keys and queries
  *   clm_decode_attention   single- or K-query GQA attention over each stream's
  *                          ragged cache (split-KV flash decoding)
  *   clm_codebook_head      codebook logit projection, optionally grouped by
@@ -107,6 +109,34 @@ int clm_kv_cache_append(const void* k_new, const void* v_new, void* k_cache, voi
                         const int32_t* block_table, int max_blocks, const int32_t* len_before,
                         int B, int T_new, int H_kv, int D, int block_size, int num_blocks,
                         clm_dtype dt, hipStream_t stream);
+
+/*
+ * The append with rotary position embedding at logical positions fused in
+ * (TontaubeV1: positions are logical coordinates and rotary attention depends
+ * only on their differences - the vLLM adapters add one constant to every
+ * prefill coordinate; the speculative-decoding blog, "Engine-Level
+ * Optimizations with TensorRT-LLM": rotary embedding fused with the KV-cache
+ * write).  For new token t of stream b at logical position p = positions[b,t]:
+ *     theta_i = rope_base^(-2i/D),  a_i = p * theta_i      (fp64)
+ *     (x_i, x_{i+D/2}) -> (x_i cos a_i - x_{i+D/2} sin a_i,
+ *                          x_i sin a_i + x_{i+D/2} cos a_i)   i < D/2
+ * is applied to the key row as it is written into its cache slot (the slot
+ * is len_before[b] + t, as in clm_kv_cache_append), and to q[b,t,:,:] in
+ * place; values are copied unrotated.
+ *   q          [B, T_new, H_q, D]   queries of the step's new tokens, rotated in place
+ *   positions  [B, T_new] int32     logical positions (any integers)
+ *   rope_base  host float > 1       (e.g. 1e6)
+ *   other arguments as clm_kv_cache_append; k_new is not modified
+ * Arithmetic: angles, cos and sin in fp64; rotation in fp32; results rounded
+ * to dt once.
+ * Errors: as clm_kv_cache_append, plus INVALID_ARG for null q or positions,
+ *   H_q % H_kv != 0, or rope_base not finite or <= 1.
+ */
+int clm_rope_kv_cache_append(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* block_table, int max_blocks, const int32_t* len_before,
+                             const int32_t* positions, float rope_base, int B, int T_new, int H_q,
+                             int H_kv, int D, int block_size, int num_blocks, clm_dtype dt,
+                             hipStream_t stream);
 
 /*
  * Bytes of workspace clm_decode_attention needs for these sizes (0 on a size

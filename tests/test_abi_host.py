@@ -129,6 +129,24 @@ def test_two_layer_head_argument_errors(lib):
     assert f(P, W, W, 1, N, P, P, 16, 2048, 4096, 4096, 0, S) == UNSUPPORTED  # fp32 not supported
 
 
+def test_rope_append_argument_errors(lib):
+    f = lib.clm_rope_kv_cache_append
+    args = [P, P, P, P, P, P, 8, P, P, C.c_float(1e6), 4, 1, 16, 8, 128, 16, 64, 1, S]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=N) == INVALID                       # q missing
+    assert call(a8=N) == INVALID                       # positions missing
+    assert call(a9=C.c_float(1.0)) == INVALID          # base <= 1
+    assert call(a9=C.c_float(float("nan"))) == INVALID
+    assert call(a12=12) == INVALID                     # H_q % H_kv
+    assert call(a14=96) == UNSUPPORTED                 # D
+    assert call(a15=24) == UNSUPPORTED                 # block size
+    assert call(a11=1000) == CAPACITY                  # T_new > max_blocks * bs
+
+
 def test_head_sampler_verify_argument_errors(lib):
     Ws = (C.c_void_p * 3)(0x100000, 0x200000, 0x300000)
     assert lib.clm_codebook_head(P, Ws, 3, N, P, 64, 2048, 4096, 1, S) == INVALID   # G > 1 needs head_id

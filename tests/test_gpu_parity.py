@@ -83,6 +83,49 @@ def test_kv_append_bit_exact(clm_gpu, cfg):
     np.testing.assert_array_equal(gv, rv.view(dt))
 
 
+@pytest.mark.parametrize("cfg,offset", [(1, 0), (2, 1000), (4, 37), (5, 123456)])
+def test_rope_kv_append(clm_gpu, cfg, offset):
+    """Fused rotary append at logical positions len_before + offset + t: the
+    rotated new keys in their slots and the rotated queries against the
+    oracle; values and every other slot bit-exact."""
+    import torch
+    x = inputs(cfg, SMALL_B[cfg])
+    c = x.cfg
+    bf = c.dtype == "bf16"
+    d = Dev(x, include_new=False)
+    pos = (x.len_before[:, None] + offset + np.arange(c.Kq)[None, :]).astype(np.int32)
+    base = 1.0e6
+    q = d.q.clone()
+    before_k, before_v = as_bits(d.k_cache), as_bits(d.v_cache)
+    clm_gpu.rope_kv_cache_append(q, d.k_new, d.v_new, d.k_cache, d.v_cache, d.block_table, d.len_before,
+                                 to_torch(pos), base, block_size=c.block_size)
+    kp, vp = x.build_pool(include_new=False)
+    f32 = (lambda a: synth.bf16_bits_to_f32(a)) if bf else (lambda a: a)
+    q_ref, k_ref, _ = oracle.rope_kv_cache_append(f32(x.q), f32(kp), f32(vp), x.block_table, x.len_before,
+                                                  pos, f32(x.k_new), f32(x.v_new), c.block_size, base)
+    check_close(bf16_tensor_to_f32(q), q_ref, f"rope q c{cfg}")
+    # the new rows, gathered through the block table
+    k_gpu = bf16_tensor_to_f32(d.k_cache)
+    for b in range(c.B):
+        for t in range(c.Kq):
+            p_ = int(x.len_before[b]) + t
+            blk, slot = int(x.block_table[b, p_ // c.block_size]), p_ % c.block_size
+            check_close(k_gpu[blk, :, slot, :], k_ref[blk, :, slot, :], f"rope k c{cfg} b{b} t{t}")
+    # values exactly as the plain append writes them; untouched key slots unchanged
+    kp_plain, vp_plain = x.build_pool(include_new=True)
+    v_bits = as_bits(d.v_cache)
+    np.testing.assert_array_equal(v_bits, as_bits(to_torch(vp_plain, bf16=bf)))
+    k_bits = as_bits(d.k_cache)
+    touched = np.zeros(k_bits.shape[:1] + k_bits.shape[2:3], bool)     # [nb, bs]
+    for b in range(c.B):
+        for t in range(c.Kq):
+            p_ = int(x.len_before[b]) + t
+            touched[int(x.block_table[b, p_ // c.block_size]), p_ % c.block_size] = True
+    keep = ~touched
+    np.testing.assert_array_equal(k_bits.transpose(0, 2, 1, 3)[keep], before_k.transpose(0, 2, 1, 3)[keep])
+    del torch, before_v
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_decode_attention_parity(clm_gpu, cfg):
     x = inputs(cfg, SMALL_B[cfg])
