@@ -36,6 +36,7 @@ from .attention import attend, attention_weights, decode_attention
 from .head import codebook_head, codebook_head_mlp, mish
 from .kv import gather_logical, kv_cache_append
 from .rope import rope, rope_kv_cache_append
+from . import fp8
 from .sampling import argmax_token, inverse_cdf, sample_or_argmax, sample_token
 from .verify import spec_verify, spec_verify_stream, target_probs
 from .step import decode_step, round_to_bf16
