@@ -21,7 +21,8 @@ from . import _lib
 from ._lib import CLM_BF16, CLM_F32, STATUS
 
 __all__ = [
-    "ClmError", "load", "kv_cache_append", "rope_kv_cache_append", "decode_attention", "decode_attention_workspace_size",
+    "ClmError", "load", "kv_cache_append", "rope_kv_cache_append", "kv_cache_append_fp8", "decode_attention",
+    "decode_attention_fp8", "decode_attention_workspace_size",
     "codebook_head", "codebook_head_mlp", "sample_or_argmax", "spec_verify", "spec_verify_bonus",
     "Workspace",
 ]
@@ -150,6 +151,32 @@ def rope_kv_cache_append(q, k_new, v_new, k_cache, v_cache, block_table, len_bef
         block_size, nb, _dt(k_new), _stream()))
 
 
+def kv_cache_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, len_before,
+                        block_size=16):
+    """E4M3 cache append: k_new, v_new [B,T,H_kv,D] bf16; k_cache [nb,H_kv,bs,D]
+    and v_cache [nb,H_kv,D,bs] uint8; k_scale, v_scale [nb,H_kv,bs] float32.
+    In place."""
+    torch = _torch()
+    lib = load()
+    _cuda("k_new", k_new, torch.bfloat16, 4)
+    _cuda("v_new", v_new, torch.bfloat16, 4)
+    _cuda("k_cache", k_cache, torch.uint8, 4)
+    _cuda("v_cache", v_cache, torch.uint8, 4)
+    _cuda("k_scale", k_scale, torch.float32, 3)
+    _cuda("v_scale", v_scale, torch.float32, 3)
+    _cuda("block_table", block_table, torch.int32, 2)
+    _cuda("len_before", len_before, torch.int32, 1)
+    B, T, H, D = k_new.shape
+    nb = k_cache.shape[0]
+    if tuple(v_new.shape) != (B, T, H, D) or tuple(k_cache.shape) != (nb, H, block_size, D) \
+            or tuple(v_cache.shape) != (nb, H, D, block_size) or tuple(k_scale.shape) != (nb, H, block_size) \
+            or tuple(v_scale.shape) != (nb, H, block_size):
+        raise ValueError("kv_cache_append_fp8: shape mismatch")
+    _check("clm_kv_cache_append_fp8", lib.clm_kv_cache_append_fp8(
+        _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        block_table.shape[1], _ptr(len_before), B, T, H, D, block_size, nb, _stream()))
+
+
 def decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len) -> int:
     return int(load().clm_decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len))
 
@@ -184,6 +211,35 @@ def decode_attention(q, k_cache, v_cache, block_table, kv_len, max_kv_len, scale
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(kv_len),
         int(max_kv_len), _ptr(out), B, Kq, H_q, H_kv, D, block_size, nb, C.c_float(scale), _dt(q),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, kv_len, max_kv_len, scale=None,
+                         out=None, workspace=None):
+    """Attention over the E4M3 cache: q [B,Kq,H_q,D] bf16; caches uint8 and
+    scales float32 as kv_cache_append_fp8.  Returns o [B,Kq,H_q,D] bf16."""
+    torch = _torch()
+    lib = load()
+    _cuda("q", q, torch.bfloat16, 4)
+    _cuda("k_cache", k_cache, torch.uint8, 4)
+    _cuda("v_cache", v_cache, torch.uint8, 4)
+    _cuda("k_scale", k_scale, torch.float32, 3)
+    _cuda("v_scale", v_scale, torch.float32, 3)
+    _cuda("block_table", block_table, torch.int32, 2)
+    _cuda("kv_len", kv_len, torch.int32, 1)
+    B, Kq, H_q, D = q.shape
+    nb, H_kv, bs, _ = k_cache.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len)
+    if workspace is None:
+        workspace = Workspace.get(need, q.device)
+    _check("clm_decode_attention_fp8", lib.clm_decode_attention_fp8(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        block_table.shape[1], _ptr(kv_len), int(max_kv_len), _ptr(out), B, Kq, H_q, H_kv, D, bs, nb,
+        C.c_float(scale), _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 

@@ -110,6 +110,8 @@ struct KParams {
   const int32_t* block_table;
   const int32_t* kv_len;
   void* o;
+  const float* k_scale;   // FP8 cache: [num_blocks][H_kv][bs] per-row scales
+  const float* v_scale;
   float* part_ml;   // [B][H_kv][max_splits][NR][2]   (m in log2 units, l)
   float* part_acc;  // [B][H_kv][max_splits][NR][D]
   int max_blocks, cap, B, Kq, H_q, H_kv, G, nr, bs, num_blocks, split, max_splits;
@@ -532,9 +534,22 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
 //              B = P^T (16 tokens x 16 rows: exactly the layout S came out in)
 // Per lane: 4 score, D/2 accumulator and D/8 query registers, whatever the
 // row count, where the vector kernel needs NR*D/16 accumulators per lane.
-template <int D, int NR, int BS>
+// Four E4M3 bytes -> four bf16 values in two words (exact: every E4M3 value
+// is a bf16 value), through the hardware fp8 -> f32 conversion.
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return make_uint2(pack_bf16x2(lo.x, lo.y), pack_bf16x2(hi.x, hi.y));
+}
+
+template <int D, int NR, int BS, bool F8>
 __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(KParams P) {
   typedef short bf16x4s __attribute__((ext_vector_type(4)));
+  // K/V element: bf16, or E4M3 bytes with one fp32 scale per (token, KV head)
+  using KT = typename std::conditional<F8, uint2, bf16x8_t>::type;    // 8 keys-dims per lane
+  using VTy = typename std::conditional<F8, uint32_t, uint2>::type;   // 4 tokens per lane
+  using E = typename std::conditional<F8, uint8_t, uint16_t>::type;
   constexpr int NS = D / 32;   // score MFMAs per tile
   constexpr int NJ = D / 16;   // value MFMAs per tile
   static_assert(NR <= 16, "one MFMA column block of query rows");
@@ -552,8 +567,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(KParams P) {
   const int nrow = P.nr;
 
   const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(P.q);
-  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(P.kc);
-  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(P.vc);
+  const E* __restrict__ kc = static_cast<const E*>(P.kc);
+  const E* __restrict__ vc = static_cast<const E*>(P.vc);
   uint16_t* __restrict__ op = static_cast<uint16_t*>(P.o);
 
   for (int b = tid; b < P.B; b += kThreads) s_len[b] = stream_len(P.kv_len[b], P);
@@ -630,33 +645,53 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(KParams P) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto issue = [&](int ti, bf16x8_t (&kr)[NS], uint2 (&vr)[NJ]) {
+    auto issue = [&](int ti, KT (&kr)[NS], VTy (&vr)[NJ], float4& ks, float4& vs) {
       const int tk = t0 + (ti << 4);
       const int blk = __builtin_amdgcn_readlane(my_blk, uniform(tk / bs - p0));
       const int slot0 = tk % bs;
       const size_t hb = (size_t)blk * P.H_kv + h;
-      const uint16_t* kp = kc + (hb * bs + slot0 + l16) * D + 8 * lg;
-      const uint16_t* vp = vc + hb * D * bs + (size_t)l16 * bs + slot0 + 4 * lg;
+      const E* kp = kc + (hb * bs + slot0 + l16) * D + 8 * lg;
+      const E* vp = vc + hb * D * bs + (size_t)l16 * bs + slot0 + 4 * lg;
+      if constexpr (F8) {
 #pragma unroll
-      for (int k = 0; k < NS; ++k) {
-        const uint4 w = ld_nt(reinterpret_cast<const uint4*>(kp + 32 * k));
-        kr[k] = __builtin_bit_cast(bf16x8_t, w);
+        for (int k = 0; k < NS; ++k) kr[k] = ld_nt(reinterpret_cast<const uint2*>(kp + 32 * k));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) vr[j] = ld_nt(reinterpret_cast<const uint32_t*>(vp + (size_t)16 * j * bs));
+        ks = *reinterpret_cast<const float4*>(P.k_scale + hb * bs + slot0 + 4 * lg);
+        vs = *reinterpret_cast<const float4*>(P.v_scale + hb * bs + slot0 + 4 * lg);
+      } else {
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+          const uint4 w = ld_nt(reinterpret_cast<const uint4*>(kp + 32 * k));
+          kr[k] = __builtin_bit_cast(bf16x8_t, w);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) vr[j] = ld_nt(reinterpret_cast<const uint2*>(vp + (size_t)16 * j * bs));
       }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) vr[j] = ld_nt(reinterpret_cast<const uint2*>(vp + (size_t)16 * j * bs));
     };
 
     // tk: first token of the tile; tiles past the item (tk >= t1) are
     // duplicates of its last tile and are masked entirely
-    auto compute = [&](int tk, const bf16x8_t (&kr)[NS], const uint2 (&vr)[NJ]) {
+    auto compute = [&](int tk, const KT (&kr)[NS], const VTy (&vr)[NJ], const float4& ks, const float4& vs) {
       f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < NS; ++k) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k], qf[k], S, 0, 0, 0);
+      for (int k = 0; k < NS; ++k) {
+        bf16x8_t a;
+        if constexpr (F8) {
+          const uint2 lo = fp8x4_to_bf16x4(kr[k].x), hi = fp8x4_to_bf16x4(kr[k].y);
+          a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        } else {
+          a = kr[k];
+        }
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[k], S, 0, 0, 0);
+      }
       const int lim = tk < t1 ? n_row : 0;
       const int tl = tk + 4 * lg;                 // this lane's first token
+      float kscale[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (F8) { kscale[0] = ks.x; kscale[1] = ks.y; kscale[2] = ks.z; kscale[3] = ks.w; }
       float sc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[i] = tl + i < lim ? S[i] * P.scale_log2 : -INFINITY;
+      for (int i = 0; i < 4; ++i) sc[i] = tl + i < lim ? S[i] * kscale[i] * P.scale_log2 : -INFINITY;
       float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -667,33 +702,48 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(KParams P) {
       for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
       lsum = lsum * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
       m = m_new;
-      const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
-      const bf16x4s pb = __builtin_bit_cast(bf16x4s, make_uint2(p01, p23));
       // values of slots that hold no key yet may be anything (NaN): zero them
       const int vis = tk < t1 ? n_total : 0;
-      const uint32_t keep0 = (tl < vis ? 0x0000ffffu : 0u) | (tl + 1 < vis ? 0xffff0000u : 0u);
-      const uint32_t keep1 = (tl + 2 < vis ? 0x0000ffffu : 0u) | (tl + 3 < vis ? 0xffff0000u : 0u);
+      float pv[4] = {pr[0], pr[1], pr[2], pr[3]};
+      if constexpr (F8) {                         // the value scale folds into P
+        const float vsc[4] = {vs.x, vs.y, vs.z, vs.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = tl + i < vis ? pr[i] * vsc[i] : 0.f;
+      }
+      const uint32_t p01 = pack_bf16x2(pv[0], pv[1]), p23 = pack_bf16x2(pv[2], pv[3]);
+      const bf16x4s pb = __builtin_bit_cast(bf16x4s, make_uint2(p01, p23));
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const bf16x4s va = __builtin_bit_cast(bf16x4s, make_uint2(vr[j].x & keep0, vr[j].y & keep1));
+        uint2 vw;
+        if constexpr (F8) {
+          const uint32_t keep = (tl < vis ? 0xffu : 0u) | (tl + 1 < vis ? 0xff00u : 0u) |
+                                (tl + 2 < vis ? 0xff0000u : 0u) | (tl + 3 < vis ? 0xff000000u : 0u);
+          vw = fp8x4_to_bf16x4(vr[j] & keep);
+        } else {
+          const uint32_t keep0 = (tl < vis ? 0x0000ffffu : 0u) | (tl + 1 < vis ? 0xffff0000u : 0u);
+          const uint32_t keep1 = (tl + 2 < vis ? 0x0000ffffu : 0u) | (tl + 3 < vis ? 0xffff0000u : 0u);
+          vw = make_uint2(vr[j].x & keep0, vr[j].y & keep1);
+        }
+        const bf16x4s va = __builtin_bit_cast(bf16x4s, vw);
         acc[j] = acc[j] * corr;
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[j], 0, 0, 0);
       }
     };
 
-    bf16x8_t ka[NS], kb[NS];
-    uint2 va[NJ], vb[NJ];
+    KT ka[NS], kb[NS];
+    VTy va[NJ], vb[NJ];
+    float4 ksa, vsa, ksb, vsb;
     const int last = n_tiles - 1;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see attn_split_kernel
-    issue(0, ka, va);
+    issue(0, ka, va, ksa, vsa);
     int nblk = 0;
     bf16x8_t nq[NS];
     if (next_item < total_items) fetch(next_item, nblk, nq);
     for (int ti = 0; ti <= last; ti += 2) {
-      issue(min(ti + 1, last), kb, vb);
-      compute(t0 + (ti << 4), ka, va);
-      issue(min(ti + 2, last), ka, va);
-      compute(t0 + ((ti + 1) << 4), kb, vb);
+      issue(min(ti + 1, last), kb, vb, ksb, vsb);
+      compute(t0 + (ti << 4), ka, va, ksa, vsa);
+      issue(min(ti + 2, last), ka, va, ksa, vsa);
+      compute(t0 + ((ti + 1) << 4), kb, vb, ksb, vsb);
     }
 
     // row sums: add the four lanes of each row
@@ -805,11 +855,20 @@ int device_cus() {
 template <typename T, int D, int NR>
 hipError_t launch_t(const KParams& P, int grid, hipStream_t s) {
   const bool exact = P.nr == NR;
-  if constexpr (std::is_same<T, uint16_t>::value && NR > 2) {
+  if (P.k_scale) {                       // FP8 cache: matrix-core kernel at every row count
+    if constexpr (std::is_same<T, uint16_t>::value) {
+      if (P.bs == 16)
+        hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 16, true>), dim3(grid), dim3(kThreads), 0, s, P);
+      else
+        hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 0, true>), dim3(grid), dim3(kThreads), 0, s, P);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if constexpr (std::is_same<T, uint16_t>::value && NR > 2) {
     if (P.bs == 16)
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 16>), dim3(grid), dim3(kThreads), 0, s, P);
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 16, false>), dim3(grid), dim3(kThreads), 0, s, P);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 0>), dim3(grid), dim3(kThreads), 0, s, P);
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 0, false>), dim3(grid), dim3(kThreads), 0, s, P);
   } else if (P.bs == 16 && exact)
     hipLaunchKernelGGL((attn_split_kernel<T, D, NR, 16, true>), dim3(grid), dim3(kThreads), 0, s, P);
   else if (P.bs == 16)
@@ -873,6 +932,7 @@ bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_l
 hipError_t launch_decode_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   KParams P;
   P.q = a.q; P.kc = a.k_cache; P.vc = a.v_cache;
+  P.k_scale = a.k_scale; P.v_scale = a.v_scale;
   P.block_table = a.block_table; P.kv_len = a.kv_len; P.o = a.o;
   char* ws = static_cast<char*>(a.workspace);
   P.part_ml = reinterpret_cast<float*>(ws + p.ml_offset);

@@ -36,6 +36,19 @@ struct RopeAppendArgs {
 };
 hipError_t launch_rope_kv_append(const RopeAppendArgs& a, hipStream_t s);
 
+struct Fp8AppendArgs {
+  const void* k_new;           // [B, T_new, H_kv, D] bf16
+  const void* v_new;
+  void* k_cache;               // [num_blocks, H_kv, bs, D] E4M3 bytes
+  void* v_cache;               // [num_blocks, H_kv, D, bs] E4M3 bytes
+  float* k_scale;              // [num_blocks, H_kv, bs]
+  float* v_scale;
+  const int32_t* block_table;
+  const int32_t* len_before;
+  int max_blocks, B, T_new, H_kv, D, block_size, num_blocks;
+};
+hipError_t launch_fp8_kv_append(const Fp8AppendArgs& a, hipStream_t s);
+
 struct AttnPlan {
   int split;        // tokens per work item (multiple of 64)
   int max_splits;   // ceil(max_kv_len / split)
@@ -57,6 +70,8 @@ struct AttnArgs {
   int max_blocks, max_kv_len, B, Kq, H_q, H_kv, D, block_size, num_blocks;
   float scale;
   bool bf16;
+  const float* k_scale = nullptr;   // non-null: E4M3 K/V cache with per-row scales
+  const float* v_scale = nullptr;
 };
 hipError_t launch_decode_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 

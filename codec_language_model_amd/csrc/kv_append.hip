@@ -139,6 +139,83 @@ hipError_t go_rope(const RopeP& R, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- FP8 (E4M3) cache: one scale per (token, KV head) row --------------------
+// E4M3: 4 exponent bits (bias 7), 3 mantissa bits, largest 448, subnormals
+// m * 2^-9.  Encoding of |x| <= 448, round to nearest, ties to the even code;
+// the sign bit is x's (so -0 gives 0x80).
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a < 0.015625f) {                            // below 2^-6: subnormal step 2^-9
+    const int m = (int)rintf(a * 512.0f);         // exact scaling; rint is round-half-even
+    return sign | (uint32_t)m;                    // m == 8 is 2^-6, code 0x08
+  }
+  uint32_t u = __float_as_uint(a);
+  u += 0x7FFFFu + ((u >> 20) & 1u);               // round the fp32 mantissa at bit 20, ties to even
+  const int e = (int)(u >> 23) - 127 + 7;         // 1 .. 15
+  return sign | ((uint32_t)e << 3) | ((u >> 20) & 7u);
+}
+
+// One wave quantizes one D-wide row held as D/64 values per lane: scale =
+// max|x| / 448 (1 for an all-zero row), codes of x / scale clamped to +-448.
+template <int D>
+__device__ __forceinline__ float quantize_row(const float (&x)[D / 64], uint32_t (&code)[D / 64]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = wave_max(amax);
+  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) code[i] = e4m3_rne(fminf(fmaxf(x[i] / scale, -448.0f), 448.0f));
+  return scale;
+}
+
+struct Fp8AppendP {
+  AppendP a;
+  float* k_scale;     // [num_blocks, H_kv, bs]
+  float* v_scale;
+};
+
+// One workgroup of 2 waves per (stream, KV head): wave 0 quantizes and writes
+// the key row of each new token, wave 1 the value row (transposed block).
+template <int D>
+__global__ __launch_bounds__(128) void fp8_append_kernel(Fp8AppendP F) {
+  const AppendP& P = F.a;
+  const int b = blockIdx.x / P.H_kv;
+  const int h = blockIdx.x - b * P.H_kv;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lb = P.len_before[b];
+  const int32_t* bt_row = P.bt + (size_t)b * P.max_blocks;
+  const uint16_t* src = static_cast<const uint16_t*>(w == 0 ? P.k_new : P.v_new);
+  uint8_t* kc = static_cast<uint8_t*>(P.k_cache);
+  uint8_t* vc = static_cast<uint8_t*>(P.v_cache);
+  for (int t = 0; t < P.T_new; ++t) {
+    const int pos = lb + t;
+    if (pos < 0) continue;
+    const int page = pos / P.bs;
+    if (page >= P.max_blocks) continue;
+    const int blk = bt_row[page];
+    if (blk < 0 || blk >= P.num_blocks) continue;
+    const int slot = pos - page * P.bs;
+    const uint16_t* row = src + ((size_t)(b * P.T_new + t) * P.H_kv + h) * D;
+    float x[D / 64];
+    uint32_t code[D / 64];
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) x[i] = bf16_to_f32(row[lane + 64 * i]);
+    const float scale = quantize_row<D>(x, code);
+    const size_t hb = (size_t)blk * P.H_kv + h;
+    if (w == 0) {
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) kc[(hb * P.bs + slot) * D + lane + 64 * i] = (uint8_t)code[i];
+      if (lane == 0) F.k_scale[hb * P.bs + slot] = scale;
+    } else {
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) vc[(hb * D + lane + 64 * i) * P.bs + slot] = (uint8_t)code[i];
+      if (lane == 0) F.v_scale[hb * P.bs + slot] = scale;
+    }
+  }
+}
+
 template <typename T, int D>
 hipError_t go(const AppendP& P, int grid, hipStream_t s) {
   hipLaunchKernelGGL((kv_append_kernel<T, D>), dim3(grid), dim3(256), 0, s, P);
@@ -183,6 +260,23 @@ hipError_t launch_rope_kv_append(const RopeAppendArgs& a, hipStream_t s) {
     if (a.D == 64) return go_rope<float, 64>(R, grid, s);
   }
   return hipErrorInvalidValue;
+}
+
+}  // namespace clm
+
+namespace clm {
+
+hipError_t launch_fp8_kv_append(const Fp8AppendArgs& a, hipStream_t s) {
+  Fp8AppendP F;
+  F.a = AppendP{a.k_new, a.v_new, a.k_cache, a.v_cache, a.block_table, a.len_before,
+                a.max_blocks, a.T_new, a.H_kv, a.block_size, a.num_blocks};
+  F.k_scale = a.k_scale;
+  F.v_scale = a.v_scale;
+  const dim3 grid(a.B * a.H_kv), block(128);
+  if (a.D == 128) hipLaunchKernelGGL((fp8_append_kernel<128>), grid, block, 0, s, F);
+  else if (a.D == 64) hipLaunchKernelGGL((fp8_append_kernel<64>), grid, block, 0, s, F);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace clm

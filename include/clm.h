@@ -12,6 +12,8 @@
  *                          logical positions applied to the new keys and queries
  *   clm_decode_attention   single- or K-query GQA attention over each stream's
  *                          ragged cache (split-KV flash decoding)
+ *   clm_kv_cache_append_fp8, clm_decode_attention_fp8
+ *                          the same two calls for an FP8 (E4M3) cache
  *   clm_codebook_head      codebook logit projection, optionally grouped by
  *                          stage (one weight matrix per stage)
  *   clm_codebook_head_mlp  the two-layer (d -> F -> Mish -> V) form of that head
@@ -183,6 +185,44 @@ int clm_decode_attention(const void* q, const void* k_cache, const void* v_cache
                          int max_kv_len, void* o, int B, int Kq, int H_q, int H_kv, int D,
                          int block_size, int num_blocks, float scale, clm_dtype dt,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * FP8 (E4M3) KV cache (the speculative-decoding blog, "Engine-Level
+ * Optimizations with TensorRT-LLM": FP8 quantization of the target model's
+ * attention; here applied to the KV cache every step reads, halving its
+ * bytes).  Layout as the bf16 cache with one byte per element, plus one fp32
+ * scale per (block, KV head, slot) for keys and for values:
+ *   k_cache [num_blocks, H_kv, block_size, D]  E4M3 codes (uint8)
+ *   v_cache [num_blocks, H_kv, D, block_size]  E4M3 codes, transposed per block
+ *   k_scale, v_scale [num_blocks, H_kv, block_size] float32, 16-byte aligned
+ * E4M3: 4 exponent bits (bias 7), 3 mantissa bits, largest 448, no
+ * infinities.  A stored row x (D values of one token and KV head) is
+ *   scale = max|x| / 448 (1 if all zero),  code_i = E4M3(clamp(x_i / scale, +-448))
+ * rounded to nearest with ties to the even code, and reads back as
+ * decode(code_i) * scale.
+ *
+ * clm_kv_cache_append_fp8: clm_kv_cache_append for this cache; k_new, v_new
+ * are bf16 [B, T_new, H_kv, D], quantized as written.  Errors as
+ * clm_kv_cache_append (dt is bf16 implicitly).
+ */
+int clm_kv_cache_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            float* k_scale, float* v_scale, const int32_t* block_table, int max_blocks,
+                            const int32_t* len_before, int B, int T_new, int H_kv, int D, int block_size,
+                            int num_blocks, hipStream_t stream);
+
+/*
+ * clm_decode_attention over the FP8 cache: q and o bf16, the same visibility,
+ * scale and split plan (workspace: clm_decode_attention_workspace_size).
+ * Keys and values are decoded to bf16 exactly in registers; scores are
+ * multiplied by the key scales and probabilities by the value scales, all in
+ * fp32.  Errors as clm_decode_attention, plus INVALID_ARG for a null or
+ * misaligned scale array.
+ */
+int clm_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                             const float* v_scale, const int32_t* block_table, int max_blocks,
+                             const int32_t* kv_len, int max_kv_len, void* o, int B, int Kq, int H_q, int H_kv,
+                             int D, int block_size, int num_blocks, float scale, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Codebook logit projection (TontaubeV1, audio head paragraph: each stage owns

@@ -1,0 +1,109 @@
+"""GPU parity of the FP8 (E4M3) KV cache: the quantizing append bit-exact
+against the oracle's quantizer, and attention over the FP8 cache against the
+oracle's attention on the dequantized rows.  Empty slots hold NaN codes and
+NaN scales, so any read of them shows."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import fp8
+from parity import bf16_tensor_to_f32, check_close, to_torch
+
+pytestmark = pytest.mark.gpu
+
+SMALL_B = {2: None, 3: 16, 4: None, 5: 24}
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-case] {request.node.nodeid}", file=sys.stderr, flush=True)
+    yield
+
+
+def fp8_pool(x, include_new):
+    """The bf16 synthetic pool quantized row by row (oracle quantizer); empty
+    slots become NaN codes with NaN scales."""
+    kp, vp = x.build_pool(include_new=include_new)
+    kf = synth.bf16_bits_to_f32(kp)                               # [nb, H, bs, D]
+    vf = synth.bf16_bits_to_f32(vp).transpose(0, 1, 3, 2)         # [nb, H, bs, D]
+    out = []
+    for rows in (kf, vf):
+        empty = np.isnan(rows).any(axis=-1)
+        codes, scale = fp8.quantize_rows(np.where(empty[..., None], 0.0, rows).astype(np.float32))
+        codes[empty] = 0x7F
+        scale = scale.astype(np.float32)
+        scale[empty] = np.nan
+        out.append((codes, scale))
+    (kc, ks), (vc, vs) = out
+    return kc, np.ascontiguousarray(vc.transpose(0, 1, 3, 2)), ks, vs
+
+
+def dev(a):
+    return to_torch(np.ascontiguousarray(a))
+
+
+@pytest.mark.parametrize("cfg", [2, 4, 5])
+def test_fp8_append_bit_exact(clm_gpu, cfg):
+    import torch
+    x = synth.make_inputs(cfg, B=SMALL_B[cfg])
+    c = x.cfg
+    kc, vc, ks, vs = fp8_pool(x, include_new=False)
+    dk, dv, dks, dvs = dev(kc), dev(vc), dev(ks), dev(vs)
+    clm_gpu.kv_cache_append_fp8(to_torch(x.k_new, bf16=True), to_torch(x.v_new, bf16=True), dk, dv, dks, dvs,
+                                dev(x.block_table), dev(x.len_before), block_size=c.block_size)
+    rk, rv, rks, rvs = fp8.fp8_kv_cache_append(kc, vc, ks, vs, x.block_table, x.len_before,
+                                               synth.bf16_bits_to_f32(x.k_new), synth.bf16_bits_to_f32(x.v_new),
+                                               c.block_size)
+    np.testing.assert_array_equal(dk.cpu().numpy(), rk)
+    np.testing.assert_array_equal(dv.cpu().numpy(), rv)
+    np.testing.assert_array_equal(dks.cpu().numpy().view(np.uint32), rks.view(np.uint32))
+    np.testing.assert_array_equal(dvs.cpu().numpy().view(np.uint32), rvs.view(np.uint32))
+    del torch
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_fp8_attention_parity(clm_gpu, cfg):
+    x = synth.make_inputs(cfg, B=SMALL_B[cfg])
+    c = x.cfg
+    kc, vc, ks, vs = fp8_pool(x, include_new=True)
+    scale = 1.0 / math.sqrt(c.D)
+    o = clm_gpu.decode_attention_fp8(to_torch(x.q, bf16=True), dev(kc), dev(vc), dev(ks), dev(vs),
+                                     dev(x.block_table), dev(x.kv_len), int(x.kv_len.max()), scale=scale)
+    keys, vals = [], []
+    for b in range(c.B):
+        K, V = fp8.gather_dequantized(kc, vc, ks, vs, x.block_table, b, int(x.kv_len[b]), c.block_size)
+        keys.append(K)
+        vals.append(V)
+    ref = oracle.decode_attention(synth.bf16_bits_to_f32(x.q), keys, vals, x.kv_len, scale, c.H_kv)
+    err = check_close(bf16_tensor_to_f32(o), ref, f"fp8 attention c{cfg}")
+    print(f"fp8 attention c{cfg}: max abs err {err:.3g}")
+
+
+def test_fp8_append_then_attention(clm_gpu):
+    """The chained pair: quantizing append of the step's rows, then attention
+    over the cache that now holds them."""
+    x = synth.make_inputs(4)
+    c = x.cfg
+    kc, vc, ks, vs = fp8_pool(x, include_new=False)
+    dk, dv, dks, dvs = dev(kc), dev(vc), dev(ks), dev(vs)
+    bt, kl = dev(x.block_table), dev(x.kv_len)
+    clm_gpu.kv_cache_append_fp8(to_torch(x.k_new, bf16=True), to_torch(x.v_new, bf16=True), dk, dv, dks, dvs,
+                                bt, dev(x.len_before), block_size=c.block_size)
+    scale = 1.0 / math.sqrt(c.D)
+    o = clm_gpu.decode_attention_fp8(to_torch(x.q, bf16=True), dk, dv, dks, dvs, bt, kl, int(x.kv_len.max()),
+                                     scale=scale)
+    rk, rv, rks, rvs = fp8.fp8_kv_cache_append(kc, vc, ks, vs, x.block_table, x.len_before,
+                                               synth.bf16_bits_to_f32(x.k_new), synth.bf16_bits_to_f32(x.v_new),
+                                               c.block_size)
+    keys, vals = [], []
+    for b in range(c.B):
+        K, V = fp8.gather_dequantized(rk, rv, rks, rvs, x.block_table, b, int(x.kv_len[b]), c.block_size)
+        keys.append(K)
+        vals.append(V)
+    ref = oracle.decode_attention(synth.bf16_bits_to_f32(x.q), keys, vals, x.kv_len, scale, c.H_kv)
+    check_close(bf16_tensor_to_f32(o), ref, "fp8 append + attention c4")
