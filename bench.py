@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--head", choices=("linear", "mlp"), default="linear",
                     help="codebook head: one linear map per stage (the workloads' head) or TontaubeV1's "
                          "two-layer d -> 4096 -> Mish -> V head (random N(0, 0.02) weights)")
+    ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16",
+                    help="KV cache element: the workloads' bf16, or E4M3 bytes with per-row scales "
+                         "(random codes and scales of the same shapes)")
     ap.add_argument("--append", choices=("plain", "rope"), default="plain",
                     help="plain KV append, or the append with rotary embedding at logical positions "
                          "(len_before + 1000 + t, base 1e6) applied to the new keys and the queries")
@@ -74,11 +77,13 @@ def parse():
     return ap.parse_args()
 
 
-def attention_bytes(cfg, kv_len):
+def attention_bytes(cfg, kv_len, fp8=False):
     """Algorithmic bytes of one decode_attention launch: every visible K and V
-    row once (2 * H_kv * D * elem bytes per token), q read once, o written once."""
+    row once (2 * H_kv * D * elem bytes per token, plus its fp32 scale with an
+    FP8 cache), q read once, o written once."""
     e = 2 if cfg.dtype == "bf16" else 4
-    kv = int(kv_len.astype("int64").sum()) * 2 * cfg.H_kv * cfg.D * e
+    row = cfg.D + 4 if fp8 else cfg.D * e
+    kv = int(kv_len.astype("int64").sum()) * 2 * cfg.H_kv * row
     qo = 2 * cfg.B * cfg.Kq * cfg.H_q * cfg.D * e
     return kv + qo
 
@@ -250,6 +255,25 @@ def main():
         return t.to(dev)
 
     k_cache, v_cache = dev_t(kp, bf), dev_t(vp, bf)
+    f8 = None
+    if args.kv == "fp8":
+        if not bf:
+            print("--kv fp8 needs a bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        # synthetic E4M3 cache of the pool's shapes: uniform codes without the
+        # two NaN codes, row scales uniform in [0.002, 0.01] (max|x|/448 for
+        # rows of N(0,1) values is ~0.007)
+        g = torch.Generator(device=dev).manual_seed(4321)
+        def codes(shape):
+            cde = torch.randint(0, 254, shape, generator=g, device=dev, dtype=torch.int32)
+            cde = cde + (cde >= 0x7F).to(torch.int32)
+            return cde.to(torch.uint8)
+        nb_, hk_, bs_ = kp.shape[0], kp.shape[1], kp.shape[2]
+        f8 = (codes((nb_, hk_, c.D // 8, bs_, 8)), codes(tuple(vp.shape)),
+              torch.empty((nb_, hk_, bs_), device=dev).uniform_(0.002, 0.01, generator=g),
+              torch.empty((nb_, hk_, bs_), device=dev).uniform_(0.002, 0.01, generator=g))
+        del k_cache, v_cache
+        k_cache = v_cache = None
     del kp, vp
     bt, kv_len, len_before = dev_t(x.block_table, False), dev_t(x.kv_len, False), dev_t(x.len_before, False)
     k_new, v_new, q = dev_t(x.k_new, bf), dev_t(x.v_new, bf), dev_t(x.q, bf)
@@ -290,14 +314,19 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        if rope_pos is None:
+        if f8 is not None:
+            clm.kv_cache_append_fp8(k_new, v_new, *f8, bt, len_before, block_size=c.block_size)
+        elif rope_pos is None:
             clm.kv_cache_append(k_new, v_new, k_cache, v_cache, bt, len_before, block_size=c.block_size)
         else:
             clm.rope_kv_cache_append(q, k_new, v_new, k_cache, v_cache, bt, len_before, rope_pos, 1.0e6,
                                      block_size=c.block_size)
         if ev is not None:
             ev[1].record()
-        clm.decode_attention(q, k_cache, v_cache, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
+        if f8 is None:
+            clm.decode_attention(q, k_cache, v_cache, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
+        else:
+            clm.decode_attention_fp8(q, *f8, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
         if ev is not None:
             ev[2].record()
         if mlp is None:
@@ -360,9 +389,9 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = c.B * c.Kq / (wall / args.steps)
     attn_s = per_us[1] * 1e-6
-    attn_bytes = attention_bytes(c, x.kv_len)
+    attn_bytes = attention_bytes(c, x.kv_len, fp8=f8 is not None)
     achieved = attn_bytes / attn_s / 1e9
-    traffic = traffic_for_current_kernel()
+    traffic = traffic_for_current_kernel() if f8 is None else None
     log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; per call (us): append {per_us[0]:.1f}, "
         f"attention {per_us[1]:.1f}, head {per_us[2]:.1f}, token {per_us[3]:.1f}; attention "
         f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
@@ -394,7 +423,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if bf else "f32",
+        "dtype": ("bf16" if bf else "f32") if f8 is None else "bf16 q/o, e4m3 kv",
         "data": "synthetic (seeded N(0,1) q/K/V, N(0,0.02) head weights; no dataset or checkpoint)",
         "config": {
             "workload": c.workload,
@@ -404,6 +433,7 @@ def main():
             "launch": "hip_graph" if args.graph == "on" else "eager",
             "head": "linear" if mlp is None else "two-layer d->4096->Mish->V",
             "append": "plain" if rope_pos is None else "rope at logical positions",
+            "kv_cache": "bf16" if f8 is None else "e4m3 + fp32 row scales",
         },
         "roofline": {
             "bound": "hbm",

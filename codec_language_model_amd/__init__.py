@@ -153,14 +153,14 @@ def rope_kv_cache_append(q, k_new, v_new, k_cache, v_cache, block_table, len_bef
 
 def kv_cache_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, len_before,
                         block_size=16):
-    """E4M3 cache append: k_new, v_new [B,T,H_kv,D] bf16; k_cache [nb,H_kv,bs,D]
-    and v_cache [nb,H_kv,D,bs] uint8; k_scale, v_scale [nb,H_kv,bs] float32.
-    In place."""
+    """E4M3 cache append: k_new, v_new [B,T,H_kv,D] bf16; k_cache
+    [nb,H_kv,D/8,bs,8] and v_cache [nb,H_kv,D,bs] uint8; k_scale, v_scale
+    [nb,H_kv,bs] float32.  In place."""
     torch = _torch()
     lib = load()
     _cuda("k_new", k_new, torch.bfloat16, 4)
     _cuda("v_new", v_new, torch.bfloat16, 4)
-    _cuda("k_cache", k_cache, torch.uint8, 4)
+    _cuda("k_cache", k_cache, torch.uint8, 5)
     _cuda("v_cache", v_cache, torch.uint8, 4)
     _cuda("k_scale", k_scale, torch.float32, 3)
     _cuda("v_scale", v_scale, torch.float32, 3)
@@ -168,7 +168,7 @@ def kv_cache_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_
     _cuda("len_before", len_before, torch.int32, 1)
     B, T, H, D = k_new.shape
     nb = k_cache.shape[0]
-    if tuple(v_new.shape) != (B, T, H, D) or tuple(k_cache.shape) != (nb, H, block_size, D) \
+    if tuple(v_new.shape) != (B, T, H, D) or tuple(k_cache.shape) != (nb, H, D // 8, block_size, 8) \
             or tuple(v_cache.shape) != (nb, H, D, block_size) or tuple(k_scale.shape) != (nb, H, block_size) \
             or tuple(v_scale.shape) != (nb, H, block_size):
         raise ValueError("kv_cache_append_fp8: shape mismatch")
@@ -221,14 +221,17 @@ def decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, kv_
     torch = _torch()
     lib = load()
     _cuda("q", q, torch.bfloat16, 4)
-    _cuda("k_cache", k_cache, torch.uint8, 4)
+    _cuda("k_cache", k_cache, torch.uint8, 5)
     _cuda("v_cache", v_cache, torch.uint8, 4)
     _cuda("k_scale", k_scale, torch.float32, 3)
     _cuda("v_scale", v_scale, torch.float32, 3)
     _cuda("block_table", block_table, torch.int32, 2)
     _cuda("kv_len", kv_len, torch.int32, 1)
     B, Kq, H_q, D = q.shape
-    nb, H_kv, bs, _ = k_cache.shape
+    nb, H_kv, _, bs, _ = k_cache.shape
+    if tuple(k_cache.shape) != (nb, H_kv, D // 8, bs, 8) or tuple(v_cache.shape) != (nb, H_kv, D, bs) \
+            or tuple(k_scale.shape) != (nb, H_kv, bs) or tuple(v_scale.shape) != (nb, H_kv, bs):
+        raise ValueError("decode_attention_fp8: shape mismatch")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:

@@ -544,7 +544,7 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
 }
 
 template <int D, int NR, int BS, bool F8>
-__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(KParams P) {
+__global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
   typedef short bf16x4s __attribute__((ext_vector_type(4)));
   // K/V element: bf16, or E4M3 bytes with one fp32 scale per (token, KV head)
   using KT = typename std::conditional<F8, uint2, bf16x8_t>::type;    // 8 keys-dims per lane
@@ -653,8 +653,12 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(KParams P) {
       const E* kp = kc + (hb * bs + slot0 + l16) * D + 8 * lg;
       const E* vp = vc + hb * D * bs + (size_t)l16 * bs + slot0 + 4 * lg;
       if constexpr (F8) {
+        // keys in 8-dimension groups [block][head][d/8][slot][8]: lane (token
+        // l%16, group 4k + l/16) reads 8 bytes, and one instruction reads 4
+        // whole groups of the tile's 16 keys (512 contiguous bytes at bs 16)
+        const E* kg = kc + ((hb * (D / 8) + lg) * bs + slot0 + l16) * 8;
 #pragma unroll
-        for (int k = 0; k < NS; ++k) kr[k] = ld_nt(reinterpret_cast<const uint2*>(kp + 32 * k));
+        for (int k = 0; k < NS; ++k) kr[k] = ld_nt(reinterpret_cast<const uint2*>(kg + (size_t)32 * k * bs));
 #pragma unroll
         for (int j = 0; j < NJ; ++j) vr[j] = ld_nt(reinterpret_cast<const uint32_t*>(vp + (size_t)16 * j * bs));
         ks = *reinterpret_cast<const float4*>(P.k_scale + hb * bs + slot0 + 4 * lg);
@@ -730,20 +734,32 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(KParams P) {
       }
     };
 
-    KT ka[NS], kb[NS];
-    VTy va[NJ], vb[NJ];
-    float4 ksa, vsa, ksb, vsb;
+    // TPS tiles per pipeline stage: an FP8 tile is half the bytes of a bf16
+    // one, so two are staged together to keep as many bytes in flight
+    constexpr int TPS = F8 ? 2 : 1;
+    KT ka[TPS][NS], kb[TPS][NS];
+    VTy va[TPS][NJ], vb[TPS][NJ];
+    float4 ksa[TPS], vsa[TPS], ksb[TPS], vsb[TPS];
     const int last = n_tiles - 1;
+    auto issue_s = [&](int ti0, KT (&kr)[TPS][NS], VTy (&vr)[TPS][NJ], float4 (&ks)[TPS], float4 (&vs)[TPS]) {
+#pragma unroll
+      for (int u = 0; u < TPS; ++u) issue(min(ti0 + u, last), kr[u], vr[u], ks[u], vs[u]);
+    };
+    auto compute_s = [&](int ti0, const KT (&kr)[TPS][NS], const VTy (&vr)[TPS][NJ], const float4 (&ks)[TPS],
+                         const float4 (&vs)[TPS]) {
+#pragma unroll
+      for (int u = 0; u < TPS; ++u) compute(t0 + ((ti0 + u) << 4), kr[u], vr[u], ks[u], vs[u]);
+    };
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see attn_split_kernel
-    issue(0, ka, va, ksa, vsa);
+    issue_s(0, ka, va, ksa, vsa);
     int nblk = 0;
     bf16x8_t nq[NS];
     if (next_item < total_items) fetch(next_item, nblk, nq);
-    for (int ti = 0; ti <= last; ti += 2) {
-      issue(min(ti + 1, last), kb, vb, ksb, vsb);
-      compute(t0 + (ti << 4), ka, va, ksa, vsa);
-      issue(min(ti + 2, last), ka, va, ksa, vsa);
-      compute(t0 + ((ti + 1) << 4), kb, vb, ksb, vsb);
+    for (int ti = 0; ti <= last; ti += 2 * TPS) {
+      issue_s(ti + TPS, kb, vb, ksb, vsb);
+      compute_s(ti, ka, va, ksa, vsa);
+      issue_s(ti + 2 * TPS, ka, va, ksa, vsa);
+      compute_s(ti + TPS, kb, vb, ksb, vsb);
     }
 
     // row sums: add the four lanes of each row

@@ -39,7 +39,7 @@ hipError_t launch_rope_kv_append(const RopeAppendArgs& a, hipStream_t s);
 struct Fp8AppendArgs {
   const void* k_new;           // [B, T_new, H_kv, D] bf16
   const void* v_new;
-  void* k_cache;               // [num_blocks, H_kv, bs, D] E4M3 bytes
+  void* k_cache;               // [num_blocks, H_kv, D/8, bs, 8] E4M3 bytes
   void* v_cache;               // [num_blocks, H_kv, D, bs] E4M3 bytes
   float* k_scale;              // [num_blocks, H_kv, bs]
   float* v_scale;

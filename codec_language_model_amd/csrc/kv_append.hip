@@ -205,8 +205,12 @@ __global__ __launch_bounds__(128) void fp8_append_kernel(Fp8AppendP F) {
     const float scale = quantize_row<D>(x, code);
     const size_t hb = (size_t)blk * P.H_kv + h;
     if (w == 0) {
+      // keys in 8-dimension groups: [block][head][d / 8][slot][d % 8]
 #pragma unroll
-      for (int i = 0; i < D / 64; ++i) kc[(hb * P.bs + slot) * D + lane + 64 * i] = (uint8_t)code[i];
+      for (int i = 0; i < D / 64; ++i) {
+        const int d = lane + 64 * i;
+        kc[((hb * (D / 8) + (d >> 3)) * P.bs + slot) * 8 + (d & 7)] = (uint8_t)code[i];
+      }
       if (lane == 0) F.k_scale[hb * P.bs + slot] = scale;
     } else {
 #pragma unroll

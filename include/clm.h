@@ -190,9 +190,10 @@ int clm_decode_attention(const void* q, const void* k_cache, const void* v_cache
  * FP8 (E4M3) KV cache (the speculative-decoding blog, "Engine-Level
  * Optimizations with TensorRT-LLM": FP8 quantization of the target model's
  * attention; here applied to the KV cache every step reads, halving its
- * bytes).  Layout as the bf16 cache with one byte per element, plus one fp32
- * scale per (block, KV head, slot) for keys and for values:
- *   k_cache [num_blocks, H_kv, block_size, D]  E4M3 codes (uint8)
+ * bytes).  One byte per element, plus one fp32 scale per (block, KV head,
+ * slot) for keys and for values:
+ *   k_cache [num_blocks, H_kv, D/8, block_size, 8]  E4M3 codes (uint8): keys
+ *           in 8-dimension groups, each group of a block's keys contiguous
  *   v_cache [num_blocks, H_kv, D, block_size]  E4M3 codes, transposed per block
  *   k_scale, v_scale [num_blocks, H_kv, block_size] float32, 16-byte aligned
  * E4M3: 4 exponent bits (bias 7), 3 mantissa bits, largest 448, no

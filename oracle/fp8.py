@@ -14,8 +14,10 @@ subnormals (-1)^s 2^-6 (m/8) for e = 0.
 A row x (one token's D values of one KV head) is stored as
   scale = max|x| / 448            (1 when the row is all zero)
   code_i = E4M3( x_i / scale )    round to nearest, ties to even
-and read back as decode(code_i) * scale.  Readings where the page leaves a
-step open: the E4M3 variant, one fp32 scale per (token, KV head) row for keys
+and read back as decode(code_i) * scale.  Cache layout: keys as 8-dimension
+groups, k_pool[block, head, d // 8, slot, d % 8] (each group of a block's
+keys contiguous), values transposed as in the bf16 cache, v_pool[block,
+head, d, slot].  Readings where the page leaves a step open: the E4M3 variant, one fp32 scale per (token, KV head) row for keys
 and for values, the scale and the division in float32, and the quotient
 clamped to +-448 before rounding.
 """
@@ -85,8 +87,9 @@ def dequantize_rows(codes, scale):
 def fp8_kv_cache_append(k_pool, v_pool, k_scale, v_scale, block_table, len_before, k_new, v_new,
                         block_size):
     """Quantize the new rows and write them into copies of the fp8 pool:
-    k_pool [nb, H, bs, D] uint8, v_pool [nb, H, D, bs] uint8, k_scale and
-    v_scale [nb, H, bs] float32; k_new, v_new [B, T, H, D] (float32 values)."""
+    k_pool [nb, H, D/8, bs, 8] uint8, v_pool [nb, H, D, bs] uint8, k_scale
+    and v_scale [nb, H, bs] float32; k_new, v_new [B, T, H, D] (float32
+    values)."""
     k, v = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
     ks, vs = np.array(k_scale, copy=True), np.array(v_scale, copy=True)
     kq, kscale = quantize_rows(k_new)
@@ -97,7 +100,7 @@ def fp8_kv_cache_append(k_pool, v_pool, k_scale, v_scale, block_table, len_befor
             pos = int(len_before[b]) + t
             blk = int(block_table[b, pos // block_size])
             slot = pos % block_size
-            k[blk, :, slot, :] = kq[b, t]
+            k[blk, :, :, slot, :] = kq[b, t].reshape(kq.shape[2], -1, 8)
             v[blk, :, :, slot] = vq[b, t]
             ks[blk, :, slot] = kscale[b, t]
             vs[blk, :, slot] = vscale[b, t]
@@ -106,12 +109,12 @@ def fp8_kv_cache_append(k_pool, v_pool, k_scale, v_scale, block_table, len_befor
 
 def gather_dequantized(k_pool, v_pool, k_scale, v_scale, block_table, b, n, block_size):
     """Stream b's first n positions as dequantized K, V [n, H, D] float64."""
-    H, D = k_pool.shape[1], k_pool.shape[3]
+    H, D = k_pool.shape[1], k_pool.shape[2] * k_pool.shape[4]
     K = np.empty((n, H, D))
     V = np.empty((n, H, D))
     for pos in range(n):
         blk = int(block_table[b, pos // block_size])
         slot = pos % block_size
-        K[pos] = dequantize_rows(k_pool[blk, :, slot, :], k_scale[blk, :, slot])
+        K[pos] = dequantize_rows(k_pool[blk, :, :, slot, :].reshape(H, D), k_scale[blk, :, slot])
         V[pos] = dequantize_rows(v_pool[blk, :, :, slot], v_scale[blk, :, slot])
     return K, V

@@ -26,8 +26,9 @@ def _announce(request):
 
 
 def fp8_pool(x, include_new):
-    """The bf16 synthetic pool quantized row by row (oracle quantizer); empty
-    slots become NaN codes with NaN scales."""
+    """The bf16 synthetic pool quantized row by row (oracle quantizer), keys in
+    the grouped layout [nb, H, D/8, bs, 8]; empty slots become NaN codes with
+    NaN scales."""
     kp, vp = x.build_pool(include_new=include_new)
     kf = synth.bf16_bits_to_f32(kp)                               # [nb, H, bs, D]
     vf = synth.bf16_bits_to_f32(vp).transpose(0, 1, 3, 2)         # [nb, H, bs, D]
@@ -40,6 +41,8 @@ def fp8_pool(x, include_new):
         scale[empty] = np.nan
         out.append((codes, scale))
     (kc, ks), (vc, vs) = out
+    nb, H, bs, D = kc.shape
+    kc = np.ascontiguousarray(kc.reshape(nb, H, bs, D // 8, 8).transpose(0, 1, 3, 2, 4))   # [nb, H, D/8, bs, 8]
     return kc, np.ascontiguousarray(vc.transpose(0, 1, 3, 2)), ks, vs
 
 

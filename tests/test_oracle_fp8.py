@@ -79,7 +79,7 @@ def test_fp8_append_and_attention_on_exactly_representable_rows():
         a[..., 0] = 448.0
         return (a / 64.0).astype(np.float32)
     nb = x.block_table.max() + 1
-    kp = np.zeros((nb, c.H_kv, c.block_size, c.D), np.uint8)
+    kp = np.zeros((nb, c.H_kv, c.D // 8, c.block_size, 8), np.uint8)
     vp = np.zeros((nb, c.H_kv, c.D, c.block_size), np.uint8)
     ks = np.ones((nb, c.H_kv, c.block_size), np.float32)
     vs = np.ones((nb, c.H_kv, c.block_size), np.float32)
