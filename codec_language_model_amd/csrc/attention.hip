@@ -13,10 +13,10 @@
 // bytes, so every K/V byte is read from HBM once per step.  The grid is
 // persistent: every workgroup rebuilds the item numbering from kv_len once
 // (stream lengths and prefix sums in LDS) - first every full-size split of
-// every stream, then each stream's shorter last split - and its waves take
-// items round-robin over the grid's waves.  (A shared ticket counter balanced
-// the tail better but cost more: device-wide atomics on one address serialise
-// across the chip.)  While a wave streams one item it already loads the next
+// every stream, then each stream's shorter last split, longest first - and
+// its waves take items in a snake order over the grid's waves.  (A shared
+// ticket counter balanced the tail better but cost more: device-wide atomics
+// on one address serialise across the chip.)  While a wave streams one item it already loads the next
 // item's block ids and query slice.  No barrier, LDS access or cross-wave
 // traffic in the main loop.
 //
@@ -296,15 +296,20 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
     }
   };
 
-  // Items go round-robin over the grid's waves (full-size splits first); the
-  // next item's block ids and query slice are loaded while this one streams.
-  int item = blockIdx.x * kWaves + (tid >> 6);
+  // The next item's block ids and query slice are loaded while this one
+  // streams.  Snake deal: round r gives wave w item r*nw + (r even ? w : nw-1-w).  The
+  // items are ordered longest first, so the waves that took the longest
+  // items of one round take the shortest of the next.
+  const int my_w = blockIdx.x * kWaves + (tid >> 6);
+  int round_ = 0;
+  auto deal = [&](int r) { return r * nw_total + ((r & 1) ? nw_total - 1 - my_w : my_w); };
+  int item = deal(0);
   int my_blk = 0;
   uint32_t qw[NR][4 * CPL];
   if (item < total_items) fetch(item, my_blk, qw);
 
   while (item < total_items) {
-    const int next_item = item + nw_total;
+    const int next_item = deal(++round_);
     int b, s, h;
     locate(item, b, s, h);
     const int n_total = s_len[b];
@@ -622,13 +627,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
     }
   };
 
-  int item = blockIdx.x * kWaves + (tid >> 6);
+  // Snake deal: round r gives wave w item r*nw + (r even ? w : nw-1-w).  The
+  // items are ordered longest first, so the waves that took the longest
+  // items of one round take the shortest of the next.
+  const int my_w = blockIdx.x * kWaves + (tid >> 6);
+  int round_ = 0;
+  auto deal = [&](int r) { return r * nw_total + ((r & 1) ? nw_total - 1 - my_w : my_w); };
+  int item = deal(0);
   int my_blk = 0;
   bf16x8_t qf[NS];
   if (item < total_items) fetch(item, my_blk, qf);
 
   while (item < total_items) {
-    const int next_item = item + nw_total;
+    const int next_item = deal(++round_);
     int b, s, h;
     locate(item, b, s, h);
     const int n_total = s_len[b];
