@@ -133,7 +133,7 @@ __device__ void block_prefix(int* s, int* s_wsum, int B, F count) {
   int local = 0;
   for (int k = 0; k < per; ++k)
     if (b0 + k < B) local += count(b0 + k);
-  const int incl = wave_incl_scan_i(local, lane);
+  const int incl = wave_incl_scan_i(local);
   if (lane == 63) s_wsum[w] = incl;
   __syncthreads();
   int run = incl - local;
@@ -179,7 +179,7 @@ __device__ int short_splits_sorted(int* s, int (*s_bins)[16], int B, F bin) {
   int excl[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const int incl = wave_incl_scan_i(cnt[k], lane);
+    const int incl = wave_incl_scan_i(cnt[k]);
     excl[k] = incl - cnt[k];
     if (lane == 63) s_bins[w][k] = incl;
   }

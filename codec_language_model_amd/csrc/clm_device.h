@@ -83,12 +83,18 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
   }
   return x;
 }
-__device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+// Integer inclusive prefix sum over the 64 lanes with DPP moves only (no LDS
+// round trips): shifts by 1, 2, 4 and 8 inside each 16-lane row, then lane 15
+// of rows 0 and 2 is added into rows 1 and 3, and lane 31 into rows 2 and 3.
+// Lanes without a source add 0.  Integer addition is exact, so any scan
+// order gives the same result.
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
 }
 

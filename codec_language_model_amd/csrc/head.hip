@@ -60,7 +60,7 @@ __device__ __forceinline__ int gather_rows(const HeadP& P, int grp, int rc, int*
       const int r = r0 + k;
       if (r < P.M && clampi(P.head_id[r], 0, P.G - 1) == grp) ++cnt;
     }
-    const int incl = wave_incl_scan_i(cnt, lane);
+    const int incl = wave_incl_scan_i(cnt);
     if (lane == 63) s_cnt[w] = incl;
     __syncthreads();
     int rank = incl - cnt;
