@@ -332,11 +332,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
       for (int jj = 0; jj < DPL; ++jj) acc[r][jj] = 0.f;
     }
 
+    // A tile past the item's end (the pipeline's tail) reads slots 0..15 of
+    // block 0, KV head 0 instead: the same bytes for every wave, so they stay
+    // in L2 rather than costing HBM reads.  Such a tile is masked entirely.
     auto issue = [&](int ti, uint4 (&kr)[KPG][CPL], VT (&vr)[DPL]) {
+      const bool past = ti >= n_tiles;
       const int tk = t0 + (ti << 4);
-      const int blk = __builtin_amdgcn_readlane(my_blk, uniform(tk / bs - p0));
-      const int slot0 = tk % bs;
-      const size_t hb = (size_t)blk * P.H_kv + h;
+      const int blk = past ? 0 : __builtin_amdgcn_readlane(my_blk, uniform(min(tk / bs - p0, 63)));
+      const int slot0 = past ? 0 : tk % bs;
+      const size_t hb = past ? 0 : (size_t)blk * P.H_kv + h;
       const T* kp = kc + (hb * bs + slot0 + g * KPG) * D + c * VE;
       const T* vp = vc + hb * D * bs + slot0 + (size_t)c * bs + g * KPG;
 #pragma unroll
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
     };
 
     // tk: first token of the tile; a tile past the item (tk >= t1) is masked
-    // entirely (its loads were a duplicate of the last tile).  No branch:
+    // entirely (its loads read the shared block-0 tile).  No branch:
     // the key masks are applied on every tile (all-pass on full tiles), which
     // costs a few selects but keeps the accumulators in place.
     auto compute = [&](int tk, const uint4 (&kr)[KPG][CPL], const VT (&vr)[DPL]) {
@@ -454,17 +458,17 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
     uint4 ka[KPG][CPL], kb[KPG][CPL];
     VT va[DPL], vb[DPL];
     const int last = n_tiles - 1;
-    // Drain what is still in flight (the previous item's trailing duplicate
-    // tile, cache hits) so that the tile loop's waits count exactly.
+    // Drain what is still in flight (the previous item's trailing tile past
+    // its end, an L2 hit) so that the tile loop's waits count exactly.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     issue(0, ka, va);
     int nblk = 0;
     uint32_t nq[NR][4 * CPL];
     if (next_item < total_items) fetch(next_item, nblk, nq);
     for (int ti = 0; ti <= last; ti += 2) {
-      issue(min(ti + 1, last), kb, vb);
+      issue(ti + 1, kb, vb);
       compute(t0 + (ti << 4), ka, va);
-      issue(min(ti + 2, last), ka, va);
+      issue(ti + 2, ka, va);
       compute(t0 + ((ti + 1) << 4), kb, vb);
     }
 
@@ -656,11 +660,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // a tile past the item's end reads block 0, KV head 0 (kept in L2; the
+    // tile is masked entirely), as in attn_split_kernel
     auto issue = [&](int ti, KT (&kr)[NS], VTy (&vr)[NJ], float4& ks, float4& vs) {
+      const bool past = ti >= n_tiles;
       const int tk = t0 + (ti << 4);
-      const int blk = __builtin_amdgcn_readlane(my_blk, uniform(tk / bs - p0));
-      const int slot0 = tk % bs;
-      const size_t hb = (size_t)blk * P.H_kv + h;
+      const int blk = past ? 0 : __builtin_amdgcn_readlane(my_blk, uniform(min(tk / bs - p0, 63)));
+      const int slot0 = past ? 0 : tk % bs;
+      const size_t hb = past ? 0 : (size_t)blk * P.H_kv + h;
       const E* kp = kc + (hb * bs + slot0 + l16) * D + 8 * lg;
       const E* vp = vc + hb * D * bs + (size_t)l16 * bs + slot0 + 4 * lg;
       if constexpr (F8) {
@@ -686,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
     };
 
     // tk: first token of the tile; tiles past the item (tk >= t1) are
-    // duplicates of its last tile and are masked entirely
+    // masked entirely
     auto compute = [&](int tk, const KT (&kr)[NS], const VTy (&vr)[NJ], const float4& ks, const float4& vs) {
       f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -754,7 +761,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
     const int last = n_tiles - 1;
     auto issue_s = [&](int ti0, KT (&kr)[TPS][NS], VTy (&vr)[TPS][NJ], float4 (&ks)[TPS], float4 (&vs)[TPS]) {
 #pragma unroll
-      for (int u = 0; u < TPS; ++u) issue(min(ti0 + u, last), kr[u], vr[u], ks[u], vs[u]);
+      for (int u = 0; u < TPS; ++u) issue(ti0 + u, kr[u], vr[u], ks[u], vs[u]);
     };
     auto compute_s = [&](int ti0, const KT (&kr)[TPS][NS], const VTy (&vr)[TPS][NJ], const float4 (&ks)[TPS],
                          const float4 (&vs)[TPS]) {
