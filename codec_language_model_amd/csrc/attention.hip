@@ -544,12 +544,13 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
 // Per lane: 4 score, D/2 accumulator and D/8 query registers, whatever the
 // row count, where the vector kernel needs NR*D/16 accumulators per lane.
 // Four E4M3 bytes -> four bf16 values in two words (exact: every E4M3 value
-// is a bf16 value), through the hardware fp8 -> f32 conversion.
+// is a bf16 value), with gfx950's scaled fp8 -> bf16 pair conversion at
+// scale 1: one instruction per two values.
 __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  return make_uint2(pack_bf16x2(lo.x, lo.y), pack_bf16x2(hi.x, hi.y));
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 template <int D, int NR, int BS, bool F8>
@@ -734,6 +735,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
       }
       const uint32_t p01 = pack_bf16x2(pv[0], pv[1]), p23 = pack_bf16x2(pv[2], pv[3]);
       const bf16x4s pb = __builtin_bit_cast(bf16x4s, make_uint2(p01, p23));
+      // rescale the accumulators only when some row's maximum rose in this
+      // tile (corr is exactly 1 otherwise): after the first tiles of an item
+      // most tiles skip it
+      if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[j] = acc[j] * corr;
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         uint2 vw;
@@ -747,7 +755,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
           vw = make_uint2(vr[j].x & keep0, vr[j].y & keep1);
         }
         const bf16x4s va = __builtin_bit_cast(bf16x4s, vw);
-        acc[j] = acc[j] * corr;
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[j], 0, 0, 0);
       }
     };
