@@ -48,6 +48,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxB = 4096;
+constexpr int kRingMaxB = 512;       // streams the LDS-staged FP8 kernel takes
+constexpr int kRingStages = 4;       // its per-wave ring of tile stages
 
 template <int BYTES> struct VecT;
 template <> struct VecT<4> { using type = uint32_t; };
@@ -553,7 +555,7 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
   return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
-template <int D, int NR, int BS, bool F8>
+template <int D, int NR, int BS, bool F8, bool RING = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
   typedef short bf16x4s __attribute__((ext_vector_type(4)));
   // K/V element: bf16, or E4M3 bytes with one fp32 scale per (token, KV head)
@@ -563,12 +565,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
   constexpr int NS = D / 32;   // score MFMAs per tile
   constexpr int NJ = D / 16;   // value MFMAs per tile
   static_assert(NR <= 16, "one MFMA column block of query rows");
+  static_assert(!RING || F8, "the LDS ring stages FP8 tiles");
+  // LDS ring (FP8): per wave kRingStages stages of one tile each: keys
+  // [D/8 groups][16 slots][8 B], values [D dims][16 slots], then the 16 key
+  // scales and 16 value scales (and a copy of both)
+  constexpr int kStageB = 32 * D + 256;
+  constexpr int MB = RING ? kRingMaxB : kMaxB;
 
-  __shared__ int s_full[kMaxB + 1];
-  __shared__ int s_plist[kMaxB];
+  __shared__ int s_full[MB + 1];
+  __shared__ int s_plist[MB];
   __shared__ int s_bins[kWaves][16];
-  __shared__ int s_len[kMaxB];
+  __shared__ int s_len[MB];
   __shared__ int s_wsum[kWaves];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[RING ? kWaves * kRingStages * kStageB : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -759,32 +768,88 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
       }
     };
 
-    // TPS tiles per pipeline stage: an FP8 tile is half the bytes of a bf16
-    // one, so two are staged together to keep as many bytes in flight
-    constexpr int TPS = F8 ? 2 : 1;
-    KT ka[TPS][NS], kb[TPS][NS];
-    VTy va[TPS][NJ], vb[TPS][NJ];
-    float4 ksa[TPS], vsa[TPS], ksb[TPS], vsb[TPS];
-    const int last = n_tiles - 1;
-    auto issue_s = [&](int ti0, KT (&kr)[TPS][NS], VTy (&vr)[TPS][NJ], float4 (&ks)[TPS], float4 (&vs)[TPS]) {
-#pragma unroll
-      for (int u = 0; u < TPS; ++u) issue(ti0 + u, kr[u], vr[u], ks[u], vs[u]);
-    };
-    auto compute_s = [&](int ti0, const KT (&kr)[TPS][NS], const VTy (&vr)[TPS][NJ], const float4 (&ks)[TPS],
-                         const float4 (&vs)[TPS]) {
-#pragma unroll
-      for (int u = 0; u < TPS; ++u) compute(t0 + ((ti0 + u) << 4), kr[u], vr[u], ks[u], vs[u]);
-    };
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see attn_split_kernel
-    issue_s(0, ka, va, ksa, vsa);
     int nblk = 0;
     bf16x8_t nq[NS];
-    if (next_item < total_items) fetch(next_item, nblk, nq);
-    for (int ti = 0; ti <= last; ti += 2 * TPS) {
-      issue_s(ti + TPS, kb, vb, ksb, vsb);
-      compute_s(ti, ka, va, ksa, vsa);
-      issue_s(ti + 2 * TPS, ka, va, ksa, vsa);
-      compute_s(ti + TPS, kb, vb, ksb, vsb);
+    if constexpr (RING) {
+      // Tiles reach LDS by DMA into this wave's ring (no registers held while
+      // in flight, no barrier: only this wave touches its stages).  Tile ti
+      // lives in stage ti % kRingStages; kRingStages - 1 tiles are in flight
+      // while one is multiplied.
+      constexpr int kOps = D / 32 + 1;     // DMA instructions per tile
+      uint8_t* ring = s_ring + (tid >> 6) * (kRingStages * kStageB);
+      const uint32_t ring_lds = (uint32_t)reinterpret_cast<uintptr_t>(ring);
+      const uint8_t* __restrict__ kc8 = reinterpret_cast<const uint8_t*>(P.kc);
+      const uint8_t* __restrict__ vc8 = reinterpret_cast<const uint8_t*>(P.vc);
+      auto dma_tile = [&](int ti) {
+        const bool past = ti >= n_tiles;   // past the item: block 0, KV head 0 (L2)
+        const int tk = t0 + (ti << 4);
+        const int blk = past ? 0 : __builtin_amdgcn_readlane(my_blk, uniform(min(tk / bs - p0, 63)));
+        const int slot0 = past ? 0 : tk % bs;
+        const size_t hb = past ? 0 : (size_t)blk * P.H_kv + h;
+        const uint32_t base = ring_lds + (uint32_t)((ti & (kRingStages - 1)) * kStageB);
+        // keys: instruction i, lane l: group 8 i + l/8, bytes 16 (l%8) of its 128
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i)
+          dma16(kc8 + ((hb * (D / 8) + 8 * i + (lane >> 3)) * bs + slot0) * 8 + 16 * (lane & 7),
+                uniform(base + 1024 * i));
+        // values: instruction i, lane l: dimension 64 i + l, its 16 slots
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i)
+          dma16(vc8 + (hb * D + 64 * i + lane) * bs + slot0, uniform(base + 16 * D + 1024 * i));
+        // scales: lanes 0-15 key scales, 16-31 value scales (32-63 a copy)
+        dma4(((lane & 16) ? P.v_scale : P.k_scale) + hb * bs + slot0 + (lane & 15), uniform(base + 32 * D));
+      };
+      auto compute_tile = [&](int ti) {
+        const uint8_t* sb = ring + (ti & (kRingStages - 1)) * kStageB;
+        KT kr[NS];
+        VTy vr[NJ];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) kr[k] = *reinterpret_cast<const uint2*>(sb + (4 * k + lg) * 128 + 8 * l16);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          vr[j] = *reinterpret_cast<const uint32_t*>(sb + 16 * D + 16 * (16 * j + l16) + 4 * lg);
+        const float4 ks = *reinterpret_cast<const float4*>(sb + 32 * D + 16 * lg);
+        const float4 vs = *reinterpret_cast<const float4*>(sb + 32 * D + 64 + 16 * lg);
+        compute(t0 + (ti << 4), kr, vr, ks, vs);
+      };
+      // the previous item's trailing tiles (past its end, L2 hits) and the
+      // next item's block ids and query land before this item's tiles, so
+      // the waits below count this item's DMA exactly
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      if (next_item < total_items) fetch(next_item, nblk, nq);
+#pragma unroll
+      for (int c = 0; c < kRingStages - 1; ++c) dma_tile(c);
+      for (int ti = 0; ti < n_tiles; ++ti) {
+        dma_tile(ti + kRingStages - 1);            // into the stage of tile ti-1
+        wait_vmcnt<(kRingStages - 1) * kOps>();    // tile ti has landed
+        compute_tile(ti);
+      }
+    } else {
+      // TPS tiles per pipeline stage: an FP8 tile is half the bytes of a bf16
+      // one, so two are staged together to keep as many bytes in flight
+      constexpr int TPS = F8 ? 2 : 1;
+      KT ka[TPS][NS], kb[TPS][NS];
+      VTy va[TPS][NJ], vb[TPS][NJ];
+      float4 ksa[TPS], vsa[TPS], ksb[TPS], vsb[TPS];
+      const int last = n_tiles - 1;
+      auto issue_s = [&](int ti0, KT (&kr)[TPS][NS], VTy (&vr)[TPS][NJ], float4 (&ks)[TPS], float4 (&vs)[TPS]) {
+  #pragma unroll
+        for (int u = 0; u < TPS; ++u) issue(ti0 + u, kr[u], vr[u], ks[u], vs[u]);
+      };
+      auto compute_s = [&](int ti0, const KT (&kr)[TPS][NS], const VTy (&vr)[TPS][NJ], const float4 (&ks)[TPS],
+                           const float4 (&vs)[TPS]) {
+  #pragma unroll
+        for (int u = 0; u < TPS; ++u) compute(t0 + ((ti0 + u) << 4), kr[u], vr[u], ks[u], vs[u]);
+      };
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see attn_split_kernel
+      issue_s(0, ka, va, ksa, vsa);
+      if (next_item < total_items) fetch(next_item, nblk, nq);
+      for (int ti = 0; ti <= last; ti += 2 * TPS) {
+        issue_s(ti + TPS, kb, vb, ksb, vsb);
+        compute_s(ti, ka, va, ksa, vsa);
+        issue_s(ti + 2 * TPS, ka, va, ksa, vsa);
+        compute_s(ti + TPS, kb, vb, ksb, vsb);
+      }
     }
 
     // row sums: add the four lanes of each row
@@ -898,7 +963,12 @@ hipError_t launch_t(const KParams& P, int grid, hipStream_t s) {
   const bool exact = P.nr == NR;
   if (P.k_scale) {                       // FP8 cache: matrix-core kernel at every row count
     if constexpr (std::is_same<T, uint16_t>::value) {
-      if (P.bs == 16)
+      // up to kRingMaxB streams: tiles staged through an LDS ring
+      if (P.B <= kRingMaxB && P.bs == 16)
+        hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 16, true, true>), dim3(grid), dim3(kThreads), 0, s, P);
+      else if (P.B <= kRingMaxB)
+        hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 0, true, true>), dim3(grid), dim3(kThreads), 0, s, P);
+      else if (P.bs == 16)
         hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 16, true>), dim3(grid), dim3(kThreads), 0, s, P);
       else
         hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 0, true>), dim3(grid), dim3(kThreads), 0, s, P);

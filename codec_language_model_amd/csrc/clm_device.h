@@ -98,6 +98,27 @@ __device__ __forceinline__ int wave_incl_scan_i(int x) {
   return x;
 }
 
+// ---- global -> LDS DMA -----------------------------------------------------------
+// Loads from global memory straight into LDS (no registers): lane l's bytes
+// land at lds_byte_addr + 16 l (dma16) or + 4 l (dma4), lds_byte_addr being
+// wave-uniform (M0).  The compiler does not see these loads; waits for them
+// are explicit s_waitcnt vmcnt(n).  vmcnt retires in issue order, so the
+// compiler's own waits stay correct, only more conservative.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_byte_addr) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gptr), "s"(lds_byte_addr) : "memory");
+}
+// s_waitcnt with only vmcnt = n (0..63) constrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---- streaming loads ----------------------------------------------------------
 // Non-temporal global loads (the nt bit): for data read once per call (the
 // KV cache, head weights, logits).  On gfx950 they sustain a higher HBM read

@@ -83,22 +83,6 @@ __device__ __forceinline__ int gather_rows(const HeadP& P, int grp, int rc, int*
   return uniform(n_rows);
 }
 
-// 16 bytes per lane from global memory straight into LDS (no registers):
-// lane l's bytes land at lds_byte_addr + 16 l, lds_byte_addr being wave-uniform
-// (M0).  The compiler does not see these loads; waits for them are explicit
-// s_waitcnt vmcnt(n) (vmcnt retires in issue order, so the compiler's own
-// waits stay correct, only more conservative).
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_byte_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gptr), "s"(lds_byte_addr) : "memory");
-}
-// s_waitcnt with only vmcnt = n (0..63) constrained.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // LDS fed by DMA: S LDS stages of one 64-k chunk each, holding NV
 // codebook rows then MR h rows (128 bytes per row, the 16-byte pieces
 // XOR-swizzled by row so the operand reads are bank-conflict free).  Each

@@ -110,3 +110,40 @@ def test_fp8_append_then_attention(clm_gpu):
         vals.append(V)
     ref = oracle.decode_attention(synth.bf16_bits_to_f32(x.q), keys, vals, x.kv_len, scale, c.H_kv)
     check_close(bf16_tensor_to_f32(o), ref, "fp8 append + attention c4")
+
+
+
+def test_fp8_attention_many_streams(clm_gpu):
+    """More than 512 streams: the register-staged kernel (the LDS-staged one
+    takes up to 512).  520 streams of 1..64 keys over random E4M3 codes (no
+    NaN codes) and scales in [0.002, 0.01]; every 13th stream is checked
+    against the oracle on the dequantized rows."""
+    rng = np.random.default_rng(520)
+    B, Hq, Hk, D, bs = 520, 16, 8, 128, 16
+    kv_len = rng.integers(1, 65, size=B).astype(np.int32)
+    pages = (kv_len + bs - 1) // bs
+    nb = int(pages.sum()) + 2
+    perm = rng.permutation(nb).astype(np.int32)
+    max_blocks = int(pages.max())
+    bt = np.zeros((B, max_blocks), np.int32)
+    o_ = 0
+    for b in range(B):
+        bt[b, :pages[b]] = perm[o_:o_ + pages[b]]
+        o_ += pages[b]
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    kc = finite[rng.integers(0, finite.size, size=(nb, Hk, D // 8, bs, 8))]
+    vc = finite[rng.integers(0, finite.size, size=(nb, Hk, D, bs))]
+    ks = rng.uniform(0.002, 0.01, size=(nb, Hk, bs)).astype(np.float32)
+    vs = rng.uniform(0.002, 0.01, size=(nb, Hk, bs)).astype(np.float32)
+    q_bits = synth.f32_to_bf16_bits(rng.standard_normal((B, 1, Hq, D)).astype(np.float32))
+    scale = 1.0 / math.sqrt(D)
+    o = clm_gpu.decode_attention_fp8(to_torch(q_bits, bf16=True), dev(kc), dev(vc), dev(ks), dev(vs),
+                                     dev(bt), dev(kv_len), int(kv_len.max()), scale=scale)
+    idx = np.arange(0, B, 13)
+    keys, vals = [], []
+    for b in idx:
+        K, V = fp8.gather_dequantized(kc, vc, ks, vs, bt, int(b), int(kv_len[b]), bs)
+        keys.append(K)
+        vals.append(V)
+    ref = oracle.decode_attention(synth.bf16_bits_to_f32(q_bits)[idx], keys, vals, kv_len[idx], scale, Hk)
+    check_close(bf16_tensor_to_f32(o)[idx], ref, "fp8 attention, 520 streams (sampled)")
