@@ -63,16 +63,58 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// ---- whole-wave reductions (ds_bpermute based shuffles) ------------------------
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// ---- whole-wave reductions ------------------------------------------------------
+// The four in-row DPP steps give every lane its 16-lane row's result; the four
+// rows are then combined from lanes 0, 16, 32 and 48 (readlane), so every lane
+// returns the same value and no LDS round trip is made.  Sums add the rows in
+// order ((r0 + r1) + r2) + r3.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  x = group_sum<16>(x);
+  return ((lane_f(x, 0) + lane_f(x, 16)) + lane_f(x, 32)) + lane_f(x, 48);
 }
 __device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+  x = max(x, dpp_i<0xB1>(x));
+  x = max(x, dpp_i<0x4E>(x));
+  x = max(x, dpp_i<0x141>(x));
+  x = max(x, dpp_i<0x140>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+// (value, index) maximum over the wave, ties to the lower index (an order on
+// pairs, so the combination order does not matter).  Every lane returns it.
+__device__ __forceinline__ void argmax_step(float& bv, int& bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& bv, int& bi) {
+  argmax_step(bv, bi, dpp_f<CTRL>(bv), dpp_i<CTRL>(bi));
+}
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  argmax_dpp<0xB1>(bv, bi);
+  argmax_dpp<0x4E>(bv, bi);
+  argmax_dpp<0x141>(bv, bi);
+  argmax_dpp<0x140>(bv, bi);
+  float v = lane_f(bv, 0);
+  int i = __builtin_amdgcn_readlane(bi, 0);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
+  for (int r = 16; r < 64; r += 16) argmax_step(v, i, lane_f(bv, r), __builtin_amdgcn_readlane(bi, r));
+  bv = v;
+  bi = i;
 }
 // Inclusive prefix sum over the 64 lanes (Hillis-Steele, fixed order).
 __device__ __forceinline__ float wave_incl_scan(float x, int lane) {

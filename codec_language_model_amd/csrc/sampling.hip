@@ -56,8 +56,7 @@ __device__ __forceinline__ float block_max(float x, Scratch& sc) {
 
 __device__ __forceinline__ int block_max_int(int x, Scratch& sc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
+  x = wave_max_i(x);
   __syncthreads();
   if (lane == 0) sc.wi[w] = x;
   __syncthreads();
@@ -69,12 +68,7 @@ __device__ __forceinline__ int block_max_int(int x, Scratch& sc) {
 // (value, index) maximum with ties to the lower index.
 __device__ __forceinline__ int block_argmax_pair(float bv, int bi, Scratch& sc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off, 64);
-    const int oi = __shfl_xor(bi, off, 64);
-    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-  }
+  wave_argmax(bv, bi);
   __syncthreads();
   if (lane == 0) { sc.wf[w] = bv; sc.wi[w] = bi; }
   __syncthreads();
@@ -283,12 +277,7 @@ __device__ RowStat wave_row_stat(const float* __restrict__ x, int n, float T) {
   }
   for (int i = 4 * n4 + lane; i < n; i += 64)
     if (x[i] > bv) { bv = x[i]; bi = i; }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off, 64);
-    const int oi = __shfl_xor(bi, off, 64);
-    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-  }
+  wave_argmax(bv, bi);
   RowStat r{bv, 0.f, bi == 0x7fffffff ? 0 : bi};
   if (T > 0.f) {
     const float m = bv / T;
