@@ -3,8 +3,10 @@
 // sample_or_argmax (TontaubeV1: later stages decode at temperature zero;
 // Section 3.3: logits outside the stage's vocabulary are masked at sampling):
 // one 1024-thread workgroup per row.  Greedy rows take a block argmax (lowest
-// index on ties).  Sampled rows compute z = logit / T, e = exp(z - max z) and
-// draw by inverse CDF at the supplied uniform.
+// index on ties).  Sampled rows compute the softmax weights of z = logit / T,
+// e = exp(z - max z), as 2^((logit - max logit) * log2(e) / T) (fp32, within a
+// few ulps of the quotient form), and draw by inverse CDF at the supplied
+// uniform.
 //
 // spec_verify (Optimizing Streaming Text-to-Speech Models ..., "Speculative
 // Decoding for Acoustic Tokens"): one workgroup per stream.  The K target
@@ -34,6 +36,14 @@ constexpr int kCH = 16;                 // consecutive entries per thread per pa
 constexpr int kPass = kT * kCH;         // entries per pass
 constexpr int kMaxPasses = 64;          // V <= 1 << 20
 constexpr int kMaxDraft = 16;
+
+// exp(x / T - mx / T) as 2^((x - mx) * c), c = log2(e) / T: one subtraction,
+// one multiply and the hardware exp2 (x <= mx, so the argument is <= 0).  c
+// is kept finite so that x = mx gives 2^0 = 1 at any temperature.
+__device__ __forceinline__ float softmax_c(float T) { return fminf(kLog2e / T, 3.0e38f); }
+__device__ __forceinline__ float softmax_w(float x, float mx, float c) {
+  return __builtin_amdgcn_exp2f((x - mx) * c);
+}
 
 struct Scratch {
   float wf[kW];
@@ -226,18 +236,18 @@ __global__ __launch_bounds__(kT) void sample_kernel(SampleArgs P) {
       for (int k = 0; k < kCH; ++k) mx = fmaxf(mx, v[k]);
     }
     mx = block_max(mx, sc);
-    const float m = mx / T;
+    const float c = softmax_c(T);
     const float u = P.uniforms[r];
     auto wf = [&](int i0, float (&w)[kCH]) {
       float y[kCH];
       load16(x, i0, n, y, 0.f);
 #pragma unroll
-      for (int k = 0; k < kCH; ++k) w[k] = i0 + k < n ? expf(y[k] / T - m) : 0.f;
+      for (int k = 0; k < kCH; ++k) w[k] = i0 + k < n ? softmax_w(y[k], mx, c) : 0.f;
     };
     if (one) {
       const int i0 = threadIdx.x * kCH;
 #pragma unroll
-      for (int k = 0; k < kCH; ++k) e[k] = i0 + k < n ? expf(v[k] / T - m) : 0.f;
+      for (int k = 0; k < kCH; ++k) e[k] = i0 + k < n ? softmax_w(v[k], mx, c) : 0.f;
     }
     tok = block_draw(n, u, wf, e, one, sc);
     if (tok < 0) tok = 0;
@@ -280,7 +290,7 @@ __device__ RowStat wave_row_stat(const float* __restrict__ x, int n, float T) {
   wave_argmax(bv, bi);
   RowStat r{bv, 0.f, bi == 0x7fffffff ? 0 : bi};
   if (T > 0.f) {
-    const float m = bv / T;
+    const float c = softmax_c(T);
     float sum = 0.f;
     for (int j0 = 0; j0 < n4; j0 += 64 * U) {
       float4 v[U];
@@ -291,9 +301,10 @@ __device__ RowStat wave_row_stat(const float* __restrict__ x, int n, float T) {
       }
 #pragma unroll
       for (int k = 0; k < U; ++k)
-        sum += expf(v[k].x / T - m) + expf(v[k].y / T - m) + expf(v[k].z / T - m) + expf(v[k].w / T - m);
+        sum += softmax_w(v[k].x, bv, c) + softmax_w(v[k].y, bv, c) + softmax_w(v[k].z, bv, c) +
+               softmax_w(v[k].w, bv, c);
     }
-    for (int i = 4 * n4 + lane; i < n; i += 64) sum += expf(x[i] / T - m);
+    for (int i = 4 * n4 + lane; i < n; i += 64) sum += softmax_w(x[i], bv, c);
     r.sum = wave_sum(sum);
   }
   return r;
@@ -342,8 +353,7 @@ __global__ __launch_bounds__(kT) void verify_kernel(VerifyArgs P) {
       const float qx = s_qx[i];
       bool accept;
       if (T > 0.f) {
-        const float m = s_m[i] / T;
-        const float px = expf(s_xx[i] / T - m) / s_sum[i];
+        const float px = softmax_w(s_xx[i], s_m[i], softmax_c(T)) / s_sum[i];
         accept = qx > 0.f && s_ua[i] < px / qx;
       } else {
         accept = qx > 0.f && xt == s_amax[i];
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(kT) void verify_kernel(VerifyArgs P) {
     if (T > 0.f) {
       const float* __restrict__ x = P.target_logits + trow * V;
       const float* __restrict__ q = P.draft_probs + row * V;
-      const float m = s_m[rej] / T, S = s_sum[rej];
+      const float mx = s_m[rej], c = softmax_c(T), inv_s = 1.f / s_sum[rej];
       const float ur = P.u_resample[b];
       float e[kCH];
       auto resid = [&](int i0, float (&wgt)[kCH]) {
@@ -372,7 +382,7 @@ __global__ __launch_bounds__(kT) void verify_kernel(VerifyArgs P) {
         load16(x, i0, V, y, 0.f);
         load16(q, i0, V, z, 0.f);
 #pragma unroll
-        for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? fmaxf(expf(y[k] / T - m) / S - z[k], 0.f) : 0.f;
+        for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? fmaxf(softmax_w(y[k], mx, c) * inv_s - z[k], 0.f) : 0.f;
       };
       tok = block_draw(V, ur, resid, e, false, sc);
       if (tok < 0) {
@@ -380,7 +390,7 @@ __global__ __launch_bounds__(kT) void verify_kernel(VerifyArgs P) {
           float y[kCH];
           load16(x, i0, V, y, 0.f);
 #pragma unroll
-          for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? expf(y[k] / T - m) / S : 0.f;
+          for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? softmax_w(y[k], mx, c) * inv_s : 0.f;
         };
         tok = block_draw(V, ur, target, e, false, sc);
       }
@@ -397,13 +407,13 @@ __global__ __launch_bounds__(kT) void verify_kernel(VerifyArgs P) {
     int tok;
     if (T > 0.f) {
       const float* __restrict__ x = P.target_logits + trow * V;
-      const float m = s_m[K] / T, S = s_sum[K];
+      const float mx = s_m[K], c = softmax_c(T), inv_s = 1.f / s_sum[K];
       float e[kCH];
       auto target = [&](int i0, float (&wgt)[kCH]) {
         float y[kCH];
         load16(x, i0, V, y, 0.f);
 #pragma unroll
-        for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? expf(y[k] / T - m) / S : 0.f;
+        for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? softmax_w(y[k], mx, c) * inv_s : 0.f;
       };
       tok = block_draw(V, P.u_resample[b], target, e, false, sc);
       if (tok < 0) tok = 0;
