@@ -565,11 +565,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
   constexpr int NS = D / 32;   // score MFMAs per tile
   constexpr int NJ = D / 16;   // value MFMAs per tile
   static_assert(NR <= 16, "one MFMA column block of query rows");
-  static_assert(!RING || F8, "the LDS ring stages FP8 tiles");
-  // LDS ring (FP8): per wave kRingStages stages of one tile each: keys
+  // LDS ring: per wave kRingStages stages of one tile each.  FP8: keys
   // [D/8 groups][16 slots][8 B], values [D dims][16 slots], then the 16 key
-  // scales and 16 value scales (and a copy of both)
-  constexpr int kStageB = 32 * D + 256;
+  // scales and 16 value scales (and a copy of both).  bf16: keys [16 slots][D]
+  // with the 16-byte chunks of slot r XOR-swizzled by r (bank-conflict-free
+  // operand reads), values [D dims][16 slots].
+  constexpr int kStageB = F8 ? 32 * D + 256 : 64 * D;
   constexpr int MB = RING ? kRingMaxB : kMaxB;
 
   __shared__ int s_full[MB + 1];
@@ -775,7 +776,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
       // in flight, no barrier: only this wave touches its stages).  Tile ti
       // lives in stage ti % kRingStages; kRingStages - 1 tiles are in flight
       // while one is multiplied.
-      constexpr int kOps = D / 32 + 1;     // DMA instructions per tile
+      constexpr int kOps = F8 ? D / 32 + 1 : D / 16;   // DMA instructions per tile
+      constexpr int kCh = D / 8;                        // bf16: 16-byte chunks per key row
       uint8_t* ring = s_ring + (tid >> 6) * (kRingStages * kStageB);
       const uint32_t ring_lds = (uint32_t)reinterpret_cast<uintptr_t>(ring);
       const uint8_t* __restrict__ kc8 = reinterpret_cast<const uint8_t*>(P.kc);
@@ -787,29 +789,57 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
         const int slot0 = past ? 0 : tk % bs;
         const size_t hb = past ? 0 : (size_t)blk * P.H_kv + h;
         const uint32_t base = ring_lds + (uint32_t)((ti & (kRingStages - 1)) * kStageB);
-        // keys: instruction i, lane l: group 8 i + l/8, bytes 16 (l%8) of its 128
+        if constexpr (F8) {
+          // keys: instruction i, lane l: group 8 i + l/8, bytes 16 (l%8) of its 128
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i)
-          dma16(kc8 + ((hb * (D / 8) + 8 * i + (lane >> 3)) * bs + slot0) * 8 + 16 * (lane & 7),
-                uniform(base + 1024 * i));
-        // values: instruction i, lane l: dimension 64 i + l, its 16 slots
+          for (int i = 0; i < D / 64; ++i)
+            dma16(kc8 + ((hb * (D / 8) + 8 * i + (lane >> 3)) * bs + slot0) * 8 + 16 * (lane & 7),
+                  uniform(base + 1024 * i));
+          // values: instruction i, lane l: dimension 64 i + l, its 16 slots
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i)
-          dma16(vc8 + (hb * D + 64 * i + lane) * bs + slot0, uniform(base + 16 * D + 1024 * i));
-        // scales: lanes 0-15 key scales, 16-31 value scales (32-63 a copy)
-        dma4(((lane & 16) ? P.v_scale : P.k_scale) + hb * bs + slot0 + (lane & 15), uniform(base + 32 * D));
+          for (int i = 0; i < D / 64; ++i)
+            dma16(vc8 + (hb * D + 64 * i + lane) * bs + slot0, uniform(base + 16 * D + 1024 * i));
+          // scales: lanes 0-15 key scales, 16-31 value scales (32-63 a copy)
+          dma4(((lane & 16) ? P.v_scale : P.k_scale) + hb * bs + slot0 + (lane & 15), uniform(base + 32 * D));
+        } else {
+          // keys: LDS chunk p = 64 i + l is chunk (p % kCh) of slot r = p / kCh
+          // and holds the row's chunk (p % kCh) ^ (r % kCh)
+#pragma unroll
+          for (int i = 0; i < D / 32; ++i) {
+            const int pc = 64 * i + lane, r = pc / kCh, cc = (pc % kCh) ^ (r % kCh);
+            dma16(kc8 + ((hb * bs + slot0 + r) * D + 8 * cc) * 2, uniform(base + 1024 * i));
+          }
+          // values: LDS chunk p = 64 i + l is half (p % 2) of dimension p / 2
+#pragma unroll
+          for (int i = 0; i < D / 32; ++i) {
+            const int pc = 64 * i + lane;
+            dma16(vc8 + ((hb * D + (pc >> 1)) * bs + slot0 + 8 * (pc & 1)) * 2, uniform(base + 32 * D + 1024 * i));
+          }
+        }
       };
       auto compute_tile = [&](int ti) {
         const uint8_t* sb = ring + (ti & (kRingStages - 1)) * kStageB;
         KT kr[NS];
         VTy vr[NJ];
+        float4 ks = make_float4(1.f, 1.f, 1.f, 1.f), vs = ks;
+        if constexpr (F8) {
 #pragma unroll
-        for (int k = 0; k < NS; ++k) kr[k] = *reinterpret_cast<const uint2*>(sb + (4 * k + lg) * 128 + 8 * l16);
+          for (int k = 0; k < NS; ++k) kr[k] = *reinterpret_cast<const uint2*>(sb + (4 * k + lg) * 128 + 8 * l16);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          vr[j] = *reinterpret_cast<const uint32_t*>(sb + 16 * D + 16 * (16 * j + l16) + 4 * lg);
-        const float4 ks = *reinterpret_cast<const float4*>(sb + 32 * D + 16 * lg);
-        const float4 vs = *reinterpret_cast<const float4*>(sb + 32 * D + 64 + 16 * lg);
+          for (int j = 0; j < NJ; ++j)
+            vr[j] = *reinterpret_cast<const uint32_t*>(sb + 16 * D + 16 * (16 * j + l16) + 4 * lg);
+          ks = *reinterpret_cast<const float4*>(sb + 32 * D + 16 * lg);
+          vs = *reinterpret_cast<const float4*>(sb + 32 * D + 64 + 16 * lg);
+        } else {
+          // lane (slot l%16, dims 32 k + 8 (l/16) ..): chunk 4 k + l/16 of its slot
+#pragma unroll
+          for (int k = 0; k < NS; ++k)
+            kr[k] = *reinterpret_cast<const KT*>(sb + 2 * D * l16 + 16 * ((4 * k + lg) ^ (l16 % kCh)));
+          // lane (dimension 16 j + l%16, slots 4 (l/16) ..): 8 bytes
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            vr[j] = *reinterpret_cast<const VTy*>(sb + 32 * D + 32 * (16 * j + l16) + 8 * lg);
+        }
         compute(t0 + (ti << 4), kr, vr, ks, vs);
       };
       // the previous item's trailing tiles (past its end, L2 hits) and the
@@ -976,7 +1006,11 @@ hipError_t launch_t(const KParams& P, int grid, hipStream_t s) {
       return hipErrorInvalidValue;
     }
   } else if constexpr (std::is_same<T, uint16_t>::value && NR > 2) {
-    if (P.bs == 16)
+    if (P.B <= kRingMaxB && P.bs == 16)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 16, false, true>), dim3(grid), dim3(kThreads), 0, s, P);
+    else if (P.B <= kRingMaxB)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 0, false, true>), dim3(grid), dim3(kThreads), 0, s, P);
+    else if (P.bs == 16)
       hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 16, false>), dim3(grid), dim3(kThreads), 0, s, P);
     else
       hipLaunchKernelGGL((attn_mfma_kernel<D, NR, 0, false>), dim3(grid), dim3(kThreads), 0, s, P);
