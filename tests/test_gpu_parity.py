@@ -143,6 +143,40 @@ def test_decode_attention_parity(clm_gpu, cfg):
     assert np.array_equal(as_bits(o), as_bits(o2))
 
 
+
+def test_decode_attention_multi_query_many_streams(clm_gpu):
+    """Blocks of 6 queries over more than 512 streams: the register-staged
+    matrix-core kernel (the LDS-staged one takes up to 512).  520 streams of
+    6..70 keys, bf16 N(0, 1) keys and values in a shuffled page pool; every
+    13th stream is checked against the oracle."""
+    rng = np.random.default_rng(5206)
+    B, Kq, Hq, Hk, D, bs = 520, 6, 16, 8, 128, 16
+    kv_len = rng.integers(Kq, 71, size=B).astype(np.int32)
+    pages = (kv_len + bs - 1) // bs
+    nb = int(pages.sum()) + 2
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.zeros((B, int(pages.max())), np.int32)
+    o_ = 0
+    for b in range(B):
+        bt[b, :pages[b]] = perm[o_:o_ + pages[b]]
+        o_ += pages[b]
+    kc = synth.f32_to_bf16_bits(rng.standard_normal((nb, Hk, bs, D)).astype(np.float32))
+    vc = synth.f32_to_bf16_bits(rng.standard_normal((nb, Hk, D, bs)).astype(np.float32))
+    q = synth.f32_to_bf16_bits(rng.standard_normal((B, Kq, Hq, D)).astype(np.float32))
+    scale = 1.0 / math.sqrt(D)
+    o = clm_gpu.decode_attention(to_torch(q, bf16=True), to_torch(kc, bf16=True), to_torch(vc, bf16=True),
+                                 to_torch(bt), to_torch(kv_len), int(kv_len.max()), scale=scale)
+    idx = np.arange(0, B, 13)
+    kf, vf = synth.bf16_bits_to_f32(kc), synth.bf16_bits_to_f32(vc)
+    keys, vals = {}, {}
+    for b in idx:
+        pos = np.arange(int(kv_len[b]))
+        blk, slot = bt[b, pos // bs], pos % bs
+        keys[b] = kf[blk, :, slot, :]          # [n, H_kv, D]
+        vals[b] = vf[blk, :, :, slot]          # [n, H_kv, D]
+    ref = oracle.decode_attention(synth.bf16_bits_to_f32(q), keys, vals, kv_len, scale, Hk, streams=idx)
+    check_close(bf16_tensor_to_f32(o)[idx], ref[idx], "6-query attention, 520 streams (sampled)")
+
 @pytest.mark.parametrize("cfg", [2, 5])
 def test_decode_attention_split_plan_and_batch_order(clm_gpu, cfg):
     """A looser max_kv_len bound changes the split plan (longer splits, more
