@@ -16,9 +16,9 @@
 // every stream, then each stream's shorter last split, longest first - and
 // its waves take items in a snake order over the grid's waves.  (A shared
 // ticket counter balanced the tail better but cost more: device-wide atomics
-// on one address serialise across the chip.)  While a wave streams one item it already loads the next
-// item's block ids and query slice.  No barrier, LDS access or cross-wave
-// traffic in the main loop.
+// on one address serialise across the chip.)  While a wave streams one item
+// it already loads the next item's block ids and query slice.  No barrier or
+// cross-wave traffic in the main loop.
 //
 // Inside an item a wave walks 16-token tiles.  The block ids of the item's
 // pages are fetched once, one per lane, and picked out with readlane.  Keys
@@ -29,14 +29,21 @@
 // gfx950 that policy streams scattered 4 KiB pages faster than the default.
 // Values are stored transposed inside a block ([D][bs]), so for each of its
 // head dimensions a lane reads the run of keys its group scored, contiguous
-// across the wave.  The loop body covers two tiles without a branch: while one tile
-// buffer is computed the other's loads are in flight (past the last tile the
-// loads re-read it, which hits in cache, and the tile is masked), so the wait
-// counts stay exact.  Each 16-lane key group keeps its own online-softmax
-// state (running max m, sum l, accumulator) in registers; the groups merge
-// with shuffles at the end of an item.  A stream that fits in one split is
-// written directly; otherwise the split's (m, l, acc) goes to the workspace
-// and a second kernel merges the splits of each row in split order.
+// across the wave.  The loop body covers two tiles without a branch: while
+// one tile buffer is computed the other's loads are in flight (past the last
+// tile the loads read one shared tile that stays in L2, and the tile is
+// masked), so the wait counts stay exact.  Each 16-lane key group keeps its
+// own online-softmax state (running max m, sum l, accumulator) in registers;
+// the groups merge with shuffles at the end of an item.  A stream that fits
+// in one split is written directly; otherwise the split's (m, l, acc) goes to
+// the workspace and a second kernel merges the splits of each row in split
+// order.
+//
+// Blocks of 3..16 query rows per KV head, and every FP8 cache, use the
+// matrix-core kernel (attn_mfma_kernel): S = K.q^T and O^T += V^T.P^T per tile
+// on the MFMA units.  Up to kRingMaxB streams, its tiles reach LDS by
+// global-to-LDS DMA into a per-wave ring of kRingStages stages, so three tiles
+// are in flight per wave without holding registers.
 #include <type_traits>
 
 #include "clm_device.h"
@@ -48,7 +55,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxB = 4096;
-constexpr int kRingMaxB = 512;       // streams the LDS-staged FP8 kernel takes
+constexpr int kRingMaxB = 512;       // streams the LDS-staged matrix-core kernel takes
 constexpr int kRingStages = 4;       // its per-wave ring of tile stages
 
 template <int BYTES> struct VecT;

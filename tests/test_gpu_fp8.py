@@ -147,3 +147,32 @@ def test_fp8_attention_many_streams(clm_gpu):
         vals.append(V)
     ref = oracle.decode_attention(synth.bf16_bits_to_f32(q_bits)[idx], keys, vals, kv_len[idx], scale, Hk)
     check_close(bf16_tensor_to_f32(o)[idx], ref, "fp8 attention, 520 streams (sampled)")
+
+
+
+@pytest.mark.parametrize("cfg,bs", [(2, 32), (4, 64)])
+def test_fp8_block_sizes(clm_gpu, cfg, bs):
+    """The FP8 append and attention with pages of 32 and 64 slots (the
+    block-size-generic kernels, LDS-staged attention)."""
+    import dataclasses
+    c = dataclasses.replace(synth.get_config(cfg), block_size=bs)
+    x = synth.make_inputs(c)
+    kc, vc, ks, vs = fp8_pool(x, include_new=False)
+    dk, dv, dks, dvs = dev(kc), dev(vc), dev(ks), dev(vs)
+    bt, kl = dev(x.block_table), dev(x.kv_len)
+    clm_gpu.kv_cache_append_fp8(to_torch(x.k_new, bf16=True), to_torch(x.v_new, bf16=True), dk, dv, dks, dvs,
+                                bt, dev(x.len_before), block_size=bs)
+    rk, rv, rks, rvs = fp8.fp8_kv_cache_append(kc, vc, ks, vs, x.block_table, x.len_before,
+                                               synth.bf16_bits_to_f32(x.k_new), synth.bf16_bits_to_f32(x.v_new), bs)
+    np.testing.assert_array_equal(dk.cpu().numpy(), rk)
+    np.testing.assert_array_equal(dv.cpu().numpy(), rv)
+    scale = 1.0 / math.sqrt(c.D)
+    o = clm_gpu.decode_attention_fp8(to_torch(x.q, bf16=True), dk, dv, dks, dvs, bt, kl, int(x.kv_len.max()),
+                                     scale=scale)
+    keys, vals = [], []
+    for b in range(c.B):
+        K, V = fp8.gather_dequantized(rk, rv, rks, rvs, x.block_table, b, int(x.kv_len[b]), bs)
+        keys.append(K)
+        vals.append(V)
+    ref = oracle.decode_attention(synth.bf16_bits_to_f32(x.q), keys, vals, x.kv_len, scale, c.H_kv)
+    check_close(bf16_tensor_to_f32(o), ref, f"fp8 attention c{cfg} block size {bs}")

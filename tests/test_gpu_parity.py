@@ -177,6 +177,30 @@ def test_decode_attention_multi_query_many_streams(clm_gpu):
     ref = oracle.decode_attention(synth.bf16_bits_to_f32(q), keys, vals, kv_len, scale, Hk, streams=idx)
     check_close(bf16_tensor_to_f32(o)[idx], ref[idx], "6-query attention, 520 streams (sampled)")
 
+
+@pytest.mark.parametrize("cfg,bs,B", [(2, 32, None), (3, 64, 16), (4, 32, None), (4, 128, 12)])
+def test_block_sizes(clm_gpu, cfg, bs, B):
+    """Pages of 32 to 128 slots (the block-size-generic kernels): the append
+    bit-exact, then attention over the cache it wrote, against the oracle.
+    Single-query rows take the vector kernel; the 6-query blocks the
+    matrix-core kernel with its LDS ring."""
+    import dataclasses
+    c = dataclasses.replace(synth.get_config(cfg), block_size=bs)
+    x = synth.make_inputs(c, B=B)
+    d = Dev(x, include_new=False)
+    clm_gpu.kv_cache_append(d.k_new, d.v_new, d.k_cache, d.v_cache, d.block_table, d.len_before, block_size=bs)
+    rk, rv = oracle.kv_cache_append(d.k_pool_host, d.v_pool_host, x.block_table, x.len_before,
+                                    x.k_new, x.v_new, bs)
+    dt = np.int16 if d.bf else np.uint32
+    np.testing.assert_array_equal(as_bits(d.k_cache), rk.view(dt))
+    np.testing.assert_array_equal(as_bits(d.v_cache), rv.view(dt))
+    scale = 1.0 / math.sqrt(x.cfg.D)
+    o = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len, scale=scale,
+                                 block_size=bs)
+    keys, vals = logical(x)
+    ref = oracle.decode_attention(x.f32(x.q), keys, vals, x.kv_len, scale, x.cfg.H_kv)
+    check_close(bf16_tensor_to_f32(o), ref, f"attention c{cfg} block size {bs}")
+
 @pytest.mark.parametrize("cfg", [2, 5])
 def test_decode_attention_split_plan_and_batch_order(clm_gpu, cfg):
     """A looser max_kv_len bound changes the split plan (longer splits, more
