@@ -32,8 +32,20 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendP P) {
   T* kc = static_cast<T*>(P.k_cache);
   T* vc = static_cast<T*>(P.v_cache);
 
-  for (int e = threadIdx.x; e < P.T_new * CH; e += blockDim.x) {
-    const int t = e / CH, ch = e - (e / CH) * CH;
+  // One pass over the key chunks (16 bytes) and then the value elements of
+  // the new rows.  The source load does not depend on the destination, so
+  // it is issued before the page lookup (len_before, then the block table).
+  const int nk = P.T_new * CH;
+  const int n_all = nk + P.T_new * D;
+  for (int e = threadIdx.x; e < n_all; e += blockDim.x) {
+    const bool is_k = e < nk;
+    const int t = is_k ? e / CH : (e - nk) / D;
+    const int part = is_k ? e - t * CH : (e - nk) - t * D;   // key chunk or value dimension
+    const size_t row = ((size_t)(b * P.T_new + t) * P.H_kv + h) * D;
+    uint4 k4 = make_uint4(0u, 0u, 0u, 0u);
+    T v1 = T();
+    if (is_k) k4 = *reinterpret_cast<const uint4*>(kn + row + part * VE);
+    else v1 = vn[row + part];
     const int pos = lb + t;
     if (pos < 0) continue;
     const int page = pos / P.bs;
@@ -41,21 +53,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendP P) {
     const int blk = bt_row[page];
     if (blk < 0 || blk >= P.num_blocks) continue;
     const int slot = pos - page * P.bs;
-    const T* src = kn + ((size_t)(b * P.T_new + t) * P.H_kv + h) * D + ch * VE;
-    T* dst = kc + (((size_t)blk * P.H_kv + h) * P.bs + slot) * D + ch * VE;
-    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-  }
-  for (int e = threadIdx.x; e < P.T_new * D; e += blockDim.x) {
-    const int t = e / D, d = e - (e / D) * D;
-    const int pos = lb + t;
-    if (pos < 0) continue;
-    const int page = pos / P.bs;
-    if (page >= P.max_blocks) continue;
-    const int blk = bt_row[page];
-    if (blk < 0 || blk >= P.num_blocks) continue;
-    const int slot = pos - page * P.bs;
-    vc[(((size_t)blk * P.H_kv + h) * D + d) * P.bs + slot] =
-        vn[((size_t)(b * P.T_new + t) * P.H_kv + h) * D + d];
+    if (is_k)
+      *reinterpret_cast<uint4*>(kc + (((size_t)blk * P.H_kv + h) * P.bs + slot) * D + part * VE) = k4;
+    else
+      vc[(((size_t)blk * P.H_kv + h) * D + part) * P.bs + slot] = v1;
   }
 }
 
