@@ -222,9 +222,9 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only: the decode step shards by stream with no exchange, "
-              f"and multi-GPU runs are not part of this build (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world})", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the decode step shards by stream with no exchange "
+              f"between GPUs, so a multi-GPU figure is N independent copies of this one "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
