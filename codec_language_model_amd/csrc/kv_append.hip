@@ -191,6 +191,14 @@ __global__ __launch_bounds__(128) void fp8_append_kernel(Fp8AppendP F) {
   uint8_t* kc = static_cast<uint8_t*>(P.k_cache);
   uint8_t* vc = static_cast<uint8_t*>(P.v_cache);
   for (int t = 0; t < P.T_new; ++t) {
+    // the row and its quantization do not depend on where it goes: load and
+    // encode it while len_before and then the block table are looked up
+    const uint16_t* row = src + ((size_t)(b * P.T_new + t) * P.H_kv + h) * D;
+    float x[D / 64];
+    uint32_t code[D / 64];
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) x[i] = bf16_to_f32(row[lane + 64 * i]);
+    const float scale = quantize_row<D>(x, code);
     const int pos = lb + t;
     if (pos < 0) continue;
     const int page = pos / P.bs;
@@ -198,12 +206,6 @@ __global__ __launch_bounds__(128) void fp8_append_kernel(Fp8AppendP F) {
     const int blk = bt_row[page];
     if (blk < 0 || blk >= P.num_blocks) continue;
     const int slot = pos - page * P.bs;
-    const uint16_t* row = src + ((size_t)(b * P.T_new + t) * P.H_kv + h) * D;
-    float x[D / 64];
-    uint32_t code[D / 64];
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) x[i] = bf16_to_f32(row[lane + 64 * i]);
-    const float scale = quantize_row<D>(x, code);
     const size_t hb = (size_t)blk * P.H_kv + h;
     if (w == 0) {
       // keys in 8-dimension groups: [block][head][d / 8][slot][d % 8]
