@@ -150,12 +150,13 @@ def test_fp8_attention_many_streams(clm_gpu):
 
 
 
-@pytest.mark.parametrize("cfg,bs", [(2, 32), (4, 64)])
-def test_fp8_block_sizes(clm_gpu, cfg, bs):
-    """The FP8 append and attention with pages of 32 and 64 slots (the
-    block-size-generic kernels, LDS-staged attention)."""
+@pytest.mark.parametrize("cfg,bs,D", [(2, 32, 128), (4, 64, 128), (2, 16, 64), (4, 32, 64)])
+def test_fp8_block_sizes(clm_gpu, cfg, bs, D):
+    """The FP8 append and attention with pages of 16 to 64 slots and head
+    widths 128 and 64 (the block-size-generic kernels and the D = 64
+    instantiations, LDS-staged attention)."""
     import dataclasses
-    c = dataclasses.replace(synth.get_config(cfg), block_size=bs)
+    c = dataclasses.replace(synth.get_config(cfg), block_size=bs, D=D)
     x = synth.make_inputs(c)
     kc, vc, ks, vs = fp8_pool(x, include_new=False)
     dk, dv, dks, dvs = dev(kc), dev(vc), dev(ks), dev(vs)
@@ -175,4 +176,4 @@ def test_fp8_block_sizes(clm_gpu, cfg, bs):
         keys.append(K)
         vals.append(V)
     ref = oracle.decode_attention(synth.bf16_bits_to_f32(x.q), keys, vals, x.kv_len, scale, c.H_kv)
-    check_close(bf16_tensor_to_f32(o), ref, f"fp8 attention c{cfg} block size {bs}")
+    check_close(bf16_tensor_to_f32(o), ref, f"fp8 attention c{cfg} block size {bs} D {D}")

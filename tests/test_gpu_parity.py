@@ -178,14 +178,16 @@ def test_decode_attention_multi_query_many_streams(clm_gpu):
     check_close(bf16_tensor_to_f32(o)[idx], ref[idx], "6-query attention, 520 streams (sampled)")
 
 
-@pytest.mark.parametrize("cfg,bs,B", [(2, 32, None), (3, 64, 16), (4, 32, None), (4, 128, 12)])
-def test_block_sizes(clm_gpu, cfg, bs, B):
-    """Pages of 32 to 128 slots (the block-size-generic kernels): the append
-    bit-exact, then attention over the cache it wrote, against the oracle.
-    Single-query rows take the vector kernel; the 6-query blocks the
-    matrix-core kernel with its LDS ring."""
+@pytest.mark.parametrize("cfg,bs,B,D", [(2, 32, None, 128), (3, 64, 16, 128), (4, 32, None, 128), (4, 128, 12, 128),
+                                        (2, 16, None, 64), (4, 16, None, 64), (4, 32, 12, 64)])
+def test_block_sizes(clm_gpu, cfg, bs, B, D):
+    """Pages of 16 to 128 slots and head widths 128 and 64 (the block-size-
+    generic kernels and the D = 64 instantiations): the append bit-exact, then
+    attention over the cache it wrote, against the oracle.  Single-query rows
+    take the vector kernel; the 6-query blocks the matrix-core kernel with its
+    LDS ring."""
     import dataclasses
-    c = dataclasses.replace(synth.get_config(cfg), block_size=bs)
+    c = dataclasses.replace(synth.get_config(cfg), block_size=bs, D=D)
     x = synth.make_inputs(c, B=B)
     d = Dev(x, include_new=False)
     clm_gpu.kv_cache_append(d.k_new, d.v_new, d.k_cache, d.v_cache, d.block_table, d.len_before, block_size=bs)
@@ -199,7 +201,7 @@ def test_block_sizes(clm_gpu, cfg, bs, B):
                                  block_size=bs)
     keys, vals = logical(x)
     ref = oracle.decode_attention(x.f32(x.q), keys, vals, x.kv_len, scale, x.cfg.H_kv)
-    check_close(bf16_tensor_to_f32(o), ref, f"attention c{cfg} block size {bs}")
+    check_close(bf16_tensor_to_f32(o), ref, f"attention c{cfg} block size {bs} D {D}")
 
 @pytest.mark.parametrize("cfg", [2, 5])
 def test_decode_attention_split_plan_and_batch_order(clm_gpu, cfg):
