@@ -21,8 +21,9 @@ stage's vocabulary.  ``codebook_head_mlp`` computes that head:
 
 Readings where the page leaves a step open: no biases (as for the one-layer
 head); Mish as Misra (2019) defines it; the widened activation is stored in
-the step's element type (bf16) between the two products, rounded to nearest
-even (fp32 workloads keep it in float64).
+the step's element type (bf16) between the two products, rounded once from
+the exact (float64) value to the nearest bfloat16, ties to even (fp32
+workloads keep it in float64).
 """
 
 from __future__ import annotations
@@ -62,12 +63,19 @@ def mish(x):
 
 
 def round_to_bf16_f64(x):
-    """Round float64 values to the nearest bfloat16 (ties to even), via float32
-    (the kernel rounds its float32 activation), returned as float64."""
-    f = np.asarray(x, np.float64).astype(np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+    """Round float64 values to the nearest bfloat16 value (ties to the even
+    significand) in one step, returned as float64.  bfloat16 keeps 8
+    significant bits and float32's exponent range: a normal value
+    x = m * 2^e (0.5 <= |m| < 1) is a multiple of 2^(e-8) after rounding, and
+    below the smallest normal 2^-126 the step is the subnormal one, 2^-133.
+    Values past the largest finite bfloat16 become infinite."""
+    x = np.asarray(x, np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e.astype(np.int64) - 8, -133)
+    step = np.ldexp(1.0, q)
+    r = np.rint(x / step) * step            # np.rint rounds halves to even
+    big = np.abs(r) >= 2.0 ** 128           # past (2 - 2^-7) * 2^127
+    return np.where(big, np.copysign(np.inf, x), r)
 
 
 def codebook_head_mlp(h, W1, W2, head_id=None, act_bf16=True):

@@ -80,6 +80,31 @@ def test_bf16_rounding_of_the_activation():
     assert abs(r[3] - -3.140625) == 0
 
 
+def test_bf16_rounding_is_one_step_from_float64():
+    """One rounding from the exact value: 1 + 2^-8 + 2^-30 lies above the
+    midpoint between the bfloat16 neighbours 1 and 1 + 2^-7, so it rounds up;
+    rounding to float32 first would land on the midpoint 1 + 2^-8 and then
+    tie to 1.  Subnormal steps (2^-133), the largest finite value and the
+    overflow threshold are the format's own."""
+    from oracle.head import round_to_bf16_f64
+    x = 1.0 + 2 ** -8 + 2 ** -30
+    assert np.float32(x) == np.float32(1.0 + 2 ** -8)          # float32 first would tie ...
+    assert round_to_bf16_f64(np.array([x]))[0] == 1.0 + 2 ** -7  # ... one step rounds up
+    assert round_to_bf16_f64(np.array([-x]))[0] == -(1.0 + 2 ** -7)
+    assert round_to_bf16_f64(np.array([2.0 ** -133 * 0.75]))[0] == 2.0 ** -133
+    assert round_to_bf16_f64(np.array([2.0 ** -133 * 0.25]))[0] == 0.0
+    assert round_to_bf16_f64(np.array([2.0 ** -126 * (1 + 2 ** -8)]))[0] == 2.0 ** -126  # tie to even
+    top = (2 - 2 ** -7) * 2.0 ** 127                               # largest finite bfloat16
+    assert round_to_bf16_f64(np.array([top]))[0] == top
+    assert np.isinf(round_to_bf16_f64(np.array([(2 - 2 ** -9) * 2.0 ** 127])))[0]
+    # away from midpoints, the same as the float32 -> bfloat16 rounding torch does
+    import torch
+    y = np.random.default_rng(3).standard_normal(20000) * 10.0 ** np.random.default_rng(4).integers(-30, 30, 20000)
+    y32 = y.astype(np.float32).astype(np.float64)
+    want = torch.from_numpy(y32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(round_to_bf16_f64(y32), want)
+
+
 def test_two_layer_head_structure():
     # W1 rows = c_f e_{j(f)}: z[r, f] = c_f h[r, j(f)];  W2 = a b^T: logits = (act . b) a
     rng = np.random.default_rng(13)
