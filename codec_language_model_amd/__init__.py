@@ -23,8 +23,9 @@ from ._lib import CLM_BF16, CLM_F32, STATUS
 __all__ = [
     "ClmError", "load", "kv_cache_append", "rope_kv_cache_append", "kv_cache_append_fp8", "decode_attention",
     "decode_attention_fp8", "decode_attention_workspace_size",
-    "codebook_head", "codebook_head_mlp", "sample_or_argmax", "spec_verify", "spec_verify_bonus",
-    "Workspace",
+    "codebook_head", "codebook_head_mlp", "codebook_head_workspace_size", "codebook_head_mlp_workspace_size",
+    "sample_or_argmax", "spec_verify", "spec_verify_bonus",
+    "Workspace", "set_checked",
 ]
 
 
@@ -36,6 +37,13 @@ class ClmError(RuntimeError):
 
 def load():
     return _lib.load()
+
+
+def set_checked(on: bool) -> bool:
+    """Checked mode on or off (clm_set_checked); returns the previous setting.
+    In checked mode every call first validates its device-resident indices
+    and raises ClmError with CLM_ERR_DEVICE_DATA when one is out of range."""
+    return bool(load().clm_set_checked(1 if on else 0))
 
 
 def _torch():
@@ -69,6 +77,15 @@ def _cuda(name, t, dtype=None, ndim=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+def _out(name, t, shape, dtype):
+    """A caller-supplied output: a contiguous GPU tensor of exactly this shape
+    and element type (the kernels write every element of that shape)."""
+    _cuda(name, t, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return t
 
 
@@ -199,7 +216,7 @@ def decode_attention(q, k_cache, v_cache, block_table, kv_len, max_kv_len, scale
     if out is None:
         out = torch.empty_like(q)
     else:
-        _cuda("out", out, q.dtype, 4)
+        _out("out", out, q.shape, q.dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     need = decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len)
@@ -236,7 +253,11 @@ def decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, kv_
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _out("out", out, q.shape, torch.bfloat16)
     need = decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len)
+    if need == 0:
+        raise ClmError("clm_decode_attention_workspace_size", -1)
     if workspace is None:
         workspace = Workspace.get(need, q.device)
     _check("clm_decode_attention_fp8", lib.clm_decode_attention_fp8(
@@ -246,7 +267,30 @@ def decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, kv_
     return out
 
 
-def codebook_head(h, W, head_id=None, out=None):
+def codebook_head_workspace_size(M, d, V, G, bf16=True) -> int:
+    return int(load().clm_codebook_head_workspace_size(M, d, V, G, CLM_BF16 if bf16 else CLM_F32))
+
+
+def codebook_head_mlp_workspace_size(M, d, F, V, G) -> int:
+    return int(load().clm_codebook_head_mlp_workspace_size(M, d, F, V, G))
+
+
+def _head_workspace(need, workspace, device):
+    """The caller's workspace (checked by the library), or a cached one when
+    the plan needs scratch and none was given, or none."""
+    if workspace is not None:
+        _cuda("workspace", workspace, _torch().uint8, 1)
+        return workspace
+    if need == 0:
+        return None
+    return Workspace.get(need, device)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def codebook_head(h, W, head_id=None, out=None, workspace=None):
     """h [M,d]; W a [G,V,d] tensor or a list of G [V,d] tensors; head_id [M]
     int32 (required when G > 1).  Returns logits [M,V] float32."""
     torch = _torch()
@@ -265,14 +309,16 @@ def codebook_head(h, W, head_id=None, out=None):
     if out is None:
         out = torch.empty((M, V), dtype=torch.float32, device=h.device)
     else:
-        _cuda("out", out, torch.float32, 2)
+        _out("out", out, (M, V), torch.float32)
     arr = (C.c_void_p * G)(*[w.data_ptr() for w in Ws])
+    ws = _head_workspace(codebook_head_workspace_size(M, d, V, G, h.dtype == torch.bfloat16), workspace,
+                         h.device)
     _check("clm_codebook_head", lib.clm_codebook_head(
-        _ptr(h), arr, G, _ptr(head_id), _ptr(out), M, d, V, _dt(h), _stream()))
+        _ptr(h), arr, G, _ptr(head_id), _ptr(out), M, d, V, _dt(h), _ptr(ws), _nbytes(ws), _stream()))
     return out
 
 
-def codebook_head_mlp(h, W1, W2, head_id=None, act=None, out=None):
+def codebook_head_mlp(h, W1, W2, head_id=None, act=None, out=None, workspace=None):
     """Two-layer head: h [M,d] bf16; W1 a [G,F,d] tensor or list of G [F,d];
     W2 a [G,V,F] tensor or list of G [V,F]; head_id [M] int32 (required when
     G > 1); act [M,F] bf16 scratch for the widened activation (allocated when
@@ -300,15 +346,17 @@ def codebook_head_mlp(h, W1, W2, head_id=None, act=None, out=None):
     if act is None:
         act = torch.empty((M, F), dtype=torch.bfloat16, device=h.device)
     else:
-        _cuda("act", act, torch.bfloat16, 2)
+        _out("act", act, (M, F), torch.bfloat16)
     if out is None:
         out = torch.empty((M, V), dtype=torch.float32, device=h.device)
     else:
-        _cuda("out", out, torch.float32, 2)
+        _out("out", out, (M, V), torch.float32)
     a1 = (C.c_void_p * G)(*[w.data_ptr() for w in W1s])
     a2 = (C.c_void_p * G)(*[w.data_ptr() for w in W2s])
+    ws = _head_workspace(codebook_head_mlp_workspace_size(M, d, F, V, G), workspace, h.device)
     _check("clm_codebook_head_mlp", lib.clm_codebook_head_mlp(
-        _ptr(h), a1, a2, G, _ptr(head_id), _ptr(act), _ptr(out), M, d, F, V, _dt(h), _stream()))
+        _ptr(h), a1, a2, G, _ptr(head_id), _ptr(act), _ptr(out), M, d, F, V, _dt(h), _ptr(ws), _nbytes(ws),
+        _stream()))
     return out, act
 
 
@@ -326,6 +374,8 @@ def sample_or_argmax(logits, temperature=None, uniforms=None, vocab_valid=None, 
             _cuda(name, t, dt, 1)
     if out is None:
         out = torch.empty(M, dtype=torch.int32, device=logits.device)
+    else:
+        _out("out", out, (M,), torch.int32)
     _check("clm_sample_or_argmax", lib.clm_sample_or_argmax(
         _ptr(logits), M, V, logits.stride(0), _ptr(temperature), _ptr(uniforms), _ptr(vocab_valid),
         _ptr(out), _stream()))
@@ -349,8 +399,12 @@ def spec_verify(target_logits, draft_probs, draft_tokens, u_accept, u_resample, 
         raise ValueError("spec_verify: shape mismatch")
     if out_tokens is None:
         out_tokens = torch.empty((B, K), dtype=torch.int32, device=target_logits.device)
+    else:
+        _out("out_tokens", out_tokens, (B, K), torch.int32)
     if num_emitted is None:
         num_emitted = torch.empty(B, dtype=torch.int32, device=target_logits.device)
+    else:
+        _out("num_emitted", num_emitted, (B,), torch.int32)
     _check("clm_spec_verify", lib.clm_spec_verify(
         _ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resample),
         C.c_float(temperature), B, K, V, _ptr(out_tokens), _ptr(num_emitted), _stream()))
@@ -374,8 +428,12 @@ def spec_verify_bonus(target_logits, draft_probs, draft_tokens, u_accept, u_resa
         raise ValueError("spec_verify_bonus: shape mismatch")
     if out_tokens is None:
         out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=target_logits.device)
+    else:
+        _out("out_tokens", out_tokens, (B, K + 1), torch.int32)
     if num_emitted is None:
         num_emitted = torch.empty(B, dtype=torch.int32, device=target_logits.device)
+    else:
+        _out("num_emitted", num_emitted, (B,), torch.int32)
     _check("clm_spec_verify_bonus", lib.clm_spec_verify_bonus(
         _ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resample),
         C.c_float(temperature), B, K, V, _ptr(out_tokens), _ptr(num_emitted), _stream()))

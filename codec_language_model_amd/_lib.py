@@ -29,6 +29,7 @@ _sz = C.c_size_t
 SIGNATURES = {
     "clm_status_string": (C.c_char_p, [_i]),
     "clm_version": (_i, []),
+    "clm_set_checked": (_i, [_i]),
     "clm_kv_cache_append": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "clm_rope_kv_cache_append": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _f, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "clm_decode_attention_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -37,8 +38,10 @@ SIGNATURES = {
     "clm_kv_cache_append_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "clm_decode_attention_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
                                       _f, _vp, _sz, _vp]),
-    "clm_codebook_head": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _vp]),
-    "clm_codebook_head_mlp": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "clm_codebook_head_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "clm_codebook_head": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "clm_codebook_head_mlp_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "clm_codebook_head_mlp": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "clm_sample_or_argmax": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "clm_spec_verify": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _vp, _vp, _vp]),
     "clm_spec_verify_bonus": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _vp, _vp, _vp]),

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <atomic>
 #include <cstring>
 #include <mutex>
 
@@ -17,7 +18,12 @@ bool env_checked() {
   const char* v = std::getenv("CLM_CHECK");
   return v && *v && std::strcmp(v, "0") != 0;
 }
-const bool g_checked = env_checked();
+// Checked mode: CLM_CHECK at load time, then clm_set_checked.
+std::atomic<int> g_checked_flag{env_checked() ? 1 : 0};
+inline bool checked() { return g_checked_flag.load(std::memory_order_relaxed) != 0; }
+
+// (stream, KV head) pairs one attention call takes.
+constexpr long kMaxStreamHeads = 65536;
 
 constexpr int kMaxDevices = 64;
 int* g_bad[kMaxDevices] = {nullptr};
@@ -66,7 +72,9 @@ const char* clm_status_string(int status) {
   return "CLM_ERR_UNKNOWN";
 }
 
-int clm_version(void) { return 100; }
+int clm_version(void) { return 200; }
+
+int clm_set_checked(int on) { return g_checked_flag.exchange(on ? 1 : 0) ; }
 
 int clm_kv_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                         const int32_t* block_table, int max_blocks, const int32_t* len_before,
@@ -79,7 +87,7 @@ int clm_kv_cache_append(const void* k_new, const void* v_new, void* k_cache, voi
   if (!dt_ok(dt) || (D != 64 && D != 128) || !bs_ok(block_size)) return CLM_ERR_UNSUPPORTED;
   if ((long)T_new > (long)max_blocks * block_size) return CLM_ERR_CAPACITY;
   if ((long)B * H_kv > (1L << 31) - 1) return CLM_ERR_UNSUPPORTED;
-  if (g_checked) {
+  if (checked()) {
     const long lim = (long)max_blocks * block_size - T_new;
     int st = run_checks(stream, [&](int* bad) {
       hipError_t e = clm::launch_check_lengths(len_before, B, 0, (int)(lim > 0x7fffffff ? 0x7fffffff : lim), bad, stream);
@@ -109,7 +117,7 @@ int clm_rope_kv_cache_append(void* q, const void* k_new, const void* v_new, void
   if (!dt_ok(dt) || (D != 64 && D != 128) || !bs_ok(block_size)) return CLM_ERR_UNSUPPORTED;
   if ((long)T_new > (long)max_blocks * block_size) return CLM_ERR_CAPACITY;
   if ((long)B * H_kv > (1L << 31) - 1) return CLM_ERR_UNSUPPORTED;
-  if (g_checked) {
+  if (checked()) {
     const long lim = (long)max_blocks * block_size - T_new;
     int st = run_checks(stream, [&](int* bad) {
       hipError_t e = clm::launch_check_lengths(len_before, B, 0, (int)(lim > 0x7fffffff ? 0x7fffffff : lim), bad, stream);
@@ -126,6 +134,7 @@ int clm_rope_kv_cache_append(void* q, const void* k_new, const void* v_new, void
 
 size_t clm_decode_attention_workspace_size(int B, int Kq, int H_q, int H_kv, int D, int max_kv_len) {
   if (B < 1 || Kq < 1 || H_q < 1 || H_kv < 1 || (D != 64 && D != 128) || max_kv_len < Kq) return 0;
+  if (H_q % H_kv != 0 || B > 4096 || (long)B * H_kv > kMaxStreamHeads) return 0;
   clm::AttnPlan p;
   if (!clm::plan_decode_attention(B, Kq, H_q, H_kv, D, max_kv_len, &p)) return 0;
   return p.total_bytes;
@@ -143,11 +152,12 @@ int clm_decode_attention(const void* q, const void* k_cache, const void* v_cache
   if (H_q % H_kv != 0 || max_kv_len < Kq || !std::isfinite(scale)) return CLM_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return CLM_ERR_INVALID_ARG;
   if (!dt_ok(dt) || (D != 64 && D != 128) || !bs_ok(block_size) || B > 4096) return CLM_ERR_UNSUPPORTED;
+  if ((long)B * H_kv > kMaxStreamHeads) return CLM_ERR_UNSUPPORTED;
   if ((H_q / H_kv) * Kq > 16) return CLM_ERR_UNSUPPORTED;
   clm::AttnPlan p;
   if (!clm::plan_decode_attention(B, Kq, H_q, H_kv, D, max_kv_len, &p)) return CLM_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.total_bytes || !aligned(workspace, 256)) return CLM_ERR_WORKSPACE;
-  if (g_checked) {
+  if (checked()) {
     const long cap = (long)max_blocks * block_size;
     const int hi = (int)(cap < max_kv_len ? cap : max_kv_len);
     int st = run_checks(stream, [&](int* bad) {
@@ -174,7 +184,7 @@ int clm_kv_cache_append_fp8(const void* k_new, const void* v_new, void* k_cache,
   if ((D != 64 && D != 128) || !bs_ok(block_size)) return CLM_ERR_UNSUPPORTED;
   if ((long)T_new > (long)max_blocks * block_size) return CLM_ERR_CAPACITY;
   if ((long)B * H_kv > (1L << 31) - 1) return CLM_ERR_UNSUPPORTED;
-  if (g_checked) {
+  if (checked()) {
     const long lim = (long)max_blocks * block_size - T_new;
     int st = run_checks(stream, [&](int* bad) {
       hipError_t e = clm::launch_check_lengths(len_before, B, 0, (int)(lim > 0x7fffffff ? 0x7fffffff : lim), bad, stream);
@@ -204,11 +214,12 @@ int clm_decode_attention_fp8(const void* q, const void* k_cache, const void* v_c
       !aligned(v_scale, 16))
     return CLM_ERR_INVALID_ARG;
   if ((D != 64 && D != 128) || !bs_ok(block_size) || B > 4096) return CLM_ERR_UNSUPPORTED;
+  if ((long)B * H_kv > kMaxStreamHeads) return CLM_ERR_UNSUPPORTED;
   if ((H_q / H_kv) * Kq > 16) return CLM_ERR_UNSUPPORTED;
   clm::AttnPlan p;
   if (!clm::plan_decode_attention(B, Kq, H_q, H_kv, D, max_kv_len, &p)) return CLM_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.total_bytes || !aligned(workspace, 256)) return CLM_ERR_WORKSPACE;
-  if (g_checked) {
+  if (checked()) {
     const long cap = (long)max_blocks * block_size;
     const int hi = (int)(cap < max_kv_len ? cap : max_kv_len);
     int st = run_checks(stream, [&](int* bad) {
@@ -224,8 +235,28 @@ int clm_decode_attention_fp8(const void* q, const void* k_cache, const void* v_c
   return hip_status(clm::launch_decode_attention(a, p, stream));
 }
 
+size_t clm_codebook_head_workspace_size(int M, int d, int V, int G, clm_dtype dt) {
+  if (M < 1 || d < 1 || V < 1 || G < 1 || G > 8 || M > 65536 || !dt_ok(dt)) return 0;
+  if (dt != CLM_BF16) return 0;
+  return clm::plan_codebook_head(M, V, G).workspace_bytes;
+}
+
+size_t clm_codebook_head_mlp_workspace_size(int M, int d, int F, int V, int G) {
+  if (M < 1 || d < 1 || F < 1 || V < 1 || G < 1 || G > 8 || M > 65536) return 0;
+  const size_t a = clm::plan_codebook_head(M, F, G).workspace_bytes;
+  const size_t b = clm::plan_codebook_head(M, V, G).workspace_bytes;
+  return a > b ? a : b;
+}
+
+static bool workspace_ok(const void* ws, size_t bytes, size_t need) {
+  if (ws && !aligned(ws, 256)) return false;
+  if (need == 0) return true;
+  return ws && bytes >= need;
+}
+
 int clm_codebook_head(const void* h, const void* const* W, int G, const int32_t* head_id,
-                      float* logits, int M, int d, int V, clm_dtype dt, hipStream_t stream) {
+                      float* logits, int M, int d, int V, clm_dtype dt, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
   if (!h || !W || !logits) return CLM_ERR_INVALID_ARG;
   if (M < 1 || d < 1 || V < 1 || G < 1 || G > 8) return CLM_ERR_INVALID_ARG;
   if (G > 1 && !head_id) return CLM_ERR_INVALID_ARG;
@@ -235,7 +266,9 @@ int clm_codebook_head(const void* h, const void* const* W, int G, const int32_t*
   if (!dt_ok(dt) || M > 65536) return CLM_ERR_UNSUPPORTED;
   if (dt == CLM_BF16 && d % 128 != 0) return CLM_ERR_UNSUPPORTED;
   if (dt == CLM_F32 && d % 4 != 0) return CLM_ERR_UNSUPPORTED;
-  if (g_checked && G > 1) {
+  if (!workspace_ok(workspace, workspace_bytes, clm_codebook_head_workspace_size(M, d, V, G, dt)))
+    return CLM_ERR_WORKSPACE;
+  if (checked() && G > 1) {
     int st = run_checks(stream, [&](int* bad) { return clm::launch_check_ints(head_id, M, 0, G - 1, bad, stream); });
     if (st != CLM_OK) return st;
   }
@@ -250,7 +283,7 @@ int clm_codebook_head(const void* h, const void* const* W, int G, const int32_t*
 
 int clm_codebook_head_mlp(const void* h, const void* const* W1, const void* const* W2, int G,
                           const int32_t* head_id, void* act, float* logits, int M, int d, int F, int V,
-                          clm_dtype dt, hipStream_t stream) {
+                          clm_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!h || !W1 || !W2 || !act || !logits) return CLM_ERR_INVALID_ARG;
   if (M < 1 || d < 1 || F < 1 || V < 1 || G < 1 || G > 8) return CLM_ERR_INVALID_ARG;
   if (G > 1 && !head_id) return CLM_ERR_INVALID_ARG;
@@ -259,7 +292,9 @@ int clm_codebook_head_mlp(const void* h, const void* const* W1, const void* cons
   if (!aligned(h, 16) || !aligned(act, 16)) return CLM_ERR_INVALID_ARG;
   if (dt != CLM_BF16) return CLM_ERR_UNSUPPORTED;
   if (M > 65536 || d % 128 != 0 || F % 128 != 0) return CLM_ERR_UNSUPPORTED;
-  if (g_checked && G > 1) {
+  if (!workspace_ok(workspace, workspace_bytes, clm_codebook_head_mlp_workspace_size(M, d, F, V, G)))
+    return CLM_ERR_WORKSPACE;
+  if (checked() && G > 1) {
     int st = run_checks(stream, [&](int* bad) { return clm::launch_check_ints(head_id, M, 0, G - 1, bad, stream); });
     if (st != CLM_OK) return st;
   }
@@ -283,7 +318,7 @@ int clm_sample_or_argmax(const float* logits, int M, int V, int ld, const float*
   if (!logits || !tokens || M < 1 || V < 1 || ld < V) return CLM_ERR_INVALID_ARG;
   if (temperature && !uniforms) return CLM_ERR_INVALID_ARG;
   if (V > (1 << 20)) return CLM_ERR_UNSUPPORTED;
-  if (g_checked) {
+  if (checked()) {
     int st = run_checks(stream, [&](int* bad) {
       hipError_t e = hipSuccess;
       if (vocab_valid) e = clm::launch_check_ints(vocab_valid, M, 1, V, bad, stream);
@@ -305,7 +340,7 @@ static int spec_verify_impl(const float* target_logits, const float* draft_probs
     return CLM_ERR_INVALID_ARG;
   if (B < 1 || K < 1 || V < 1 || !std::isfinite(temperature) || temperature < 0.f) return CLM_ERR_INVALID_ARG;
   if (K + bonus > 16 || V > (1 << 20)) return CLM_ERR_UNSUPPORTED;
-  if (g_checked) {
+  if (checked()) {
     int st = run_checks(stream, [&](int* bad) {
       hipError_t e = clm::launch_check_ints(draft_tokens, B * K, 0, V - 1, bad, stream);
       if (e == hipSuccess) e = clm::launch_check_uniforms(u_accept, B * K, bad, stream);

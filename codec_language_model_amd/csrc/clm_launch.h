@@ -85,6 +85,13 @@ struct HeadArgs {
   bool bf16;
   uint16_t* act;   // non-null: write bf16(Mish(h W^T)) here ([M, V]) instead of logits
 };
+// Tile plan of the bf16 head (a deterministic function of M, V, G).
+struct HeadPlan {
+  int nv, mr, nw;            // codebook entries and rows per workgroup, waves
+  int row_chunks, nvt, nvt_pad;
+  size_t workspace_bytes;    // scratch the plan needs (none for these tiles)
+};
+HeadPlan plan_codebook_head(int M, int V, int G);
 hipError_t launch_codebook_head(const HeadArgs& a, hipStream_t s);
 
 struct SampleArgs {

@@ -44,16 +44,17 @@ struct HeadP {
 // Rows of stage grp that fall in row chunk rc (MR rows each, batch order) into
 // s_rows; slots past the last row repeat a valid row so loads stay in bounds.
 // Returns the chunk's row count (<= 0: nothing to do), the same in all lanes.
-template <int MR>
+template <int MR, int NT>
 __device__ __forceinline__ int gather_rows(const HeadP& P, int grp, int rc, int* s_rows, int* s_cnt,
                                            int tid, int lane, int w) {
+  constexpr int NW = NT / 64;
   int n_rows;
   if (P.G == 1) {
     n_rows = min(MR, P.M - rc * MR);
-    for (int i = tid; i < MR; i += 256) s_rows[i] = min(rc * MR + i, P.M - 1);
+    for (int i = tid; i < MR; i += NT) s_rows[i] = min(rc * MR + i, P.M - 1);
     __syncthreads();
   } else {
-    const int per = (P.M + 255) / 256;
+    const int per = (P.M + NT - 1) / NT;
     const int r0 = tid * per;
     int cnt = 0;
     for (int k = 0; k < per; ++k) {
@@ -64,8 +65,11 @@ __device__ __forceinline__ int gather_rows(const HeadP& P, int grp, int rc, int*
     if (lane == 63) s_cnt[w] = incl;
     __syncthreads();
     int rank = incl - cnt;
-    for (int i = 0; i < w; ++i) rank += s_cnt[i];
-    const int total = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    int total = 0;
+    for (int i = 0; i < NW; ++i) {
+      if (i < w) rank += s_cnt[i];
+      total += s_cnt[i];
+    }
     for (int k = 0; k < per; ++k) {
       const int r = r0 + k;
       if (r < P.M && clampi(P.head_id[r], 0, P.G - 1) == grp) {
@@ -76,20 +80,13 @@ __device__ __forceinline__ int gather_rows(const HeadP& P, int grp, int rc, int*
     }
     n_rows = min(MR, total - rc * MR);
     __syncthreads();
-    for (int i = tid; i < MR; i += 256)
+    for (int i = tid; i < MR; i += NT)
       if (n_rows > 0 && i >= n_rows) s_rows[i] = s_rows[0];
     __syncthreads();
   }
   return uniform(n_rows);
 }
 
-// LDS fed by DMA: S LDS stages of one 64-k chunk each, holding NV
-// codebook rows then MR h rows (128 bytes per row, the 16-byte pieces
-// XOR-swizzled by row so the operand reads are bank-conflict free).  Each
-// wave's DMA instruction fills 8 whole rows (1 KiB), lane l taking the piece
-// that belongs in slot l % 8.  S - 1 chunks are in flight while one is
-// multiplied; one barrier per chunk.  Waves are laid out 2 (entries) x 2
-// (rows); each owns NV/2 entries x MR/2 rows and writes its logits directly.
 // Mish(x) = x * tanh(softplus(x)), written with y = 1 + e^x as
 // x * (y^2 - 1) / (y^2 + 1) = x * n (n + 2) / (n (n + 2) + 2), n = e^x; for
 // x > 20 the ratio is 1 in fp32 (and n^2 would overflow past x = 44).
@@ -100,19 +97,40 @@ __device__ __forceinline__ float mish_f(float x) {
   return x * t / (t + 2.f);
 }
 
-template <int NV, int MR, int S, bool MISH>
-__global__ __launch_bounds__(256) void head_dma_kernel(HeadP P) {
+// LDS fed by DMA: S stages of one 64-k chunk each, holding NV codebook rows
+// then MR h rows (128 bytes per row, the 16-byte pieces XOR-swizzled by row
+// so the operand reads are bank-conflict free).  Each DMA instruction fills
+// 8 whole rows (1 KiB), lane l taking the piece that belongs in slot l % 8;
+// S - 1 chunks are in flight while one is multiplied, one barrier per chunk.
+//
+// The products are always accumulated as two chains: the even 32-k substeps
+// of the chunks (k = 64c .. 64c+31) in one set of accumulators and the odd
+// ones (k = 64c+32 .. 64c+63) in another, and the two are added once at the
+// end.  With NW = 8 waves the two chains belong to two groups of 4 waves,
+// which gives each SIMD two waves to overlap operand reads, DMA and matrix
+// products (the second group's sums reach the first through LDS); with
+// NW = 4 each wave keeps both chains.  Every tile shape and wave count thus
+// produces the same bits for a given row, whatever else is in the batch.
+// Within a group the 4 waves are laid out 2 (entries) x 2 (rows), each
+// owning NV/2 entries x MR/2 rows.
+template <int NV, int MR, int S, int NW, bool MISH>
+__global__ __launch_bounds__(NW * 64) void head_dma_kernel(HeadP P) {
   constexpr int KC = 64;                      // k per chunk
   constexpr int ROWS = NV + MR;               // LDS rows per stage
   constexpr int STAGE = ROWS * KC;            // bf16 elements per stage
-  constexpr int NI = ROWS / 32;               // DMA instructions per wave per chunk
+  constexpr int NT = NW * 64;
+  constexpr int NI = ROWS / (8 * NW);         // DMA instructions per wave per chunk
   constexpr int VTW = NV / 32, RTW = MR / 32; // 16-wide tiles per wave
+  constexpr int NCH = NW == 8 ? 1 : 2;        // chains (substeps) per wave
+  static_assert(ROWS % (8 * NW) == 0, "rows per stage");
   static_assert(S >= 2 && (S - 2) * NI < 64, "pipeline depth");
+  static_assert(NW == 4 || VTW * RTW * 4 * 64 * 16 <= S * STAGE * 2, "chain sums fit the ring");
   __shared__ int s_rows[MR];
-  __shared__ int s_cnt[4];
+  __shared__ int s_cnt[NW];
   __shared__ __attribute__((aligned(1024))) uint16_t s_buf[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int grp_w = NW == 8 ? (w >> 2) : 0, wq = w & 3;
   const int per_grp = P.nvt_pad * P.row_chunks;
   const int grp = blockIdx.x / per_grp;
   const int id = blockIdx.x - grp * per_grp;
@@ -122,17 +140,17 @@ __global__ __launch_bounds__(256) void head_dma_kernel(HeadP P) {
   const int vt = super * kXcds + (rem - rc * kXcds);
   if (vt >= P.nvt) return;
   const int v0 = vt * NV;
-  const int n_rows = gather_rows<MR>(P, grp, rc, s_rows, s_cnt, tid, lane, w);
+  const int n_rows = gather_rows<MR, NT>(P, grp, rc, s_rows, s_cnt, tid, lane, w);
   if (n_rows <= 0) return;
 
   const uint16_t* __restrict__ Wg = P.W[grp];
   const int nch = P.d / KC;
-  // DMA instruction j of wave w fills rows 8g..8g+7, g = 4 j + w; lane l reads
-  // row 8g + l/8, piece (l % 8) ^ (l / 8) (row & 7 == l / 8).
+  // DMA instruction j of wave w fills rows 8r..8r+7, r = NW j + w; lane l
+  // reads row 8r + l/8, piece (l % 8) ^ (l / 8) (row & 7 == l / 8).
   const uint16_t* src[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
-    const int R = 8 * (4 * j + w) + (lane >> 3);
+    const int R = 8 * (NW * j + w) + (lane >> 3);
     const int piece = (lane & 7) ^ (lane >> 3);
     const uint16_t* row = R < NV ? Wg + (size_t)min(v0 + R, P.V - 1) * P.d
                                  : P.h + (size_t)s_rows[R - NV] * P.d;
@@ -143,46 +161,48 @@ __global__ __launch_bounds__(256) void head_dma_kernel(HeadP P) {
     const uint32_t base = lds0 + (uint32_t)(stage * STAGE * 2);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      dma16(src[j] + chunk * KC, uniform(base + (uint32_t)((4 * j + w) * 1024)));
+      dma16(src[j] + chunk * KC, uniform(base + (uint32_t)((NW * j + w) * 1024)));
   };
 
-  const int wv = w & 1, wr = w >> 1;
+  const int wv = wq & 1, wr = wq >> 1;
   const int l16 = lane & 15, lg = lane >> 4;
-  int aoff[VTW][2], boff[RTW][2];
+  int aoff[NCH][VTW], boff[NCH][RTW];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int c = 4 * s + lg;
+  for (int s = 0; s < NCH; ++s) {
+    const int c = 4 * (NW == 8 ? grp_w : s) + lg;
 #pragma unroll
     for (int t = 0; t < VTW; ++t) {
       const int R = (NV / 2) * wv + 16 * t + l16;
-      aoff[t][s] = R * KC + ((c ^ (R & 7)) << 3);
+      aoff[s][t] = R * KC + ((c ^ (R & 7)) << 3);
     }
 #pragma unroll
     for (int t = 0; t < RTW; ++t) {
       const int R = NV + wr * (MR / 2) + 16 * t + l16;
-      boff[t][s] = R * KC + ((c ^ (R & 7)) << 3);
+      boff[s][t] = R * KC + ((c ^ (R & 7)) << 3);
     }
   }
-  f32x4_t acc[VTW][RTW];
+  f32x4_t acc[NCH][VTW][RTW];
 #pragma unroll
-  for (int a = 0; a < VTW; ++a)
+  for (int s = 0; s < NCH; ++s)
 #pragma unroll
-    for (int t = 0; t < RTW; ++t) acc[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < VTW; ++a)
+#pragma unroll
+      for (int t = 0; t < RTW; ++t) acc[s][a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int stage) __attribute__((always_inline)) {
     const uint16_t* sb = s_buf + stage * STAGE;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < NCH; ++s) {
       bf16x8_t A[VTW], Bm[RTW];
 #pragma unroll
-      for (int t = 0; t < VTW; ++t) A[t] = *reinterpret_cast<const bf16x8_t*>(sb + aoff[t][s]);
+      for (int t = 0; t < VTW; ++t) A[t] = *reinterpret_cast<const bf16x8_t*>(sb + aoff[s][t]);
 #pragma unroll
-      for (int t = 0; t < RTW; ++t) Bm[t] = *reinterpret_cast<const bf16x8_t*>(sb + boff[t][s]);
+      for (int t = 0; t < RTW; ++t) Bm[t] = *reinterpret_cast<const bf16x8_t*>(sb + boff[s][t]);
 #pragma unroll
       for (int t = 0; t < RTW; ++t)
 #pragma unroll
         for (int a = 0; a < VTW; ++a)
-          acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[a], Bm[t], acc[a][t], 0, 0, 0);
+          acc[s][a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[a], Bm[t], acc[s][a][t], 0, 0, 0);
     }
   };
 
@@ -203,6 +223,30 @@ __global__ __launch_bounds__(256) void head_dma_kernel(HeadP P) {
     stage = stage == S - 1 ? 0 : stage + 1;
   }
 
+  // even chain + odd chain
+  f32x4_t tot[VTW][RTW];
+  if constexpr (NW == 8) {
+    __syncthreads();                          // every wave is done with the ring
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(s_buf);
+    if (grp_w == 1) {
+#pragma unroll
+      for (int a = 0; a < VTW; ++a)
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) red[((wq * VTW + a) * RTW + t) * 64 + lane] = acc[0][a][t];
+    }
+    __syncthreads();
+    if (grp_w == 1) return;
+#pragma unroll
+    for (int a = 0; a < VTW; ++a)
+#pragma unroll
+      for (int t = 0; t < RTW; ++t) tot[a][t] = acc[0][a][t] + red[((wq * VTW + a) * RTW + t) * 64 + lane];
+  } else {
+#pragma unroll
+    for (int a = 0; a < VTW; ++a)
+#pragma unroll
+      for (int t = 0; t < RTW; ++t) tot[a][t] = acc[0][a][t] + acc[NCH - 1][a][t];
+  }
+
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
     const int R = wr * (MR / 2) + 16 * t + l16;
@@ -212,8 +256,8 @@ __global__ __launch_bounds__(256) void head_dma_kernel(HeadP P) {
 #pragma unroll
         for (int a = 0; a < VTW; ++a) {
           const int v = v0 + (NV / 2) * wv + 16 * a + 4 * lg;
-          const f32x4_t y = {mish_f(acc[a][t][0]), mish_f(acc[a][t][1]), mish_f(acc[a][t][2]),
-                             mish_f(acc[a][t][3])};
+          const f32x4_t y = {mish_f(tot[a][t][0]), mish_f(tot[a][t][1]), mish_f(tot[a][t][2]),
+                             mish_f(tot[a][t][3])};
           if (v + 3 < P.V) {
             *reinterpret_cast<uint2*>(orow + v) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
           } else {
@@ -228,11 +272,11 @@ __global__ __launch_bounds__(256) void head_dma_kernel(HeadP P) {
         for (int a = 0; a < VTW; ++a) {
           const int v = v0 + (NV / 2) * wv + 16 * a + 4 * lg;
           if (v + 3 < P.V) {
-            *reinterpret_cast<f32x4_t*>(orow + v) = acc[a][t];
+            *reinterpret_cast<f32x4_t*>(orow + v) = tot[a][t];
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (v + e < P.V) orow[v + e] = acc[a][t][e];
+              if (v + e < P.V) orow[v + e] = tot[a][t][e];
           }
         }
       }
@@ -273,6 +317,31 @@ __global__ __launch_bounds__(256) void head_gemv_f32_kernel(GemvP P) {
 
 }  // namespace
 
+HeadPlan plan_codebook_head(int M, int V, int G) {
+  // MR in {32, 64, 96, 128}: the fewest padded rows for the rows one stage
+  // is expected to hold (all M for one stage; M/G on average otherwise), the
+  // larger on ties; NV in {128, 64, 32}: the widest that still gives
+  // kHeadWGs working workgroups; 8 waves where the tile is tall enough to
+  // keep two waves per SIMD busy (and its rows split into 64-row DMA rounds).
+  HeadPlan p{};
+  const int m_est = G == 1 ? M : (M + G - 1) / G;
+  int mr = 128;
+  for (int c : {96, 64, 32})
+    if ((m_est + c - 1) / c * c < (m_est + mr - 1) / mr * mr) mr = c;
+  const int rc_est = (m_est + mr - 1) / mr;
+  int nv = 32;
+  for (int c : {128, 64})
+    if ((long)((V + c - 1) / c) * rc_est * G >= kHeadWGs) { nv = c; break; }
+  p.mr = mr;
+  p.nv = nv;
+  p.nw = (mr >= 96 && (nv + mr) % 64 == 0) ? 8 : 4;
+  p.row_chunks = (M + mr - 1) / mr;
+  p.nvt = (V + nv - 1) / nv;
+  p.nvt_pad = (p.nvt + kXcds - 1) / kXcds * kXcds;
+  p.workspace_bytes = 0;
+  return p;
+}
+
 hipError_t launch_codebook_head(const HeadArgs& a, hipStream_t s) {
   if (a.bf16) {
     HeadP P;
@@ -282,28 +351,21 @@ hipError_t launch_codebook_head(const HeadArgs& a, hipStream_t s) {
     P.logits = a.logits;
     P.act = a.act;
     P.G = a.G; P.M = a.M; P.d = a.d; P.V = a.V;
-    // LDS-staged tiles of NV codebook entries x MR rows: MR in {32, 64, 128}
-    // with the least row padding (the larger on ties), then the widest NV in
-    // {128, 64, 32} that still gives kHeadWGs workgroups (else 32)
-    int mr = 128;
-    for (int c : {64, 32})
-      if ((a.M + c - 1) / c * c < (a.M + mr - 1) / mr * mr) mr = c;
-    P.row_chunks = (a.M + mr - 1) / mr;
-    int nv = 32;
-    for (int c : {128, 64})
-      if ((long)((a.V + c - 1) / c) * P.row_chunks * a.G >= kHeadWGs) { nv = c; break; }
-    P.nvt = (a.V + nv - 1) / nv;
-    P.nvt_pad = (P.nvt + kXcds - 1) / kXcds * kXcds;
-    const dim3 g((unsigned)((long)P.nvt_pad * P.row_chunks * a.G)), b(256);
-#define CLM_HEAD_DMA(NV_, MR_)                                                                    \
-    if (nv == NV_ && mr == MR_) {                                                                 \
-      if (a.act) hipLaunchKernelGGL((head_dma_kernel<NV_, MR_, 4, true>), g, b, 0, s, P);         \
-      else hipLaunchKernelGGL((head_dma_kernel<NV_, MR_, 4, false>), g, b, 0, s, P);              \
-      return hipGetLastError();                                                                   \
+    const HeadPlan hp = plan_codebook_head(a.M, a.V, a.G);
+    P.row_chunks = hp.row_chunks;
+    P.nvt = hp.nvt;
+    P.nvt_pad = hp.nvt_pad;
+    const dim3 g((unsigned)((long)P.nvt_pad * P.row_chunks * a.G)), b(hp.nw * 64);
+#define CLM_HEAD_DMA(NV_, MR_)                                                                         \
+    if (hp.nv == NV_ && hp.mr == MR_) {                                                                \
+      constexpr int NW_ = (MR_ >= 96 && (NV_ + MR_) % 64 == 0) ? 8 : 4;                                \
+      if (a.act) hipLaunchKernelGGL((head_dma_kernel<NV_, MR_, 4, NW_, true>), g, b, 0, s, P);         \
+      else hipLaunchKernelGGL((head_dma_kernel<NV_, MR_, 4, NW_, false>), g, b, 0, s, P);              \
+      return hipGetLastError();                                                                        \
     }
-    CLM_HEAD_DMA(128, 128) CLM_HEAD_DMA(128, 64) CLM_HEAD_DMA(128, 32)
-    CLM_HEAD_DMA(64, 128) CLM_HEAD_DMA(64, 64) CLM_HEAD_DMA(64, 32)
-    CLM_HEAD_DMA(32, 128) CLM_HEAD_DMA(32, 64) CLM_HEAD_DMA(32, 32)
+    CLM_HEAD_DMA(128, 128) CLM_HEAD_DMA(128, 96) CLM_HEAD_DMA(128, 64) CLM_HEAD_DMA(128, 32)
+    CLM_HEAD_DMA(64, 128) CLM_HEAD_DMA(64, 96) CLM_HEAD_DMA(64, 64) CLM_HEAD_DMA(64, 32)
+    CLM_HEAD_DMA(32, 128) CLM_HEAD_DMA(32, 96) CLM_HEAD_DMA(32, 64) CLM_HEAD_DMA(32, 32)
 #undef CLM_HEAD_DMA
     return hipErrorInvalidValue;
   }

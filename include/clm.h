@@ -30,10 +30,14 @@
  *   kernels on `stream` (NULL = the null stream) and returns.  It never
  *   synchronises and never reads device memory on the host, so a fixed-shape
  *   step can be captured in a HIP graph.  The one exception is checked mode
- *   (environment variable CLM_CHECK=1, read once at load): each call then first
+ *   (on when the environment variable CLM_CHECK is set to a value other than
+ *   "0" at load, and switched with clm_set_checked): each call then first
  *   runs a validator over its device-resident indices (lengths, block ids,
  *   head ids, tokens, uniforms), synchronises, and returns
  *   CLM_ERR_DEVICE_DATA without launching anything if one is out of range.
+ *   Checked mode allocates one 4-byte device counter per GPU on first use
+ *   and clears it with hipMemsetAsync before each validation, so it is for
+ *   tests and debugging, not for graph capture.
  * Errors.  A call returns CLM_OK or a negative clm_status.  Host-visible
  *   arguments are checked before any HIP call: a call that returns an error
  *   other than CLM_ERR_HIP has enqueued nothing.  Device-resident values are
@@ -74,6 +78,14 @@ const char* clm_status_string(int status);
 
 /* ABI version: major*10000 + minor*100 + patch. */
 int clm_version(void);
+
+/*
+ * Checked mode on (on != 0) or off for every later call of this process, on
+ * every GPU; returns the previous setting (0 or 1).  The initial setting
+ * comes from CLM_CHECK.  Host-only: no HIP call.  Calls already running on
+ * other host threads keep the setting they started with.
+ */
+int clm_set_checked(int on);
 
 /* --------------------------------------------------------------------------
  * KV cache layout (paged).  Optimizing Streaming Text-to-Speech Models for
@@ -234,16 +246,28 @@ int clm_decode_attention_fp8(const void* q, const void* k_cache, const void* v_c
  *   W        host array of G device pointers, each [V, d] (element type dt)
  *   head_id  [M] int32 in [0, G), or NULL when G == 1
  *   logits   [M, V] float32           output
+ *   workspace, workspace_bytes        caller-owned scratch of at least
+ *            clm_codebook_head_workspace_size(M, d, V, G, dt) bytes, 256-byte
+ *            aligned when non-NULL.  NULL with 0 bytes is valid when that size
+ *            is 0, which it is for every tile plan of this version; the
+ *            argument is part of the call so that a plan needing scratch
+ *            (partial sums of a split k range) changes no signature.
  * Each W_g is streamed from memory once per call for up to 128 rows of its
  * group; more rows are taken in chunks whose workgroups read the same W tile
  * close together in time, so it comes from memory about once.
- * Arithmetic: products of dt values accumulated in fp32.
+ * Arithmetic (bf16): products of bf16 values accumulated in fp32 in two
+ * chains, over the even and over the odd 32-wide k blocks, added once at the
+ * end; a row's logits do not depend on the other rows of the call (nor on M,
+ * G or the tile plan).  fp32: one fp32 dot product per logit.
  * Errors: INVALID_ARG (null, sizes < 1, G > 8, head_id NULL with G > 1,
  *   h or a W not 16-byte aligned), UNSUPPORTED (bf16 with d % 128 != 0, f32
- *   with d % 4 != 0, M > 65536, unknown dt).
+ *   with d % 4 != 0, M > 65536, unknown dt), WORKSPACE (smaller than the
+ *   query's size, or non-NULL and misaligned).
  */
+size_t clm_codebook_head_workspace_size(int M, int d, int V, int G, clm_dtype dt);
 int clm_codebook_head(const void* h, const void* const* W, int G, const int32_t* head_id,
-                      float* logits, int M, int d, int V, clm_dtype dt, hipStream_t stream);
+                      float* logits, int M, int d, int V, clm_dtype dt, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Two-layer audio head (TontaubeV1, audio head paragraph: each stage's head
@@ -258,16 +282,20 @@ int clm_codebook_head(const void* h, const void* const* W, int G, const int32_t*
  *   act      [M, F] bf16, caller-owned: written with the widened activation
  *            (rounded to nearest even), then read by the second product
  *   logits   [M, V] float32 output
+ *   workspace, workspace_bytes   as for clm_codebook_head, sized by
+ *            clm_codebook_head_mlp_workspace_size(M, d, F, V, G)
  * Two kernel launches on `stream`: the first product with Mish fused into its
- * epilogue, then the second.  Arithmetic: products of bf16 accumulated in
- * fp32; Mish in fp32.
+ * epilogue, then the second.  Arithmetic: each product as in
+ * clm_codebook_head (bf16 products, fp32 accumulation in two chains); Mish in
+ * fp32.
  * Errors: INVALID_ARG (null, sizes < 1, G > 8, head_id NULL with G > 1, h, act
  *   or a weight not 16-byte aligned), UNSUPPORTED (dt not bf16, d or F not a
- *   multiple of 128, M > 65536).
+ *   multiple of 128, M > 65536), WORKSPACE (as for clm_codebook_head).
  */
+size_t clm_codebook_head_mlp_workspace_size(int M, int d, int F, int V, int G);
 int clm_codebook_head_mlp(const void* h, const void* const* W1, const void* const* W2, int G,
                           const int32_t* head_id, void* act, float* logits, int M, int d, int F, int V,
-                          clm_dtype dt, hipStream_t stream);
+                          clm_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * One token per row (TontaubeV1 decodes later stages greedily; Section 3.3

@@ -40,6 +40,23 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(_lib.SIGNATURES) == set(names)
 
 
+def test_checked_mode_switch(lib):
+    prev = lib.clm_set_checked(1)
+    try:
+        assert lib.clm_set_checked(1) == 1
+        assert lib.clm_set_checked(0) == 1
+        assert lib.clm_set_checked(0) == 0
+        # host validation still runs first: no HIP call for a bad argument
+        lib.clm_set_checked(1)
+        assert append(lib, B=0) == INVALID
+        assert attn(lib, q=N) == INVALID
+    finally:
+        lib.clm_set_checked(prev)
+    # the binding's wrapper returns the previous setting as a bool
+    assert clm.set_checked(True) is bool(prev)
+    assert clm.set_checked(bool(prev)) is True
+
+
 def test_status_strings_and_version(lib):
     for code, name in _lib.STATUS.items():
         assert lib.clm_status_string(code).decode() == name
@@ -100,6 +117,7 @@ def test_attention_argument_errors(lib):
     assert attn(lib, Hq=34, Hk=2) == UNSUPPORTED          # 17 query heads per KV head
     assert attn(lib, Kq=6, Hq=32, Hk=8) == UNSUPPORTED    # 4 * 6 = 24 rows per KV head
     assert attn(lib, B=5000) == UNSUPPORTED
+    assert attn(lib, B=4096, Hq=32, Hk=32, ws_bytes=1 << 40) == UNSUPPORTED   # 131072 (stream, KV head) pairs
     assert attn(lib) == WORKSPACE                          # one byte short
     assert attn(lib, ws=N, ws_bytes=1 << 30) == WORKSPACE
     assert attn(lib, ws=C.c_void_p(0x100010), ws_bytes=1 << 30) == WORKSPACE  # misaligned
@@ -116,17 +134,35 @@ def test_workspace_size_query(lib):
     # (m, l) + accumulators for every (stream, KV head, split, row): at 256
     # streams of up to 8192 keys a split is 1024 tokens, so 8 splits
     assert big >= 256 * 8 * 8 * 2 * 130 * 4
-    assert f(4096, 1, 16, 32, 128, 100) == 0            # more than 65536 (stream, KV head) pairs
+    # more than 65536 (stream, KV head) pairs, with a valid head grouping
+    assert f(4096, 1, 32, 32, 128, 100) == 0
+    assert f(2048, 1, 32, 32, 128, 100) > 0             # exactly 65536 pairs
+    assert f(4096, 1, 16, 32, 128, 100) == 0            # H_q not a multiple of H_kv
+
+
+def test_head_workspace_size_queries(lib):
+    """Every tile plan of the workloads' shapes runs without scratch (the
+    workspace argument is accepted and may be NULL); invalid sizes give 0."""
+    f = lib.clm_codebook_head_workspace_size
+    for M, d, V, G in [(1, 256, 4096, 1), (16, 2048, 16384, 1), (64, 2048, 4096, 3), (192, 2048, 4096, 1),
+                       (256, 2048, 16384, 1), (65536, 2048, 4096, 8)]:
+        assert f(M, d, V, G, 1) == 0
+        assert f(M, d, V, G, 0) == 0
+    assert f(0, 2048, 4096, 1, 1) == 0 and f(70000, 2048, 4096, 1, 1) == 0 and f(4, 2048, 4096, 9, 1) == 0
+    g = lib.clm_codebook_head_mlp_workspace_size
+    assert g(256, 2048, 4096, 16384, 1) == 0 and g(64, 2048, 4096, 4096, 3) == 0
 
 
 def test_two_layer_head_argument_errors(lib):
     W = (C.c_void_p * 2)(0x100000, 0x200000)
     f = lib.clm_codebook_head_mlp
-    assert f(P, W, W, 2, N, P, P, 16, 2048, 4096, 4096, 1, S) == INVALID      # G > 1 needs head_id
-    assert f(P, W, W, 1, N, N, P, 16, 2048, 4096, 4096, 1, S) == INVALID      # act missing
-    assert f(P, W, W, 1, N, P, P, 16, 2048, 4000, 4096, 1, S) == UNSUPPORTED  # F % 128
-    assert f(P, W, W, 1, N, P, P, 16, 2000, 4096, 4096, 1, S) == UNSUPPORTED  # d % 128
-    assert f(P, W, W, 1, N, P, P, 16, 2048, 4096, 4096, 0, S) == UNSUPPORTED  # fp32 not supported
+    assert f(P, W, W, 2, N, P, P, 16, 2048, 4096, 4096, 1, N, 0, S) == INVALID      # G > 1 needs head_id
+    assert f(P, W, W, 1, N, N, P, 16, 2048, 4096, 4096, 1, N, 0, S) == INVALID      # act missing
+    assert f(P, W, W, 1, N, P, P, 16, 2048, 4000, 4096, 1, N, 0, S) == UNSUPPORTED  # F % 128
+    assert f(P, W, W, 1, N, P, P, 16, 2000, 4096, 4096, 1, N, 0, S) == UNSUPPORTED  # d % 128
+    assert f(P, W, W, 1, N, P, P, 16, 2048, 4096, 4096, 0, N, 0, S) == UNSUPPORTED  # fp32 not supported
+    # a workspace, when given, must be 256-byte aligned
+    assert f(P, W, W, 1, N, P, P, 16, 2048, 4096, 4096, 1, C.c_void_p(0x100040), 1 << 20, S) == WORKSPACE
 
 
 def test_rope_append_argument_errors(lib):
@@ -149,11 +185,14 @@ def test_rope_append_argument_errors(lib):
 
 def test_head_sampler_verify_argument_errors(lib):
     Ws = (C.c_void_p * 3)(0x100000, 0x200000, 0x300000)
-    assert lib.clm_codebook_head(P, Ws, 3, N, P, 64, 2048, 4096, 1, S) == INVALID   # G > 1 needs head_id
-    assert lib.clm_codebook_head(P, Ws, 9, P, P, 64, 2048, 4096, 1, S) == INVALID
-    assert lib.clm_codebook_head(P, Ws, 1, N, P, 0, 2048, 4096, 1, S) == INVALID
-    assert lib.clm_codebook_head(P, Ws, 1, N, P, 4, 2000, 4096, 1, S) == UNSUPPORTED
-    assert lib.clm_codebook_head(N, Ws, 1, N, P, 4, 2048, 4096, 1, S) == INVALID
+    head = lib.clm_codebook_head
+    assert head(P, Ws, 3, N, P, 64, 2048, 4096, 1, N, 0, S) == INVALID   # G > 1 needs head_id
+    assert head(P, Ws, 9, P, P, 64, 2048, 4096, 1, N, 0, S) == INVALID
+    assert head(P, Ws, 1, N, P, 0, 2048, 4096, 1, N, 0, S) == INVALID
+    assert head(P, Ws, 1, N, P, 4, 2000, 4096, 1, N, 0, S) == UNSUPPORTED
+    assert head(N, Ws, 1, N, P, 4, 2048, 4096, 1, N, 0, S) == INVALID
+    assert head(P, Ws, 1, N, P, 70000, 2048, 4096, 1, N, 0, S) == UNSUPPORTED
+    assert head(P, Ws, 1, N, P, 64, 2048, 4096, 1, C.c_void_p(0x100010), 4096, S) == WORKSPACE  # misaligned
     assert lib.clm_sample_or_argmax(P, 4, 100, 99, N, N, N, P, S) == INVALID       # ld < V
     assert lib.clm_sample_or_argmax(P, 4, 100, 100, P, N, N, P, S) == INVALID      # T without u
     assert lib.clm_sample_or_argmax(P, 4, (1 << 20) + 1, (1 << 20) + 1, N, N, N, P, S) == UNSUPPORTED

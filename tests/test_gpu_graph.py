@@ -1,7 +1,8 @@
 """The decode step captured as one HIP graph: every C-ABI call only enqueues
 kernels on the caller's stream (no allocation, host synchronisation or
 memset), so a fixed-shape step can be captured and replayed.  Each replay,
-with eager work in between, must reproduce the eager step bit for bit."""
+with eager work in between that clears the outputs, is checked against the
+oracle's chained step, and the replays must agree bit for bit."""
 
 import math
 import sys
@@ -9,8 +10,9 @@ import sys
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from parity import to_torch
+from parity import bf16_tensor_to_f32, check_argmax, check_close, check_sampled, check_verify, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +24,7 @@ def _announce(request):
 
 
 @pytest.mark.parametrize("cfg,B", [(2, None), (4, None), (5, 24)])
-def test_step_graph_replays_match_eager(clm_gpu, cfg, B):
+def test_step_graph_replays_match_oracle(clm_gpu, cfg, B):
     import torch
     x = synth.make_inputs(cfg, B=B)
     c = x.cfg
@@ -64,8 +66,29 @@ def test_step_graph_replays_match_eager(clm_gpu, cfg, B):
         torch.cuda.synchronize()
         return [t.clone() for t in (o, logits, tokens, out_tok, num)]
 
-    step()
-    ref = snapshot()
+    keys = [x.logical_k(b) for b in range(c.B)]
+    vals = [x.logical_v(b) for b in range(c.B)]
+    s_np = x.spec_inputs() if c.mode == "spec" else None
+    temp_np = np.full(c.M, c.temperature, np.float32) if c.mode == "sample" else None
+    u_np = x.uniforms() if c.mode == "sample" else None
+    ref = oracle.decode_step(x.f32(x.q), keys, vals, x.kv_len, 1.0 / math.sqrt(c.D), c.H_kv, x.f32(x.W),
+                             x.head_id, bf, mode=c.mode,
+                             temperature=(c.temperature if c.mode == "spec" else temp_np), uniforms=u_np,
+                             spec=s_np)
+
+    def check_against_oracle(got, what):
+        g_o, g_logits, g_tok, g_out, g_num = got
+        check_close(bf16_tensor_to_f32(g_o), ref["o"], f"{what} attention")
+        check_close(g_logits.cpu().numpy(), ref["logits"], f"{what} logits")
+        if c.mode == "spec":
+            check_verify(g_out.cpu().numpy(), g_num.cpu().numpy(), ref["logits"].reshape(c.B, c.Kq, c.V),
+                         s_np["draft_probs"], s_np["draft_tokens"], s_np["u_accept"], s_np["u_resample"],
+                         c.temperature, f"{what} verify")
+        elif c.mode == "sample":
+            check_sampled(g_tok.cpu().numpy(), ref["logits"], temp_np, u_np, f"{what} sample")
+        else:
+            check_argmax(g_tok.cpu().numpy(), ref["logits"], f"{what} argmax")
+
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -75,17 +98,22 @@ def test_step_graph_replays_match_eager(clm_gpu, cfg, B):
     with torch.cuda.graph(graph):
         step()
     torch.cuda.synchronize()
+    first = None
     for r in range(3):
         for t in (o, logits, tokens, out_tok, num):   # eager work between replays
             t.zero_()
         torch.cuda.synchronize()
         graph.replay()
         got = snapshot()
-        for name, a, b in zip(("o", "logits", "tokens", "out_tokens", "num_emitted"), got, ref):
+        check_against_oracle(got, f"graph c{cfg} replay {r}")
+        if first is None:
+            first = got
+            continue
+        for name, a, b in zip(("o", "logits", "tokens", "out_tokens", "num_emitted"), got, first):
             if name in ("tokens",) and c.mode == "spec":
                 continue
             if name in ("out_tokens", "num_emitted") and c.mode != "spec":
                 continue
             assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), (cfg, r, name)
-    print(f"graph c{cfg}: 3 replays bit-identical to the eager step")
+    print(f"graph c{cfg}: 3 replays match the oracle and each other bit for bit")

@@ -480,8 +480,9 @@ def test_chained_step(clm_gpu, cfg):
 
 def test_full_size_high_concurrency(clm_gpu):
     """256 streams, log-uniform KV lengths 64..8192, head 2048->16384, greedy:
-    the launch configuration the benchmark times; sampled streams (shortest,
-    longest and a spread between) checked against the oracle."""
+    the launch configuration the benchmark times.  Every stream's attention
+    output, logits and argmax token against the oracle, and the whole pool
+    after the append bit for bit."""
     x = synth.make_inputs(5)
     c = x.cfg
     d = Dev(x, include_new=False)
@@ -490,24 +491,177 @@ def test_full_size_high_concurrency(clm_gpu):
     o = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len, scale=scale)
     logits = clm_gpu.codebook_head(o.view(c.M, c.d_model), d.W)
     tok = clm_gpu.sample_or_argmax(logits).cpu().numpy()
-    order = np.argsort(x.kv_len)
-    streams = sorted(set([int(order[0]), int(order[-1])] + [int(order[i]) for i in np.linspace(0, c.B - 1, 10).astype(int)]))
-    keys = {b: x.logical_k(b) for b in streams}
-    vals = {b: x.logical_v(b) for b in streams}
-    ref = oracle.decode_step(x.f32(x.q), keys, vals, x.kv_len, scale, c.H_kv, x.f32(x.W), None, True,
-                             streams=streams)
-    o_np = bf16_tensor_to_f32(o)
-    lg = logits.cpu().numpy()
-    for b in streams:
-        check_close(o_np[b], ref["o"][b], f"full-size attention stream {b} (kv_len {x.kv_len[b]})")
-        check_close(lg[b], ref["logits"][b], f"full-size logits stream {b}")
-        check_argmax(tok[b:b + 1], ref["logits"][b:b + 1], f"full-size argmax stream {b}")
-    # append at full size: each sampled stream's new row sits where the
-    # block table puts position len_before[b]
-    kc, vc = d.k_cache, d.v_cache
-    for b in streams:
-        pos = int(x.len_before[b])
-        blk = int(x.block_table[b, pos // c.block_size])
-        slot = pos % c.block_size
-        np.testing.assert_array_equal(as_bits(kc[blk, :, slot, :].contiguous()), x.k_new[b, 0].view(np.int16))
-        np.testing.assert_array_equal(as_bits(vc[blk, :, :, slot].contiguous()), x.v_new[b, 0].view(np.int16))
+    keys, vals = logical(x)
+    ref = oracle.decode_step(x.f32(x.q), keys, vals, x.kv_len, scale, c.H_kv, x.f32(x.W), None, True)
+    err_o = check_close(bf16_tensor_to_f32(o), ref["o"], "full-size attention, all 256 streams")
+    err_l = check_close(logits.cpu().numpy(), ref["logits"], "full-size logits, all 256 streams")
+    ex = check_argmax(tok, ref["logits"], "full-size argmax, all 256 streams")
+    print(f"full size: max |o err| {err_o:.3g}, max |logit err| {err_l:.3g}, argmax exempt {ex}/{c.M}")
+    # the append at full size: the whole pool against the oracle's append
+    rk, rv = oracle.kv_cache_append(d.k_pool_host, d.v_pool_host, x.block_table, x.len_before,
+                                    x.k_new, x.v_new, c.block_size)
+    np.testing.assert_array_equal(as_bits(d.k_cache), rk.view(np.int16))
+    np.testing.assert_array_equal(as_bits(d.v_cache), rv.view(np.int16))
+
+
+def test_append_partitions_bit_identical(clm_gpu):
+    """The cache after T single-row appends (len_before + t, t = 0..T-1) is
+    bit-identical to the cache after one T-row append, and both equal the
+    oracle's, on the 6-query workload; likewise split 2 + 4 and 3 + 3."""
+    x = inputs(4)
+    c = x.cfg
+    T = c.Kq
+    ref_k, ref_v = oracle.kv_cache_append(*x.build_pool(include_new=False), x.block_table, x.len_before,
+                                          x.k_new, x.v_new, c.block_size)
+    for parts in ([T], [1] * T, [2, 4], [3, 3]):
+        d = Dev(x, include_new=False)
+        t0 = 0
+        for n in parts:
+            lb = to_torch((x.len_before + t0).astype(np.int32))
+            clm_gpu.kv_cache_append(d.k_new[:, t0:t0 + n].contiguous(), d.v_new[:, t0:t0 + n].contiguous(),
+                                    d.k_cache, d.v_cache, d.block_table, lb, block_size=c.block_size)
+            t0 += n
+        np.testing.assert_array_equal(as_bits(d.k_cache), ref_k.view(np.int16), err_msg=str(parts))
+        np.testing.assert_array_equal(as_bits(d.v_cache), ref_v.view(np.int16), err_msg=str(parts))
+
+
+@pytest.mark.parametrize("cfg,sub", [(5, 100), (4, 24)])
+def test_batch_compaction_bit_identical(clm_gpu, cfg, sub):
+    """Dropping streams from a batch (a serving engine compacting finished or
+    cancelled streams away) leaves every remaining stream's attention output,
+    logits and token bits unchanged.  The attention split length depends on
+    streams x KV heads x max_kv_len; it is the same for the full and the
+    compacted batch here (1024 tokens for the 256-stream mix and its 100-stream
+    subset, 512 for the 32 x 6-query batch and its 24-stream subset), and the
+    head's arithmetic does not depend on the row count.  The subset keeps the
+    streams in a shuffled order."""
+    import torch
+    x = inputs(cfg)
+    c = x.cfg
+    d = Dev(x, include_new=True)
+    scale = 1.0 / math.sqrt(c.D)
+    spec = x.spec_inputs() if c.mode == "spec" else None
+
+    def run(sel):
+        idx = torch.from_numpy(np.asarray(sel, np.int64)).to(d.q.device)
+        q = d.q[idx].contiguous()
+        o = clm_gpu.decode_attention(q, d.k_cache, d.v_cache, d.block_table[idx].contiguous(),
+                                     d.kv_len[idx].contiguous(), d.max_kv_len, scale=scale)
+        lg = clm_gpu.codebook_head(o.view(len(sel) * c.Kq, c.d_model), d.W,
+                                   None if d.head_id is None else d.head_id.view(c.B, c.Kq)[idx].reshape(-1).contiguous())
+        if spec is None:
+            tk = clm_gpu.sample_or_argmax(lg)
+            return as_bits(o), lg.cpu().numpy(), tk.cpu().numpy()
+        dp, dtok, ua, ur = (to_torch(spec[k][np.asarray(sel)]) for k in ("draft_probs", "draft_tokens",
+                                                                          "u_accept", "u_resample"))
+        toks, num = clm_gpu.spec_verify(lg.view(len(sel), c.Kq, c.V), dp, dtok, ua, ur, c.temperature)
+        return as_bits(o), lg.cpu().numpy(), (toks.cpu().numpy(), num.cpu().numpy())
+
+    full = run(np.arange(c.B))
+    sel = np.random.default_rng(77).permutation(c.B)[:sub]
+    part = run(sel)
+    np.testing.assert_array_equal(part[0], full[0][sel])
+    rows = (sel[:, None] * c.Kq + np.arange(c.Kq)[None, :]).reshape(-1)
+    np.testing.assert_array_equal(part[1].view(np.uint32), full[1][rows].view(np.uint32))
+    if spec is None:
+        np.testing.assert_array_equal(part[2], full[2][rows])
+    else:
+        np.testing.assert_array_equal(part[2][0], full[2][0][sel])
+        np.testing.assert_array_equal(part[2][1], full[2][1][sel])
+    print(f"compaction c{cfg}: {sub} of {c.B} streams bit-identical")
+
+
+def test_checked_mode_reports_bad_device_data(clm_gpu):
+    """With checked mode switched on in-process (clm_set_checked), every call
+    validates its device-resident indices first: an out-of-range block id, a
+    length beyond the block table, a head id, a uniform and a drafted token
+    each give CLM_ERR_DEVICE_DATA and launch nothing; valid data passes and
+    the results match the unchecked calls bit for bit."""
+    import torch
+    x = inputs(4)
+    c = x.cfg
+    d = Dev(x, include_new=False)
+    prev = clm_gpu.set_checked(True)
+    try:
+        def status(fn):
+            try:
+                fn()
+                return 0
+            except clm_gpu.ClmError as e:
+                return e.status
+
+        bad_bt = d.block_table.clone()
+        bad_bt[3, 0] = x.num_blocks + 5                   # block id past the pool
+        k_before = as_bits(d.k_cache)
+        assert status(lambda: clm_gpu.kv_cache_append(d.k_new, d.v_new, d.k_cache, d.v_cache, bad_bt,
+                                                      d.len_before)) == -6
+        assert np.array_equal(as_bits(d.k_cache), k_before)     # nothing launched
+        bad_lb = d.len_before.clone()
+        bad_lb[1] = x.max_blocks * c.block_size                 # no room for the new rows
+        assert status(lambda: clm_gpu.kv_cache_append(d.k_new, d.v_new, d.k_cache, d.v_cache, d.block_table,
+                                                      bad_lb)) == -6
+        assert status(lambda: clm_gpu.kv_cache_append(d.k_new, d.v_new, d.k_cache, d.v_cache, d.block_table,
+                                                      d.len_before)) == 0
+        bad_len = d.kv_len.clone()
+        bad_len[0] = d.max_kv_len + 1                           # above the caller's bound
+        assert status(lambda: clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, bad_len,
+                                                       d.max_kv_len)) == -6
+        assert status(lambda: clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, bad_bt, d.kv_len,
+                                                       d.max_kv_len)) == -6
+        o_chk = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len)
+        h = o_chk.view(c.M, c.d_model)
+        W3 = torch.stack([d.W[0]] * 3)
+        hid = torch.zeros(c.M, dtype=torch.int32, device=h.device)
+        hid[5] = 3                                              # only heads 0..2 exist
+        assert status(lambda: clm_gpu.codebook_head(h, W3, hid)) == -6
+        lg_chk = clm_gpu.codebook_head(h, d.W)
+        u = torch.full((c.M,), 0.5, device=h.device)
+        u[7] = 1.0                                              # uniforms lie in [0, 1)
+        temp = torch.full((c.M,), 0.7, device=h.device)
+        assert status(lambda: clm_gpu.sample_or_argmax(lg_chk, temp, u)) == -6
+        vv = torch.full((c.M,), c.V + 1, dtype=torch.int32, device=h.device)   # mask past V
+        assert status(lambda: clm_gpu.sample_or_argmax(lg_chk, None, None, vv)) == -6
+        s = x.spec_inputs()
+        dp, dtok, ua, ur = _spec_inputs_torch(s)
+        bad_tok = dtok.clone()
+        bad_tok[2, 1] = c.V
+        assert status(lambda: clm_gpu.spec_verify(lg_chk.view(c.B, c.Kq, c.V), dp, bad_tok, ua, ur, 0.7)) == -6
+        toks_chk, num_chk = clm_gpu.spec_verify(lg_chk.view(c.B, c.Kq, c.V), dp, dtok, ua, ur, 0.7)
+    finally:
+        clm_gpu.set_checked(prev)
+    o = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len)
+    lg = clm_gpu.codebook_head(o.view(c.M, c.d_model), d.W)
+    toks, num = clm_gpu.spec_verify(lg.view(c.B, c.Kq, c.V), dp, dtok, ua, ur, 0.7)
+    assert np.array_equal(as_bits(o), as_bits(o_chk))
+    assert torch.equal(lg, lg_chk) and torch.equal(toks, toks_chk) and torch.equal(num, num_chk)
+
+
+def test_codebook_head_rows_independent_of_batch(clm_gpu):
+    """A row's logits are the same bits whatever else is in the call: the
+    head always sums two fp32 chains (even and odd 32-wide k blocks), so the
+    tile plan - 4 or 8 waves, 32..128 rows and 32..128 codebook entries per
+    workgroup, chosen from M, V and G - changes no result.  Rows are taken
+    from a 256-row call into calls of 100, 37, 16 and 1 rows (one stage) and
+    into grouped calls over 3 stages; all against the oracle too."""
+    import torch
+    rng = np.random.default_rng(4242)
+    d, V = 2048, 4096
+    h = synth.f32_to_bf16_bits(rng.standard_normal((256, d)).astype(np.float32))
+    W = synth.f32_to_bf16_bits((rng.standard_normal((3, V, d)) * 0.02).astype(np.float32))
+    ht, Wt = to_torch(h, bf16=True), to_torch(W, bf16=True)
+    full = clm_gpu.codebook_head(ht, Wt[0:1]).cpu().numpy()
+    ref = oracle.codebook_head(synth.bf16_bits_to_f32(h), synth.bf16_bits_to_f32(W[0:1]))
+    check_close(full, ref, "head 256 rows")
+    for m in (100, 37, 16, 1):
+        sel = np.sort(rng.choice(256, size=m, replace=False))
+        part = clm_gpu.codebook_head(ht[torch.from_numpy(sel).to(ht.device)].contiguous(), Wt[0:1]).cpu().numpy()
+        np.testing.assert_array_equal(part.view(np.uint32), full[sel].view(np.uint32), err_msg=f"M={m}")
+    # grouped: every row of stage g equals the same row in a one-stage call on W[g]
+    hid = rng.integers(0, 3, size=256).astype(np.int32)
+    grouped = clm_gpu.codebook_head(ht, Wt, to_torch(hid)).cpu().numpy()
+    for g in range(3):
+        rows = np.nonzero(hid == g)[0]
+        one = clm_gpu.codebook_head(ht[torch.from_numpy(rows).to(ht.device)].contiguous(), Wt[g:g + 1]).cpu().numpy()
+        np.testing.assert_array_equal(grouped[rows].view(np.uint32), one.view(np.uint32), err_msg=f"stage {g}")
+    check_close(grouped, oracle.codebook_head(synth.bf16_bits_to_f32(h), synth.bf16_bits_to_f32(W), hid),
+                "grouped head 256 rows")
