@@ -7,7 +7,6 @@
 #include <cstdlib>
 #include <atomic>
 #include <cstring>
-#include <mutex>
 
 #include "../../include/clm.h"
 #include "clm_launch.h"
@@ -25,9 +24,6 @@ inline bool checked() { return g_checked_flag.load(std::memory_order_relaxed) !=
 // (stream, KV head) pairs one attention call takes.
 constexpr long kMaxStreamHeads = 65536;
 
-constexpr int kMaxDevices = 64;
-int* g_bad[kMaxDevices] = {nullptr};
-std::mutex g_bad_mu;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -36,15 +32,12 @@ bool bs_ok(int bs) { return bs >= 16 && bs <= 256 && bs % 16 == 0; }
 
 // Runs `launch(bad)` (validators on `stream`), waits, and reports whether any
 // device value was out of range.
+// The count lives in the library's static device memory (clm::check_counter),
+// so checked mode allocates nothing.
 template <class F>
 int run_checks(hipStream_t stream, F launch) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CLM_ERR_HIP;
-  {
-    std::lock_guard<std::mutex> lk(g_bad_mu);
-    if (!g_bad[dev] && hipMalloc(&g_bad[dev], sizeof(int)) != hipSuccess) return CLM_ERR_HIP;
-  }
-  int* bad = g_bad[dev];
+  int* bad = nullptr;
+  if (clm::check_counter(&bad) != hipSuccess) return CLM_ERR_HIP;
   if (hipMemsetAsync(bad, 0, sizeof(int), stream) != hipSuccess) return CLM_ERR_HIP;
   if (launch(bad) != hipSuccess) return CLM_ERR_HIP;
   int h = 0;

@@ -1,7 +1,15 @@
 // Checked mode (CLM_CHECK=1): validators for device-resident indices.  Each
 // adds the number of out-of-range entries it finds to *bad.
+#include <mutex>
+
 #include "clm_device.h"
 #include "clm_launch.h"
+
+// Checked mode's count of out-of-range entries, in the library's static
+// device memory (each GPU holds its own copy).  The name is a host-side
+// stand-in; the device address comes from hipGetSymbolAddress, once per
+// device (clm::check_counter).
+static __device__ __align__(256) int check_count;
 
 namespace clm {
 namespace {
@@ -46,6 +54,26 @@ int grid_for(int n) {
 }
 
 }  // namespace
+
+hipError_t check_counter(int** ptr) {
+  constexpr int kMaxDev = 64;
+  static int* addr[kMaxDev] = {nullptr};
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(check_count));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<int*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_check_lengths(const int32_t* len, int n, int lo, int hi, int* bad, hipStream_t s) {
   hipLaunchKernelGGL(check_range_kernel, dim3(grid_for(n)), dim3(256), 0, s, len, n, lo, hi, bad);

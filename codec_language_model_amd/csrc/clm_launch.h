@@ -118,8 +118,10 @@ struct VerifyArgs {
 };
 hipError_t launch_spec_verify(const VerifyArgs& a, hipStream_t s);
 
-// Checked mode: validators write the number of bad entries into *bad_count
-// (device int, zeroed by the caller).
+// Checked mode: validators add the number of bad entries to *bad (device int,
+// zeroed by the caller); check_counter gives the library's static counter on
+// the current device.
+hipError_t check_counter(int** ptr);
 hipError_t launch_check_lengths(const int32_t* len, int n, int lo, int hi, int* bad, hipStream_t s);
 hipError_t launch_check_block_table(const int32_t* bt, const int32_t* len, int B, int max_blocks,
                                     int len_add, int block_size, int num_blocks, int* bad,

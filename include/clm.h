@@ -35,9 +35,10 @@
  *   runs a validator over its device-resident indices (lengths, block ids,
  *   head ids, tokens, uniforms), synchronises, and returns
  *   CLM_ERR_DEVICE_DATA without launching anything if one is out of range.
- *   Checked mode allocates one 4-byte device counter per GPU on first use
- *   and clears it with hipMemsetAsync before each validation, so it is for
- *   tests and debugging, not for graph capture.
+ *   Checked mode counts bad entries in a 4-byte counter in the library's
+ *   static device memory (no allocation), cleared with hipMemsetAsync before
+ *   each validation; it synchronises, so it is for tests and debugging, not
+ *   for graph capture.
  * Errors.  A call returns CLM_OK or a negative clm_status.  Host-visible
  *   arguments are checked before any HIP call: a call that returns an error
  *   other than CLM_ERR_HIP has enqueued nothing.  Device-resident values are
