@@ -22,7 +22,7 @@ from ._lib import CLM_BF16, CLM_F32, STATUS
 
 __all__ = [
     "ClmError", "load", "kv_cache_append", "rope_kv_cache_append", "kv_cache_append_fp8", "decode_attention",
-    "decode_attention_fp8", "decode_attention_workspace_size",
+    "decode_attention_fp8", "decode_attention_workspace_size", "decode_attention_noalloc",
     "codebook_head", "codebook_head_mlp", "codebook_head_workspace_size", "codebook_head_mlp_workspace_size",
     "sample_or_argmax", "spec_verify", "spec_verify_bonus",
     "Workspace", "set_checked",
@@ -228,6 +228,34 @@ def decode_attention(q, k_cache, v_cache, block_table, kv_len, max_kv_len, scale
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(kv_len),
         int(max_kv_len), _ptr(out), B, Kq, H_q, H_kv, D, block_size, nb, C.c_float(scale), _dt(q),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def decode_attention_noalloc(q, k_cache, v_cache, block_table, kv_len, max_kv_len, scale=None, out=None,
+                             block_size=16):
+    """decode_attention without a workspace: the library's static 32 MiB
+    per-GPU scratch holds the split partials, so the call allocates no device
+    memory (``out`` must then be given by the caller).  Calls that overlap on
+    one GPU race on that scratch."""
+    torch = _torch()
+    lib = load()
+    _cuda("q", q, ndim=4)
+    _cuda("k_cache", k_cache, q.dtype, 4)
+    _cuda("v_cache", v_cache, q.dtype, 4)
+    _cuda("block_table", block_table, torch.int32, 2)
+    _cuda("kv_len", kv_len, torch.int32, 1)
+    B, Kq, H_q, D = q.shape
+    nb, H_kv = k_cache.shape[0], k_cache.shape[1]
+    if tuple(k_cache.shape) != (nb, H_kv, block_size, D) or tuple(v_cache.shape) != (nb, H_kv, D, block_size):
+        raise ValueError("decode_attention_noalloc: cache shape mismatch")
+    if out is None:
+        raise ValueError("decode_attention_noalloc: the caller provides `out` (nothing is allocated here)")
+    _out("out", out, q.shape, q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check("clm_decode_attention_noalloc", lib.clm_decode_attention_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(kv_len),
+        int(max_kv_len), _ptr(out), B, Kq, H_q, H_kv, D, block_size, nb, C.c_float(scale), _dt(q), _stream()))
     return out
 
 

@@ -166,6 +166,41 @@ int clm_decode_attention(const void* q, const void* k_cache, const void* v_cache
   return hip_status(clm::launch_decode_attention(a, p, stream));
 }
 
+int clm_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, int max_blocks, const int32_t* kv_len,
+                                 int max_kv_len, void* o, int B, int Kq, int H_q, int H_kv, int D,
+                                 int block_size, int num_blocks, float scale, clm_dtype dt,
+                                 hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !kv_len || !o) return CLM_ERR_INVALID_ARG;
+  if (B < 1 || Kq < 1 || H_q < 1 || H_kv < 1 || D < 1 || max_blocks < 1 || num_blocks < 1 ||
+      block_size < 1)
+    return CLM_ERR_INVALID_ARG;
+  if (H_q % H_kv != 0 || max_kv_len < Kq || !std::isfinite(scale)) return CLM_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return CLM_ERR_INVALID_ARG;
+  if (!dt_ok(dt) || (D != 64 && D != 128) || !bs_ok(block_size) || B > 4096) return CLM_ERR_UNSUPPORTED;
+  if ((long)B * H_kv > kMaxStreamHeads) return CLM_ERR_UNSUPPORTED;
+  if ((H_q / H_kv) * Kq > 16) return CLM_ERR_UNSUPPORTED;
+  clm::AttnPlan p;
+  if (!clm::plan_decode_attention(B, Kq, H_q, H_kv, D, max_kv_len, &p)) return CLM_ERR_UNSUPPORTED;
+  if (p.total_bytes > clm::kAttentionScratchBytes) return CLM_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (clm::attention_scratch(&scratch) != hipSuccess) return CLM_ERR_HIP;
+  if (checked()) {
+    const long cap = (long)max_blocks * block_size;
+    const int hi = (int)(cap < max_kv_len ? cap : max_kv_len);
+    int st = run_checks(stream, [&](int* bad) {
+      hipError_t e = clm::launch_check_lengths(kv_len, B, Kq, hi, bad, stream);
+      if (e != hipSuccess) return e;
+      return clm::launch_check_block_table(block_table, kv_len, B, max_blocks, 0, block_size,
+                                           num_blocks, bad, stream);
+    });
+    if (st != CLM_OK) return st;
+  }
+  clm::AttnArgs a{q, k_cache, v_cache, block_table, kv_len, o, scratch, max_blocks, max_kv_len,
+                  B, Kq, H_q, H_kv, D, block_size, num_blocks, scale, dt == CLM_BF16};
+  return hip_status(clm::launch_decode_attention(a, p, stream));
+}
+
 int clm_kv_cache_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             float* k_scale, float* v_scale, const int32_t* block_table, int max_blocks,
                             const int32_t* len_before, int B, int T_new, int H_kv, int D, int block_size,

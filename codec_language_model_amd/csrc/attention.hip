@@ -44,10 +44,18 @@
 // on the MFMA units.  Up to kRingMaxB streams, its tiles reach LDS by
 // global-to-LDS DMA into a per-wave ring of kRingStages stages, so three tiles
 // are in flight per wave without holding registers.
+#include <mutex>
 #include <type_traits>
 
 #include "clm_device.h"
 #include "clm_launch.h"
+
+// Split partials of clm_decode_attention_noalloc: the library's own scratch,
+// one copy per GPU for the life of the process (zero-filled at load; the
+// attention kernels need no initial contents).  Host code never passes this
+// name to a kernel: it is a host-side stand-in, so the device address comes
+// from hipGetSymbolAddress, once per device (clm::attention_scratch).
+static __device__ __align__(256) uint8_t scratch[clm::kAttentionScratchBytes];
 
 namespace clm {
 namespace {
@@ -1079,6 +1087,26 @@ bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_l
   p->acc_offset = p->ml_offset + align256(slots * 2 * sizeof(float));
   p->total_bytes = p->acc_offset + align256(slots * (size_t)D * sizeof(float));
   return true;
+}
+
+hipError_t attention_scratch(void** ptr) {
+  constexpr int kMaxDev = 64;
+  static void* addr[kMaxDev] = {nullptr};
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {

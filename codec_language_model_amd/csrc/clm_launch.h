@@ -75,6 +75,12 @@ struct AttnArgs {
 };
 hipError_t launch_decode_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 
+// The library's static scratch for attention split partials (one copy per
+// GPU): its size, and its device address on the current device (looked up
+// once per device with hipGetSymbolAddress).
+constexpr size_t kAttentionScratchBytes = (size_t)32 << 20;
+hipError_t attention_scratch(void** ptr);
+
 struct HeadArgs {
   const void* h;
   const void* W[8];

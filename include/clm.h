@@ -200,6 +200,28 @@ int clm_decode_attention(const void* q, const void* k_cache, const void* v_cache
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * clm_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that must not call hipMalloc,
+ * harnesses that forbid it).  The same computation, kernels and results as
+ * clm_decode_attention with the same arguments, but with no workspace: the
+ * split partials go to the library's own static device scratch of
+ * 32 MiB (33554432 bytes) per GPU, held from the first use on that GPU
+ * until the process ends.  The call allocates nothing: the scratch's device
+ * address is looked up once per device (hipGetSymbolAddress) and reused.
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap in
+ * time on one GPU (other streams, other host threads) race and give wrong
+ * results; order them on one stream.  The scratch needs no initial contents.
+ * Errors: those of clm_decode_attention, with WORKSPACE when
+ * clm_decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len) is
+ * above 32 MiB (the check precedes any HIP call).
+ */
+int clm_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, int max_blocks, const int32_t* kv_len,
+                                 int max_kv_len, void* o, int B, int Kq, int H_q, int H_kv, int D,
+                                 int block_size, int num_blocks, float scale, clm_dtype dt,
+                                 hipStream_t stream);
+
+/*
  * FP8 (E4M3) KV cache (the speculative-decoding blog, "Engine-Level
  * Optimizations with TensorRT-LLM": FP8 quantization of the target model's
  * attention; here applied to the KV cache every step reads, halving its

@@ -123,6 +123,26 @@ def test_attention_argument_errors(lib):
     assert attn(lib, ws=C.c_void_p(0x100010), ws_bytes=1 << 30) == WORKSPACE  # misaligned
 
 
+def test_noalloc_attention_rejects_plans_beyond_its_scratch(lib):
+    """The allocation-free attention takes plans up to 32 MiB of split
+    partials; beyond that it returns WORKSPACE before any HIP call (here
+    there is no GPU, so a HIP call would have given CLM_ERR_HIP)."""
+    f = lib.clm_decode_attention_noalloc
+    ws = lib.clm_decode_attention_workspace_size
+    def call(B, max_kv_len, **kw):
+        a = dict(q=P, Hq=16, Hk=8, D=128, Kq=1)
+        a.update(kw)
+        return f(a["q"], P, P, P, 4096, P, max_kv_len, P, B, a["Kq"], a["Hq"], a["Hk"], a["D"], 16, 1 << 20,
+                 C.c_float(0.088), 1, S)
+    assert ws(256, 1, 16, 8, 128, 65536) > 32 << 20
+    assert call(256, 65536) == WORKSPACE
+    assert ws(4096, 1, 16, 8, 128, 4096) > 32 << 20
+    assert call(4096, 4096) == WORKSPACE
+    assert call(256, 8192, q=N) == INVALID                 # argument errors come first
+    assert call(256, 8192, Hq=12) == INVALID
+    assert call(256, 8192, D=96) == UNSUPPORTED
+
+
 def test_workspace_size_query(lib):
     f = lib.clm_decode_attention_workspace_size
     assert f(0, 1, 16, 8, 128, 100) == 0
