@@ -6,10 +6,11 @@
 A step is the whole hot path over one batch: kv_cache_append ->
 decode_attention -> codebook_head -> sample_or_argmax (spec_verify for the
 speculative workload), all through the C ABI, inputs resident in HBM.  The
-timed steps are eager calls; --graph on captures the step once as a HIP graph
-and times its replays instead (faster only where launches dominate, as in
-the one-stream fp32 workload).  Per-call durations always come from HIP
-events around eager calls.  The
+timed steps are eager calls; --graph on times launches of the native decode
+loop instead (--graph-steps steps captured as one HIP graph by
+clm_decode_loop_create, lengths advancing on the device, reset between
+launches by two small device copies).  Per-call durations always come from
+HIP events around eager calls.  The
 default workload is 256 streams with log-uniform KV lengths in [64, 8192],
 16 query / 8 KV heads of width 128, bf16 cache, a 2048 -> 16384 head and
 greedy decoding: the one that fills the GPU and exposes the attention
@@ -68,7 +69,11 @@ def parse():
                     help="plain KV append, or the append with rotary embedding at logical positions "
                          "(len_before + 1000 + t, base 1e6) applied to the new keys and the queries")
     ap.add_argument("--graph", choices=("on", "off"), default="off",
-                    help="time the step as replays of one captured HIP graph (on) or as eager calls (off)")
+                    help="time the steps as launches of the native decode loop - --graph-steps steps "
+                         "captured as one HIP graph, lengths advancing on the device (on) - or as eager "
+                         "calls (off)")
+    ap.add_argument("--graph-steps", type=int, default=16,
+                    help="steps per captured decode loop with --graph on")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -241,11 +246,18 @@ def main():
     torch.cuda.set_device(dev)
 
     cfg = synth.get_config(args.workload)
+    graph = args.graph == "on"
+    if graph and (args.kv != "bf16" or args.head != "linear"):
+        print("--graph on runs the decode loop of the bf16/fp32 cache and the linear head", file=sys.stderr)
+        sys.exit(2)
     t_gen = time.perf_counter()
     x = synth.make_inputs(cfg)
     c = x.cfg
     bf = c.dtype == "bf16"
-    kp, vp = x.build_pool(include_new=False)
+    n_loop = max(1, args.graph_steps) if graph else 1
+    # pages for the loop's later steps (the same pages as the step's own for
+    # every position the eager step touches)
+    kp, vp, bt_np, _ = x.pool_with_room((n_loop - 1) * c.Kq)
     log(f"[bench] {c.workload}: inputs drawn in {time.perf_counter() - t_gen:.1f} s "
         f"(sum kv_len {int(x.kv_len.sum())}, pool {kp.nbytes * 2 / 2**30:.2f} GiB)")
 
@@ -275,7 +287,7 @@ def main():
         del k_cache, v_cache
         k_cache = v_cache = None
     del kp, vp
-    bt, kv_len, len_before = dev_t(x.block_table, False), dev_t(x.kv_len, False), dev_t(x.len_before, False)
+    bt, kv_len, len_before = dev_t(bt_np, False), dev_t(x.kv_len, False), dev_t(x.len_before, False)
     k_new, v_new, q = dev_t(x.k_new, bf), dev_t(x.v_new, bf), dev_t(x.q, bf)
     W = dev_t(x.W, bf)
     head_id = dev_t(x.head_id, False) if c.G > 1 else None
@@ -290,7 +302,7 @@ def main():
         W2 = (torch.randn((c.G, c.V, F), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
         act = torch.empty((c.M, F), dtype=torch.bfloat16, device=dev)
         mlp = (W1, W2, act, F)
-    max_kv = int(x.kv_len.max())
+    max_kv = int(x.kv_len.max()) + (n_loop - 1) * c.Kq
     rope_pos = None
     if args.append == "rope":
         rope_pos = dev_t((x.len_before[:, None] + 1000 + np.arange(c.Kq)[None, :]).astype(np.int32), False)
@@ -347,31 +359,51 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # The step as one HIP graph: every call only enqueues kernels on the
-    # current stream (no allocation, host sync or memset), so a fixed-shape
-    # step captures as is and replays without per-launch host overhead.
+    # The decode loop: n_loop steps captured natively as one HIP graph
+    # (clm_decode_loop_*), the lengths (and positions) advancing on the
+    # device between steps.  Each launch runs n_loop steps; the lengths are
+    # then reset by two small device copies so every launch sees the same
+    # workload.
     run = step
-    if args.graph == "on":
-        graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
-        run = graph.replay
-        for _ in range(args.warmup):
+    steps_per_run = 1
+    if graph:
+        rep = lambda t: t.unsqueeze(0).expand((n_loop,) + tuple(t.shape)).contiguous()
+        lg_all = torch.empty((n_loop, c.M, c.V), dtype=torch.float32, device=dev)
+        lp = dict(k_cache=k_cache, v_cache=v_cache, block_table=bt, len_before=len_before, kv_len=kv_len,
+                  max_kv_len=max_kv, k_new=rep(k_new), v_new=rep(v_new), q=rep(q), W=W, head_id=head_id,
+                  o=torch.empty_like(rep(q)), logits=lg_all, mode=c.mode, attn_workspace=ws,
+                  block_size=c.block_size)
+        if rope_pos is not None:
+            lp.update(positions=rope_pos, rope_base=1.0e6)
+        if c.mode == "spec":
+            lp.update(spec_temperature=c.temperature, draft_probs=rep(spec[0].view(c.B, c.Kq, c.V)),
+                      draft_tokens=rep(spec[1]), u_accept=rep(spec[2]), u_resample=rep(spec[3]),
+                      out_tokens=torch.empty((n_loop, c.B, c.Kq), dtype=torch.int32, device=dev),
+                      num_emitted=torch.empty((n_loop, c.B), dtype=torch.int32, device=dev))
+        else:
+            lp.update(tokens=torch.empty((n_loop, c.M), dtype=torch.int32, device=dev))
+            if c.mode == "sample":
+                lp.update(temperature=rep(temp), uniforms=rep(uni))
+        state0 = [t.clone() for t in (len_before, kv_len) + ((rope_pos,) if rope_pos is not None else ())]
+        loop = clm.DecodeLoop(**lp)
+
+        def run():
+            loop.launch()
+            for t, t0 in zip((len_before, kv_len, rope_pos), state0):
+                t.copy_(t0)
+        steps_per_run = n_loop
+        for _ in range(max(1, args.warmup // n_loop)):
             run()
         torch.cuda.synchronize()
 
     # whole-step throughput: K steps back to back, no events inside
+    n_runs = max(1, -(-args.steps // steps_per_run))
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(n_runs):
         run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    timed_steps = n_runs * steps_per_run
 
     # per-call durations: the same K steps again with HIP events between the
     # calls, recorded on the stream the kernels run on (torch's current stream)
@@ -386,8 +418,8 @@ def main():
         per += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
     per_us = per / args.steps * 1e3
 
-    ms_per_step = wall / args.steps * 1e3
-    value = c.B * c.Kq / (wall / args.steps)
+    ms_per_step = wall / timed_steps * 1e3
+    value = c.B * c.Kq / (wall / timed_steps)
     attn_s = per_us[1] * 1e-6
     attn_bytes = attention_bytes(c, x.kv_len, fp8=f8 is not None)
     achieved = attn_bytes / attn_s / 1e9
@@ -417,7 +449,7 @@ def main():
         "value": round(value, 1),
         "unit": "stream-steps/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": timed_steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
@@ -430,7 +462,7 @@ def main():
             "streams": c.B, "queries_per_stream": c.Kq, "q_heads": c.H_q, "kv_heads": c.H_kv,
             "head_dim": c.D, "kv_len": "x".join(str(a) for a in c.kv_len_dist), "block_size": c.block_size,
             "d_model": c.d_model, "codebook": c.V, "heads": c.G, "decoding": c.mode,
-            "launch": "hip_graph" if args.graph == "on" else "eager",
+            "launch": f"decode loop: {n_loop} steps per HIP graph" if graph else "eager",
             "head": "linear" if mlp is None else "two-layer d->4096->Mish->V",
             "append": "plain" if rope_pos is None else "rope at logical positions",
             "kv_cache": "bf16" if f8 is None else "e4m3 + fp32 row scales",

@@ -25,7 +25,7 @@ __all__ = [
     "decode_attention_fp8", "decode_attention_workspace_size", "decode_attention_noalloc",
     "codebook_head", "codebook_head_mlp", "codebook_head_workspace_size", "codebook_head_mlp_workspace_size",
     "sample_or_argmax", "spec_verify", "spec_verify_bonus",
-    "Workspace", "set_checked",
+    "Workspace", "set_checked", "advance_lengths", "DecodeLoop", "pick_bucket",
 ]
 
 
@@ -466,3 +466,129 @@ def spec_verify_bonus(target_logits, draft_probs, draft_tokens, u_accept, u_resa
         _ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resample),
         C.c_float(temperature), B, K, V, _ptr(out_tokens), _ptr(num_emitted), _stream()))
     return out_tokens, num_emitted
+
+
+def advance_lengths(len_before, kv_len, T_new, positions=None, num_emitted=None):
+    """Device-side advance of every stream by num_emitted[b] (or T_new):
+    len_before, kv_len [B] int32 and positions [B,T_new] int32, in place."""
+    torch = _torch()
+    lib = load()
+    _cuda("len_before", len_before, torch.int32, 1)
+    B = len_before.shape[0]
+    _out("kv_len", kv_len, (B,), torch.int32)
+    if positions is not None:
+        _out("positions", positions, (B, T_new), torch.int32)
+    if num_emitted is not None:
+        _out("num_emitted", num_emitted, (B,), torch.int32)
+    _check("clm_advance_lengths", lib.clm_advance_lengths(
+        _ptr(len_before), _ptr(kv_len), _ptr(positions), _ptr(num_emitted), B, T_new, _stream()))
+
+
+def pick_bucket(bucket_sizes, B) -> int:
+    """Index of the smallest captured batch size >= B (clm_pick_bucket), or -1."""
+    arr = (C.c_int32 * len(bucket_sizes))(*bucket_sizes)
+    return int(load().clm_pick_bucket(C.cast(arr, C.c_void_p), len(bucket_sizes), int(B)))
+
+
+class DecodeLoop:
+    """n_steps decode steps captured as one HIP graph (clm_decode_loop_*).
+
+    Per-step arrays carry a leading n_steps axis: k_new, v_new [n, B, Kq,
+    H_kv, D]; q, o [n, B, Kq, H_q, D]; logits [n, B*Kq, V]; tokens,
+    temperature, uniforms [n, B*Kq]; draft_probs [n, B, Kq, V]; draft_tokens,
+    u_accept, out_tokens [n, B, Kq]; u_resample, num_emitted [n, B].  The
+    cache, block table, lengths (and positions) are as for the single
+    calls; the lengths and positions advance on the device after each step.
+    mode: "greedy", "sample" or "spec".  Every tensor must stay alive while
+    the loop exists (this object keeps references); launch() enqueues all
+    n_steps steps on torch's current stream."""
+
+    _MODES = {"greedy": 0, "sample": 1, "spec": 2}
+
+    def __init__(self, *, k_cache, v_cache, block_table, len_before, kv_len, max_kv_len, k_new, v_new, q, W, o,
+                 logits, head_id=None, positions=None, rope_base=1.0e6, mode="greedy", tokens=None,
+                 temperature=None, uniforms=None, spec_temperature=0.0, draft_probs=None, draft_tokens=None,
+                 u_accept=None, u_resample=None, out_tokens=None, num_emitted=None, attn_workspace=None,
+                 block_size=16):
+        torch = _torch()
+        self._lib = load()
+        self._h = None
+        n, B, Kq, H_q, D = q.shape
+        dt = q.dtype
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            _cuda(name, t, dt, 5)
+        H_kv = k_new.shape[3]
+        if tuple(k_new.shape) != (n, B, Kq, H_kv, D) or tuple(v_new.shape) != (n, B, Kq, H_kv, D):
+            raise ValueError("DecodeLoop: k_new/v_new shape")
+        _cuda("q", q, dt, 5)
+        _out("o", o, q.shape, dt)
+        nb = k_cache.shape[0]
+        _out("k_cache", k_cache, (nb, H_kv, block_size, D), dt)
+        _out("v_cache", v_cache, (nb, H_kv, D, block_size), dt)
+        _cuda("block_table", block_table, torch.int32, 2)
+        if block_table.shape[0] != B:
+            raise ValueError("DecodeLoop: block_table rows")
+        _out("len_before", len_before, (B,), torch.int32)
+        _out("kv_len", kv_len, (B,), torch.int32)
+        if positions is not None:
+            _out("positions", positions, (B, Kq), torch.int32)
+        Ws = [W[g] for g in range(W.shape[0])] if isinstance(W, torch.Tensor) and W.dim() == 3 else list(W)
+        G = len(Ws)
+        V = Ws[0].shape[0]
+        for i, w in enumerate(Ws):
+            _out(f"W[{i}]", w, (V, H_q * D), dt)
+        M = B * Kq
+        _out("logits", logits, (n, M, V), torch.float32)
+        if head_id is not None:
+            _out("head_id", head_id, (M,), torch.int32)
+        if mode not in self._MODES:
+            raise ValueError(f"DecodeLoop: mode {mode!r}")
+        if mode in ("greedy", "sample"):
+            _out("tokens", tokens, (n, M), torch.int32)
+        if mode == "sample":
+            _out("temperature", temperature, (n, M), torch.float32)
+            _out("uniforms", uniforms, (n, M), torch.float32)
+        if mode == "spec":
+            _out("draft_probs", draft_probs, (n, B, Kq, V), torch.float32)
+            _out("draft_tokens", draft_tokens, (n, B, Kq), torch.int32)
+            _out("u_accept", u_accept, (n, B, Kq), torch.float32)
+            _out("u_resample", u_resample, (n, B), torch.float32)
+            _out("out_tokens", out_tokens, (n, B, Kq), torch.int32)
+            _out("num_emitted", num_emitted, (n, B), torch.int32)
+        if attn_workspace is not None:
+            _cuda("attn_workspace", attn_workspace, torch.uint8, 1)
+        self._warr = (C.c_void_p * G)(*[w.data_ptr() for w in Ws])
+        self._keep = [k_cache, v_cache, block_table, len_before, kv_len, positions, k_new, v_new, q, Ws, head_id,
+                      o, logits, tokens, temperature, uniforms, draft_probs, draft_tokens, u_accept, u_resample,
+                      out_tokens, num_emitted, attn_workspace]
+        p = lambda t: 0 if t is None else t.data_ptr()
+        d = _lib.DecodeStepDesc(
+            B=B, Kq=Kq, H_q=H_q, H_kv=H_kv, D=D, block_size=block_size, num_blocks=nb,
+            max_blocks=block_table.shape[1], max_kv_len=int(max_kv_len), G=G, V=V, dt=_dt(q),
+            k_cache=p(k_cache), v_cache=p(v_cache), block_table=p(block_table), len_before=p(len_before),
+            kv_len=p(kv_len), positions=p(positions), rope_base=float(rope_base), k_new=p(k_new), v_new=p(v_new),
+            q=p(q), W=C.cast(self._warr, C.c_void_p).value, head_id=p(head_id), o=p(o), logits=p(logits),
+            attn_workspace=p(attn_workspace), attn_workspace_bytes=_nbytes(attn_workspace),
+            mode=self._MODES[mode], temperature=p(temperature), uniforms=p(uniforms), tokens=p(tokens),
+            spec_temperature=float(spec_temperature), draft_probs=p(draft_probs), draft_tokens=p(draft_tokens),
+            u_accept=p(u_accept), u_resample=p(u_resample), out_tokens=p(out_tokens), num_emitted=p(num_emitted))
+        h = C.c_void_p()
+        _check("clm_decode_loop_create", self._lib.clm_decode_loop_create(C.byref(d), n, C.byref(h)))
+        self._h = h
+        self.n_steps = n
+
+    def launch(self):
+        if self._h is None:
+            raise RuntimeError("DecodeLoop: closed")
+        _check("clm_decode_loop_launch", self._lib.clm_decode_loop_launch(self._h, _stream()))
+
+    def close(self):
+        if self._h is not None:
+            _check("clm_decode_loop_destroy", self._lib.clm_decode_loop_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -49,6 +49,32 @@ SIGNATURES = {
     "clm_spec_verify_bonus": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _vp, _vp, _vp]),
 }
 
+
+
+class DecodeStepDesc(C.Structure):
+    """clm_decode_step_desc (include/clm.h), field for field."""
+    _fields_ = [
+        ("B", _i), ("Kq", _i), ("H_q", _i), ("H_kv", _i), ("D", _i),
+        ("block_size", _i), ("num_blocks", _i), ("max_blocks", _i), ("max_kv_len", _i),
+        ("G", _i), ("V", _i), ("dt", _i),
+        ("k_cache", _vp), ("v_cache", _vp), ("block_table", _vp), ("len_before", _vp), ("kv_len", _vp),
+        ("positions", _vp), ("rope_base", _f),
+        ("k_new", _vp), ("v_new", _vp), ("q", _vp), ("W", _vp), ("head_id", _vp),
+        ("o", _vp), ("logits", _vp), ("attn_workspace", _vp), ("attn_workspace_bytes", _sz),
+        ("mode", _i), ("temperature", _vp), ("uniforms", _vp), ("tokens", _vp),
+        ("spec_temperature", _f), ("draft_probs", _vp), ("draft_tokens", _vp), ("u_accept", _vp),
+        ("u_resample", _vp), ("out_tokens", _vp), ("num_emitted", _vp),
+    ]
+
+
+SIGNATURES.update({
+    "clm_advance_lengths": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp]),
+    "clm_decode_loop_create": (_i, [C.POINTER(DecodeStepDesc), _i, C.POINTER(_vp)]),
+    "clm_decode_loop_launch": (_i, [_vp, _vp]),
+    "clm_decode_loop_destroy": (_i, [_vp]),
+    "clm_pick_bucket": (_i, [_vp, _i, _i]),
+})
+
 _lib = None
 
 

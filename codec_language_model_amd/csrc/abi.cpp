@@ -50,6 +50,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? CLM_OK : CLM_ERR_HIP; }
 
 }  // namespace
 
+namespace clm {
+bool checked_mode() { return checked(); }
+}  // namespace clm
+
 extern "C" {
 
 const char* clm_status_string(int status) {

@@ -1076,10 +1076,14 @@ bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_l
   // keys best at 128, and 32 streams x 6-query blocks over 300..2000 keys
   // best at 512.  An item then spans at most 64 blocks of 16 tokens (one
   // block id per lane).
+  // The matrix-core kernel stops at 512: its items carry 3..16 query rows,
+  // and 32 streams x 6-query blocks over 300..2000 keys took 39.9 us at 512
+  // against 59.8 us at 1024 (a max_kv_len 4.5% larger tipped the rule over).
   const double est = (double)B * H_kv * (max_kv_len > 1 ? max_kv_len / 2.0 : 1.0);
   const double per = nr > 2 ? 256.0 : 512.0;
+  const long top = nr > 2 ? 512 : 1024;
   long split = 64;
-  while (split < 1024 && (double)(split * 2) * per <= est) split *= 2;
+  while (split < top && (double)(split * 2) * per <= est) split *= 2;
   p->split = (int)split;
   p->max_splits = (int)((max_kv_len + split - 1) / split);
   const size_t slots = (size_t)B * H_kv * p->max_splits * p->nr_tmpl;

@@ -124,6 +124,13 @@ struct VerifyArgs {
 };
 hipError_t launch_spec_verify(const VerifyArgs& a, hipStream_t s);
 
+// Checked mode on (CLM_CHECK / clm_set_checked), for calls that must refuse it.
+bool checked_mode();
+
+// Decode loop: lengths (and positions) += num_emitted[b] (or T_new) per stream.
+hipError_t launch_advance(int32_t* len_before, int32_t* kv_len, int32_t* positions, const int32_t* num_emitted,
+                          int B, int T_new, hipStream_t s);
+
 // Checked mode: validators add the number of bad entries to *bad (device int,
 // zeroed by the caller); check_counter gives the library's static counter on
 // the current device.

@@ -388,6 +388,102 @@ int clm_spec_verify_bonus(const float* target_logits, const float* draft_probs,
                           float temperature, int B, int K, int V, int32_t* out_tokens,
                           int32_t* num_emitted, hipStream_t stream);
 
+
+/* --------------------------------------------------------------------------
+ * Multi-step decode loop as one HIP graph (How We Made a Text-to-Speech Model
+ * Respond in Sub-50 ms, "Exploiting the regular building of the Code
+ * Predictor": the whole frame-generation loop is captured as one graph;
+ * section "Additional serving optimizations": graphs are kept for a set of
+ * batch sizes; Optimizing Streaming Text-to-Speech Models ...,
+ * "Engine-Level Optimizations with TensorRT-LLM": graph execution).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Advance every stream's state by one step on the device:
+ *     add = num_emitted ? num_emitted[b] (clamped to [0, T_new]) : T_new
+ *     len_before[b] += add,  kv_len[b] += add,  positions[b, t] += add (t < T_new)
+ * After speculative verification (num_emitted given) the next block of T_new
+ * queries starts right after the kept tokens, overwriting the rejected
+ * drafts' cache rows.  len_before, kv_len [B] int32 and positions [B, T_new]
+ * int32 (NULL: none) are updated in place; num_emitted [B] int32 or NULL.
+ * Errors: INVALID_ARG (null lengths, B or T_new < 1).
+ */
+int clm_advance_lengths(int32_t* len_before, int32_t* kv_len, int32_t* positions,
+                        const int32_t* num_emitted, int B, int T_new, hipStream_t stream);
+
+/*
+ * One decode step per loop iteration, as the calls above would run it:
+ *   append (rotary at logical positions when positions != NULL) ->
+ *   attention -> head -> token choice (greedy, sampling or speculative
+ *   verification) -> clm_advance_lengths.
+ * Step s (0 <= s < n_steps) reads and writes slice s of each per-step array
+ * (base + s * one step's elements).  All pointers are device memory owned by
+ * the caller and must stay valid while the loop exists; the graph bakes them
+ * in.  Sizes and meanings are those of the individual calls.
+ */
+typedef struct clm_decode_step_desc {
+  int B, Kq, H_q, H_kv, D;          /* Kq queries (= rows appended) per stream and step */
+  int block_size, num_blocks, max_blocks;
+  int max_kv_len;                   /* bound on kv_len over all n_steps steps (split plan) */
+  int G, V;                         /* head: G matrices [V, H_q*D] */
+  clm_dtype dt;
+  void* k_cache;                    /* paged pool, layout of clm_kv_cache_append */
+  void* v_cache;
+  const int32_t* block_table;       /* [B, max_blocks], must map every position the loop writes */
+  int32_t* len_before;              /* [B]  advanced on the device after every step */
+  int32_t* kv_len;                  /* [B]  (= len_before + Kq) advanced likewise */
+  int32_t* positions;               /* [B, Kq] logical positions, or NULL for the plain append */
+  float rope_base;                  /* used when positions != NULL */
+  const void* k_new;                /* [n_steps][B, Kq, H_kv, D] */
+  const void* v_new;                /* [n_steps][B, Kq, H_kv, D] */
+  void* q;                          /* [n_steps][B, Kq, H_q, D] (rotated in place with positions) */
+  const void* const* W;             /* host array of G device pointers, each [V, H_q*D] */
+  const int32_t* head_id;           /* [B*Kq] or NULL when G == 1 */
+  void* o;                          /* [n_steps][B, Kq, H_q, D] attention output (head input) */
+  float* logits;                    /* [n_steps][B*Kq, V] */
+  void* attn_workspace;             /* clm_decode_attention's workspace, or NULL: the library's */
+  size_t attn_workspace_bytes;      /*   static scratch (clm_decode_attention_noalloc) */
+  int mode;                         /* 0 greedy, 1 temperature sampling, 2 speculative verification */
+  const float* temperature;         /* mode 1: [n_steps][B*Kq] */
+  const float* uniforms;            /* mode 1: [n_steps][B*Kq] */
+  int32_t* tokens;                  /* modes 0, 1: [n_steps][B*Kq] */
+  float spec_temperature;           /* mode 2 */
+  const float* draft_probs;         /* mode 2: [n_steps][B, Kq, V] */
+  const int32_t* draft_tokens;      /* mode 2: [n_steps][B, Kq] */
+  const float* u_accept;            /* mode 2: [n_steps][B, Kq] */
+  const float* u_resample;          /* mode 2: [n_steps][B] */
+  int32_t* out_tokens;              /* mode 2: [n_steps][B, Kq] */
+  int32_t* num_emitted;             /* mode 2: [n_steps][B]; the lengths advance by these */
+} clm_decode_step_desc;
+
+typedef struct clm_decode_loop clm_decode_loop;   /* opaque */
+
+/*
+ * Captures n_steps steps described by *desc (1 <= n_steps <= 1024) into one
+ * HIP graph and instantiates it.  Host memory and the graph are allocated
+ * here; no kernel runs.  Every argument is validated as the individual call
+ * would validate it, before or during capture; on an error nothing is kept.
+ * Checked mode must be off (it synchronises): UNSUPPORTED otherwise.
+ * Errors: INVALID_ARG (null desc/loop, n_steps out of range, a null array the
+ *   mode needs, mode not 0..2), the individual calls' errors, HIP.
+ */
+int clm_decode_loop_create(const clm_decode_step_desc* desc, int n_steps, clm_decode_loop** loop);
+
+/* Runs the captured n_steps steps on `stream` (asynchronous).  Each launch
+ * continues from the lengths the previous one left on the device. */
+int clm_decode_loop_launch(clm_decode_loop* loop, hipStream_t stream);
+
+/* Releases the graph (after the launches using it have completed). */
+int clm_decode_loop_destroy(clm_decode_loop* loop);
+
+/*
+ * Host-only helper for a set of captured batch sizes: the index of the
+ * smallest bucket_sizes[i] >= B (the first such on ties), or -1 if none.
+ * A batch of B live streams runs in that bucket's loop with the remaining
+ * slots padded by idle streams.
+ */
+int clm_pick_bucket(const int32_t* bucket_sizes, int n, int B);
+
 #ifdef __cplusplus
 }
 #endif

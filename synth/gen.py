@@ -38,8 +38,11 @@ _STREAMS = {
 BF16_NAN = np.uint16(0x7FC0)
 
 
-def _rng(seed: int, name: str) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _STREAMS[name]])))
+def _rng(seed: int, name: str, step: int = 0) -> np.random.Generator:
+    """The stream for array `name`; steps after the first of a multi-step run
+    draw from streams keyed by the step as well."""
+    key = [seed, _STREAMS[name]] + ([step] if step else [])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(key)))
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -140,6 +143,38 @@ class StepInputs:
                     self.k_new.reshape(cfg.B * Kq, Hk, D), self.v_new.reshape(cfg.B * Kq, Hk, D))
         return k_pool, v_pool
 
+    def pool_with_room(self, extra_tokens: int, idle_streams: int = 0):
+        """The pool before this step's append (as build_pool) and a block table
+        with room for `extra_tokens` more tokens per stream beyond this step's
+        rows: each stream keeps its pages and gets fresh pool blocks after the
+        existing ones.  `idle_streams` padding streams follow the live ones,
+        each with pages of its own for extra_tokens + Kq tokens from position
+        0.  One more fresh block fills the unused table entries (never read).
+        Returns (k_pool, v_pool, block_table, num_blocks)."""
+        cfg = self.cfg
+        bs, Kq = cfg.block_size, cfg.Kq
+        kp, vp = self.build_pool(include_new=False)
+        have = (self.kv_len.astype(np.int64) + bs - 1) // bs
+        need = (self.kv_len.astype(np.int64) + extra_tokens + bs - 1) // bs
+        idle_need = (Kq + extra_tokens + bs - 1) // bs
+        n_new = int(np.maximum(need - have, 0).sum()) + idle_streams * idle_need + 1
+        spare = self.num_blocks + n_new - 1
+        width = int(max(need.max(), idle_need if idle_streams else 1))
+        bt = np.full((cfg.B + idle_streams, width), spare, np.int32)
+        nxt = self.num_blocks
+        for b in range(cfg.B):
+            bt[b, :have[b]] = self.block_table[b, :have[b]]
+            for p in range(int(have[b]), int(need[b])):
+                bt[b, p] = nxt
+                nxt += 1
+        for i in range(idle_streams):
+            bt[cfg.B + i, :idle_need] = np.arange(nxt, nxt + idle_need)
+            nxt += idle_need
+        fill = kp.flat[0]
+        kp = np.concatenate([kp, np.full((n_new,) + kp.shape[1:], fill, kp.dtype)])
+        vp = np.concatenate([vp, np.full((n_new,) + vp.shape[1:], fill, vp.dtype)])
+        return kp, vp, bt, self.num_blocks + n_new
+
     # ---- further draws (each from its own stream) -------------------------------
     def h_iso(self) -> np.ndarray:
         """Head input for isolated head checks, [M, d] ~ N(0, 1)."""
@@ -157,29 +192,47 @@ class StepInputs:
         x = _rng(cfg.seed, "logits_iso").standard_normal((cfg.M, cfg.V), dtype=np.float32)
         return x * np.float32(0.9 * scale)
 
-    def spec_inputs(self):
+    def step_arrays(self, step: int):
+        """(k_new, v_new, q) of decode step `step` of a multi-step run: this
+        step's arrays for step 0, fresh draws of the same shapes and
+        distributions for later steps."""
+        if step == 0:
+            return self.k_new, self.v_new, self.q
+        cfg = self.cfg
+        Kq, Hk, Hq, D = cfg.Kq, cfg.H_kv, cfg.H_q, cfg.D
+        k = _normal(_rng(cfg.seed, "k_new", step), (cfg.B, Kq, Hk, D), cfg.qkv_std, cfg.dtype)
+        v = _normal(_rng(cfg.seed, "v_new", step), (cfg.B, Kq, Hk, D), cfg.qkv_std, cfg.dtype)
+        q = _normal(_rng(cfg.seed, "q", step), (cfg.B, Kq, Hq, D), cfg.qkv_std, cfg.dtype)
+        return k, v, q
+
+    def uniforms_step(self, step: int) -> np.ndarray:
+        """One U[0,1) float32 per head row for step `step` of a multi-step run."""
+        return _rng(self.cfg.seed, "uniforms", step).random(self.cfg.M, dtype=np.float32)
+
+    def spec_inputs(self, step: int = 0):
         """Draft side of speculative verification: draft_probs [B,K,V] f32 (softmax
         of N(0, draft_logit_std) logits), draft_tokens [B,K] drawn from them,
         u_accept [B,K], u_resample [B], isolated target logits [B,K,V], and the
-        same with one more row [B,K+1,V] for the bonus-token variant."""
+        same with one more row [B,K+1,V] for the bonus-token variant.  Later
+        steps of a multi-step run (step > 0) draw from their own streams."""
         cfg = self.cfg
         B, K, V = cfg.B, cfg.Kq, cfg.V
-        z = _rng(cfg.seed, "draft_logits").standard_normal((B, K, V)) * cfg.draft_logit_std
+        z = _rng(cfg.seed, "draft_logits", step).standard_normal((B, K, V)) * cfg.draft_logit_std
         z -= z.max(axis=-1, keepdims=True)
         p = np.exp(z)
         p /= p.sum(axis=-1, keepdims=True)
         draft_probs = p.astype(np.float32)
-        u = _rng(cfg.seed, "draft_tokens").random((B, K))
+        u = _rng(cfg.seed, "draft_tokens", step).random((B, K))
         cdf = np.cumsum(draft_probs.astype(np.float64), axis=-1)
         cdf /= cdf[..., -1:]
         draft_tokens = np.empty((B, K), np.int32)
         for b in range(B):
             for i in range(K):
                 draft_tokens[b, i] = min(int(np.searchsorted(cdf[b, i], u[b, i], side="right")), V - 1)
-        u_accept = _rng(cfg.seed, "u_accept").random((B, K), dtype=np.float32)
-        u_resample = _rng(cfg.seed, "u_resample").random(B, dtype=np.float32)
-        tl = _rng(cfg.seed, "target_logits_iso").standard_normal((B, K, V), dtype=np.float32) * np.float32(0.9)
-        extra = _rng(cfg.seed, "target_logits_bonus_row").standard_normal((B, 1, V), dtype=np.float32) * np.float32(0.9)
+        u_accept = _rng(cfg.seed, "u_accept", step).random((B, K), dtype=np.float32)
+        u_resample = _rng(cfg.seed, "u_resample", step).random(B, dtype=np.float32)
+        tl = _rng(cfg.seed, "target_logits_iso", step).standard_normal((B, K, V), dtype=np.float32) * np.float32(0.9)
+        extra = _rng(cfg.seed, "target_logits_bonus_row", step).standard_normal((B, 1, V), dtype=np.float32) * np.float32(0.9)
         return dict(draft_probs=draft_probs, draft_tokens=draft_tokens, u_accept=u_accept,
                     u_resample=u_resample, target_logits_iso=tl,
                     target_logits_bonus_iso=np.concatenate([tl, extra], axis=1))

@@ -234,3 +234,46 @@ def test_oracle_bf16_rounding_pins():
     y = np.random.default_rng(0).standard_normal(10000).astype(np.float32) * 100
     np.testing.assert_array_equal(oracle.round_to_bf16(y),
                                   torch.from_numpy(y).to(torch.bfloat16).to(torch.float32).numpy())
+
+
+def test_decode_loop_host_checks(lib):
+    """The loop's host-side checks need no GPU: bucket choice, and argument
+    errors of create / launch / destroy / advance before any HIP call."""
+    import ctypes as C
+    from codec_language_model_amd._lib import DecodeStepDesc
+    sizes = (C.c_int32 * 3)(16, 64, 256)
+    pick = lib.clm_pick_bucket
+    ptr = C.cast(sizes, C.c_void_p)
+    assert [pick(ptr, 3, B) for B in (1, 16, 17, 64, 65, 256, 257)] == [0, 0, 1, 1, 2, 2, -1]
+    unsorted = (C.c_int32 * 3)(256, 16, 64)
+    assert pick(C.cast(unsorted, C.c_void_p), 3, 20) == 2
+    assert pick(N, 3, 5) == -1 and pick(ptr, 0, 5) == -1
+    h = C.c_void_p()
+    d = DecodeStepDesc(B=4, Kq=1, H_q=16, H_kv=8, D=128, block_size=16, num_blocks=64, max_blocks=8,
+                       max_kv_len=128, G=1, V=4096, dt=1, k_cache=0x100000, v_cache=0x100000,
+                       block_table=0x100000, len_before=0x100000, kv_len=0x100000, k_new=0x100000,
+                       v_new=0x100000, q=0x100000, W=0x100000, o=0x100000, logits=0x100000, tokens=0x100000,
+                       mode=0)
+    create = lib.clm_decode_loop_create
+    assert create(None, 4, C.byref(h)) == INVALID
+    assert create(C.byref(d), 0, C.byref(h)) == INVALID
+    assert create(C.byref(d), 1025, C.byref(h)) == INVALID
+    d.tokens = 0
+    assert create(C.byref(d), 4, C.byref(h)) == INVALID          # greedy needs tokens
+    d.tokens, d.mode = 0x100000, 1
+    assert create(C.byref(d), 4, C.byref(h)) == INVALID          # sampling needs temperature, uniforms
+    d.mode = 2
+    assert create(C.byref(d), 4, C.byref(h)) == INVALID          # verification needs the draft arrays
+    d.mode = 7
+    assert create(C.byref(d), 4, C.byref(h)) == INVALID
+    d.mode = 0
+    prev = lib.clm_set_checked(1)
+    try:
+        assert create(C.byref(d), 4, C.byref(h)) == UNSUPPORTED  # checked mode synchronises
+    finally:
+        lib.clm_set_checked(prev)
+    assert lib.clm_decode_loop_launch(N, S) == INVALID
+    assert lib.clm_decode_loop_destroy(N) == INVALID
+    assert lib.clm_advance_lengths(N, P, N, N, 4, 1, S) == INVALID
+    assert lib.clm_advance_lengths(P, P, N, N, 0, 1, S) == INVALID
+    assert lib.clm_advance_lengths(P, P, N, N, 4, 0, S) == INVALID

@@ -1,0 +1,222 @@
+"""The multi-step decode loop captured as one HIP graph (clm_decode_loop_*),
+against the oracle run step by step.
+
+Each case runs n_steps steps: every step appends Kq new rows per stream
+(rotary at logical positions in one case), attends, projects and picks tokens
+(greedy, sampling, or speculative verification), then the lengths advance on
+the device - by Kq, or by the number of tokens verification kept.  The oracle
+follows the same trajectory from its own decisions: per step the attention
+outputs, logits and tokens are compared by the parity rules, and at the end
+the lengths and (without rotary) the whole cache bit for bit.  One case runs
+its live streams inside a larger captured batch padded with idle streams, as
+a set of captured batch sizes would; one runs the loop twice from the same
+state and requires identical bits.  A stream whose verification decision was
+exempt (a uniform within 1e-4 of its ratio) leaves the comparison from then
+on, since its trajectory may legitimately differ.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import bf16_tensor_to_f32, check_argmax, check_close, check_sampled, check_verify, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-case] {request.node.nodeid}", file=sys.stderr, flush=True)
+    yield
+
+
+def _pages(n, bs):
+    return (np.asarray(n, np.int64) + bs - 1) // bs
+
+
+def _loop_case(clm_gpu, cfg, B_live, B_cap, n_steps, rope=False, use_ws=True, replay=False):
+    import torch
+    x = synth.make_inputs(cfg, B=B_live)
+    c = x.cfg
+    bf = c.dtype == "bf16"
+    bs, Kq, Hk, Hq, D, V, M_cap = c.block_size, c.Kq, c.H_kv, c.H_q, c.D, c.V, B_cap * c.Kq
+    f32 = x.f32
+    # ---- pool and block table with room for n_steps * Kq more tokens per
+    # stream; idle padding streams get pages of their own
+    kp, vp, bt, nb = x.pool_with_room((n_steps - 1) * Kq, idle_streams=B_cap - B_live)
+    lb0 = np.concatenate([x.len_before, np.zeros(B_cap - B_live, np.int32)]).astype(np.int32)
+    offset = 1000
+    pos0 = (lb0[:, None] + offset + np.arange(Kq)[None, :]).astype(np.int32)
+
+    # ---- per-step inputs [n_steps, B_cap, ...] (padding rows zero)
+    def padded(a, rows=B_cap):
+        out = np.zeros((rows,) + a.shape[1:], a.dtype)
+        out[:a.shape[0]] = a
+        return out
+    steps = [x.step_arrays(s) for s in range(n_steps)]
+    k_new = np.stack([padded(k) for k, _, _ in steps])
+    v_new = np.stack([padded(v) for _, v, _ in steps])
+    q_all = np.stack([padded(q) for _, _, q in steps])
+    head_id = np.concatenate([x.head_id, np.zeros(M_cap - c.M, np.int32)]) if c.G > 1 else None
+    dev = torch.device("cuda")
+    T = lambda a, b16=False: to_torch(np.ascontiguousarray(a), bf16=b16)
+    k_cache, v_cache = T(kp, bf), T(vp, bf)
+    g = dict(k_cache=k_cache, v_cache=v_cache, block_table=T(bt), len_before=T(lb0), kv_len=T(lb0 + Kq),
+             k_new=T(k_new, bf), v_new=T(v_new, bf), q=T(q_all, bf), W=T(x.W, bf),
+             head_id=None if head_id is None else T(head_id))
+    g["o"] = torch.empty_like(g["q"])
+    g["logits"] = torch.empty((n_steps, M_cap, V), dtype=torch.float32, device=dev)
+    if rope:
+        g["positions"] = T(pos0)
+    spec_np = None
+    if c.mode == "spec":
+        spec_np = [x.spec_inputs(s) for s in range(n_steps)]
+        g["draft_probs"] = T(np.stack([padded(sp["draft_probs"]) for sp in spec_np]))
+        g["draft_tokens"] = T(np.stack([padded(sp["draft_tokens"]) for sp in spec_np]))
+        g["u_accept"] = T(np.stack([padded(sp["u_accept"]) for sp in spec_np]))
+        g["u_resample"] = T(np.stack([padded(sp["u_resample"]) for sp in spec_np]))
+        g["out_tokens"] = torch.empty((n_steps, B_cap, Kq), dtype=torch.int32, device=dev)
+        g["num_emitted"] = torch.empty((n_steps, B_cap), dtype=torch.int32, device=dev)
+    else:
+        g["tokens"] = torch.empty((n_steps, M_cap), dtype=torch.int32, device=dev)
+    temp_np = uni_np = None
+    if c.mode == "sample":
+        temp_np = np.full((n_steps, M_cap), c.temperature, np.float32)
+        temp_np[:, c.M:] = 0.0
+        uni_np = np.stack([padded(x.uniforms_step(s), M_cap) for s in range(n_steps)])
+        g["temperature"], g["uniforms"] = T(temp_np), T(uni_np)
+    max_kv = int((lb0 + n_steps * Kq).max())
+    ws = None
+    if use_ws:
+        need_ws = clm_gpu.decode_attention_workspace_size(B_cap, Kq, Hq, Hk, D, max_kv)
+        ws = torch.empty(need_ws + 256, dtype=torch.uint8, device=dev)
+        ws = ws[(-ws.data_ptr()) % 256:]
+    initial = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in g.items()}
+    loop = clm_gpu.DecodeLoop(max_kv_len=max_kv, mode=c.mode, spec_temperature=c.temperature,
+                              attn_workspace=ws, block_size=bs, rope_base=1.0e6, **g)
+    loop.launch()
+    torch.cuda.synchronize()
+
+    # ---- the oracle, step by step from its own decisions
+    scale = 1.0 / math.sqrt(D)
+    keys = [x.logical_k(b)[:x.len_before[b]] for b in range(B_live)]
+    vals = [x.logical_v(b)[:x.len_before[b]] for b in range(B_live)]
+    lb = x.len_before.astype(np.int64).copy()
+    live = np.ones(B_live, bool)
+    kp_ref, vp_ref = kp.copy(), vp.copy()
+    Wf = f32(x.W)
+    for s in range(n_steps):
+        kn, vn, qs = steps[s]
+        kf, vf, qf = f32(kn), f32(vn), f32(qs)
+        if rope:
+            pos = (lb[:, None] + offset + np.arange(Kq)[None, :])
+            qf = oracle.rope(qf, pos[:, :, None], 1.0e6)
+            kf = oracle.rope(kf, pos[:, :, None], 1.0e6)
+            if bf:          # the cache and the rotated queries hold the step's element type
+                qf, kf = oracle.round_to_bf16(qf), oracle.round_to_bf16(kf)
+            qf, kf = qf.astype(np.float32), kf.astype(np.float32)
+        ks = [np.concatenate([keys[b], kf[b]]) for b in range(B_live)]
+        vs = [np.concatenate([vals[b], vf[b]]) for b in range(B_live)]
+        kv_len = (lb + Kq).astype(np.int32)
+        sp = spec_np[s] if spec_np else None
+        ref = oracle.decode_step(qf, ks, vs, kv_len, scale, Hk, Wf, x.head_id if c.G > 1 else None, bf,
+                                 mode=c.mode,
+                                 temperature=(c.temperature if c.mode == "spec" else
+                                              (temp_np[s, :c.M] if temp_np is not None else None)),
+                                 uniforms=None if uni_np is None else uni_np[s, :c.M], spec=sp)
+        sel = np.nonzero(live)[0]
+        rows = (sel[:, None] * Kq + np.arange(Kq)[None, :]).reshape(-1)
+        o_g = bf16_tensor_to_f32(g["o"][s])[:B_live]
+        lg_g = g["logits"][s].cpu().numpy()[:c.M]
+        check_close(o_g[sel], ref["o"][sel], f"loop c{cfg} step {s} attention")
+        check_close(lg_g[rows], ref["logits"][rows], f"loop c{cfg} step {s} logits")
+        if c.mode == "spec":
+            ot = g["out_tokens"][s].cpu().numpy()[:B_live]
+            ne = g["num_emitted"][s].cpu().numpy()[:B_live]
+            rl = ref["logits"].reshape(B_live, Kq, V)
+            check_verify(ot[sel], ne[sel], rl[sel], sp["draft_probs"][sel], sp["draft_tokens"][sel],
+                         sp["u_accept"][sel], sp["u_resample"][sel], c.temperature, f"loop c{cfg} step {s} verify")
+            add = ref["num_emitted"].astype(np.int64)
+            for b in sel:
+                if ne[b] != add[b] or not np.array_equal(ot[b], ref["out_tokens"][b]):
+                    live[b] = False             # exempt decision: trajectories may part here
+        else:
+            tk = g["tokens"][s].cpu().numpy()[:c.M]
+            if c.mode == "sample":
+                check_sampled(tk[rows], ref["logits"][rows], temp_np[s, rows], uni_np[s, rows],
+                              f"loop c{cfg} step {s} sample")
+            else:
+                check_argmax(tk[rows], ref["logits"][rows], f"loop c{cfg} step {s} argmax")
+            add = np.full(B_live, Kq, np.int64)
+        # the oracle's append of this step's rows (plain-append cases), then advance
+        if not rope:
+            kp_ref, vp_ref = oracle.kv_cache_append(kp_ref, vp_ref, bt[:B_live], lb.astype(np.int32),
+                                                    kn, vn, bs)
+        for b in range(B_live):
+            keys[b] = ks[b][:lb[b] + add[b]]
+            vals[b] = vs[b][:lb[b] + add[b]]
+        lb = lb + add
+    lb_g = g["len_before"].cpu().numpy()
+    kvl_g = g["kv_len"].cpu().numpy()
+    assert np.array_equal(lb_g[:B_live][live], lb[live]), "lengths after the loop"
+    assert np.array_equal(kvl_g[:B_live][live], (lb + Kq)[live])
+    idle_adv = (g["num_emitted"].cpu().numpy()[:, B_live:].sum(0) if c.mode == "spec"
+                else np.full(B_cap - B_live, n_steps * Kq))
+    assert np.array_equal(lb_g[B_live:], idle_adv), "idle streams advance too"
+    if rope:
+        assert np.array_equal(g["positions"].cpu().numpy()[:B_live][live],
+                              (lb[:, None] + offset + np.arange(Kq)[None, :])[live])
+    elif live.all():
+        dt_ = np.int16 if bf else np.uint32
+        kb = k_cache.view(torch.int16).cpu().numpy() if bf else k_cache.cpu().numpy().view(np.uint32)
+        vb = v_cache.view(torch.int16).cpu().numpy() if bf else v_cache.cpu().numpy().view(np.uint32)
+        live_blocks = np.unique(bt[:B_live])
+        np.testing.assert_array_equal(kb[live_blocks], kp_ref.view(dt_)[live_blocks], err_msg="cache keys")
+        np.testing.assert_array_equal(vb[live_blocks], vp_ref.view(dt_)[live_blocks], err_msg="cache values")
+    if replay:
+        first = {k: g[k].clone() for k in ("o", "logits", "tokens", "len_before", "k_cache") if k in g}
+        for k, v in initial.items():
+            if isinstance(v, torch.Tensor) and k not in ("W",):
+                g[k].copy_(v)
+        torch.cuda.synchronize()
+        loop.launch()
+        torch.cuda.synchronize()
+        for k, v in first.items():
+            a, b_ = g[k], v
+            if a.dtype == torch.bfloat16:          # bits, so that NaN in empty slots compares equal
+                a, b_ = a.view(torch.int16), b_.view(torch.int16)
+            elif a.dtype == torch.float32:
+                a, b_ = a.view(torch.int32), b_.view(torch.int32)
+            assert torch.equal(a, b_), f"second launch differs in {k}"
+    loop.close()
+    print(f"loop c{cfg}: {n_steps} steps, {B_live} live of {B_cap}, {int((~live).sum())} streams parted on exempt "
+          f"decisions")
+
+
+def test_loop_greedy_rope_replay(clm_gpu):
+    """256-stream mix (24 streams), 4 steps with rotary at logical positions;
+    the loop launched twice from the same state gives the same bits."""
+    _loop_case(clm_gpu, 5, 24, 24, 4, rope=True, replay=True)
+
+
+def test_loop_speculative(clm_gpu):
+    """32 streams x 6-query blocks, 4 steps; lengths advance by the tokens kept."""
+    _loop_case(clm_gpu, 4, 32, 32, 4)
+
+
+def test_loop_sampling_padded_bucket_static_scratch(clm_gpu):
+    """12 live streams in a 16-stream captured batch (4 idle), temperature
+    sampling, attention partials in the library's static scratch."""
+    sizes = [16, 64, 256]
+    assert clm_gpu.pick_bucket(sizes, 12) == 0
+    _loop_case(clm_gpu, 2, 12, sizes[clm_gpu.pick_bucket(sizes, 12)], 3, use_ws=False)
+
+
+def test_loop_grouped_heads_and_fp32(clm_gpu):
+    """Three stage heads (64 streams, 3 steps), and the one-stream fp32 step (5 steps)."""
+    _loop_case(clm_gpu, 3, 64, 64, 3)
+    _loop_case(clm_gpu, 1, 1, 1, 5, replay=True)
