@@ -9,10 +9,11 @@
 // uniform.
 //
 // spec_verify (Optimizing Streaming Text-to-Speech Models ..., "Speculative
-// Decoding for Acoustic Tokens"): one workgroup per stream.  The K target
-// rows' normalisers are computed in parallel (one wave per row), then the
-// drafted positions are walked in order - accept test u < p[x]/q[x] - and on
-// the first rejection an inverse-CDF draw from max(p - q, 0) is made.
+// Decoding for Acoustic Tokens"): one workgroup per (stream, target row)
+// decides that row's draft - accept test u < p[x]/q[x] - and, if it is
+// rejected, draws its residual token from max(p - q, 0); a one-thread-per-
+// stream pass then keeps the drafts before the first rejection and that
+// row's residual token.
 //
 // The inverse CDF is deterministic and exact about where it cuts.  A row is
 // taken in passes of 16384 entries; in a pass each thread holds 16
@@ -30,12 +31,14 @@
 namespace clm {
 namespace {
 
-constexpr int kT = 1024;                // threads per row
-constexpr int kW = kT / 64;             // waves per row
+// A row is handled by one workgroup of NT threads: 1024 for rows longer than
+// 4096 entries, 256 otherwise (fewer idle waves at each barrier).
 constexpr int kCH = 16;                 // consecutive entries per thread per pass
-constexpr int kPass = kT * kCH;         // entries per pass
-constexpr int kMaxPasses = 64;          // V <= 1 << 20
-constexpr int kMaxDraft = 16;
+constexpr int kMaxPasses = 64;          // V <= 1 << 20 at NT = 1024 (one pass at NT = 256)
+template <int NT> struct Blk {
+  static constexpr int W = NT / 64;     // waves per row
+  static constexpr int PASS = NT * kCH; // entries per pass
+};
 
 // exp(x / T - mx / T) as 2^((x - mx) * c), c = log2(e) / T: one subtraction,
 // one multiply and the hardware exp2 (x <= mx, so the argument is <= 0).  c
@@ -45,38 +48,42 @@ __device__ __forceinline__ float softmax_w(float x, float mx, float c) {
   return __builtin_amdgcn_exp2f((x - mx) * c);
 }
 
+template <int NT>
 struct Scratch {
-  float wf[kW];
-  int wi[kW];
+  float wf[Blk<NT>::W];
+  int wi[Blk<NT>::W];
   float ptot[kMaxPasses];
   int pick, psel;
   float target, total;
 };
 
-__device__ __forceinline__ float block_max(float x, Scratch& sc) {
+template <int NT>
+__device__ __forceinline__ float block_max(float x, Scratch<NT>& sc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   x = wave_max(x);
   __syncthreads();                      // earlier readers of sc.wf are done
   if (lane == 0) sc.wf[w] = x;
   __syncthreads();
   float r = sc.wf[0];
-  for (int i = 1; i < kW; ++i) r = fmaxf(r, sc.wf[i]);
+  for (int i = 1; i < Blk<NT>::W; ++i) r = fmaxf(r, sc.wf[i]);
   return r;
 }
 
-__device__ __forceinline__ int block_max_int(int x, Scratch& sc) {
+template <int NT>
+__device__ __forceinline__ int block_max_int(int x, Scratch<NT>& sc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   x = wave_max_i(x);
   __syncthreads();
   if (lane == 0) sc.wi[w] = x;
   __syncthreads();
   int r = sc.wi[0];
-  for (int i = 1; i < kW; ++i) r = max(r, sc.wi[i]);
+  for (int i = 1; i < Blk<NT>::W; ++i) r = max(r, sc.wi[i]);
   return r;
 }
 
 // (value, index) maximum with ties to the lower index.
-__device__ __forceinline__ int block_argmax_pair(float bv, int bi, Scratch& sc) {
+template <int NT>
+__device__ __forceinline__ int block_argmax_pair(float bv, int bi, Scratch<NT>& sc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   wave_argmax(bv, bi);
   __syncthreads();
@@ -84,7 +91,7 @@ __device__ __forceinline__ int block_argmax_pair(float bv, int bi, Scratch& sc) 
   __syncthreads();
   bv = sc.wf[0];
   bi = sc.wi[0];
-  for (int i = 1; i < kW; ++i)
+  for (int i = 1; i < Blk<NT>::W; ++i)
     if (sc.wf[i] > bv || (sc.wf[i] == bv && sc.wi[i] < bi)) { bv = sc.wf[i]; bi = sc.wi[i]; }
   return bi;
 }
@@ -93,7 +100,8 @@ __device__ __forceinline__ int block_argmax_pair(float bv, int bi, Scratch& sc) 
 // [start, end) of the running total, and the total.  Lane l's start is
 // computed as the same expression as lane l-1's end (and a wave's base as
 // the previous wave's last end), so consecutive intervals share their bound.
-__device__ __forceinline__ void block_scan(float s, float& start, float& end, float& tot, Scratch& sc) {
+template <int NT>
+__device__ __forceinline__ void block_scan(float s, float& start, float& end, float& tot, Scratch<NT>& sc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float incl = wave_incl_scan(s, lane);
   float prev = __shfl_up(incl, 1, 64);
@@ -102,7 +110,7 @@ __device__ __forceinline__ void block_scan(float s, float& start, float& end, fl
   if (lane == 63) sc.wf[w] = incl;
   __syncthreads();
   float base = 0.f, bw = 0.f;
-  for (int i = 0; i < kW; ++i) {
+  for (int i = 0; i < Blk<NT>::W; ++i) {
     if (i == w) bw = base;
     base += sc.wf[i];
   }
@@ -128,10 +136,11 @@ __device__ __forceinline__ void load16(const float* __restrict__ x, int i0, int 
 }
 
 // Lowest index of the largest value among x[0:n].
-__device__ int row_argmax(const float* __restrict__ x, int n, Scratch& sc) {
+template <int NT>
+__device__ int row_argmax(const float* __restrict__ x, int n, Scratch<NT>& sc) {
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i0 = threadIdx.x * kCH; i0 < n; i0 += kPass) {
+  for (int i0 = threadIdx.x * kCH; i0 < n; i0 += Blk<NT>::PASS) {
     float v[kCH];
     load16(x, i0, n, v, -INFINITY);
 #pragma unroll
@@ -146,10 +155,12 @@ __device__ int row_argmax(const float* __restrict__ x, int n, Scratch& sc) {
 // w >= 0, which wf(i0, e) gives for the 16 entries from i0 (0 past n); the
 // last index with w_i > 0 if rounding leaves none; -1 if all are zero.  When
 // the row fits one pass, `have` says e already holds this thread's weights.
-template <class WF>
-__device__ int block_draw(int n, float u, const WF& wf, float (&e)[kCH], bool have, Scratch& sc) {
+template <int NT, class WF>
+__device__ int block_draw(int n, float u, const WF& wf, float (&e)[kCH], bool have, Scratch<NT>& sc) {
+  constexpr int kPass = Blk<NT>::PASS;
   const int tid = threadIdx.x;
   const int npass = (n + kPass - 1) / kPass;
+  float start1 = 0.f, end1 = 0.f, s1 = 0.f;   // a one-pass row keeps its interval
   for (int p = 0; p < npass; ++p) {
     if (!(have && npass == 1)) wf(p * kPass + tid * kCH, e);
     float s = 0.f;
@@ -158,6 +169,7 @@ __device__ int block_draw(int n, float u, const WF& wf, float (&e)[kCH], bool ha
     float start, end, tot;
     block_scan(s, start, end, tot, sc);
     if (tid == 0) sc.ptot[p] = tot;
+    start1 = start; end1 = end; s1 = s;
   }
   __syncthreads();
   if (tid == 0) {
@@ -181,12 +193,15 @@ __device__ int block_draw(int n, float u, const WF& wf, float (&e)[kCH], bool ha
   const int psel = sc.psel;
   if (psel >= 0) {
     const int i0 = psel * kPass + tid * kCH;
-    if (npass > 1) wf(i0, e);
-    float s = 0.f;
+    float s = s1, start = start1, end = end1;
+    if (npass > 1) {
+      wf(i0, e);
+      s = 0.f;
 #pragma unroll
-    for (int k = 0; k < kCH; ++k) s += e[k];
-    float start, end, tot;
-    block_scan(s, start, end, tot, sc);      // the same numbers as in the totals pass
+      for (int k = 0; k < kCH; ++k) s += e[k];
+      float tot;
+      block_scan(s, start, end, tot, sc);      // the same numbers as in the totals pass
+    }
     const float tgt = sc.target;
     if (s > 0.f && start <= tgt && tgt < end) {
       float run = start;
@@ -216,8 +231,10 @@ __device__ int block_draw(int n, float u, const WF& wf, float (&e)[kCH], bool ha
   return block_max_int(last, sc);
 }
 
-__global__ __launch_bounds__(kT) void sample_kernel(SampleArgs P) {
-  __shared__ Scratch sc;
+template <int NT>
+__global__ __launch_bounds__(NT) void sample_kernel(SampleArgs P) {
+  constexpr int kPass = Blk<NT>::PASS;
+  __shared__ Scratch<NT> sc;
   const int r = blockIdx.x;
   const float* __restrict__ x = P.logits + (size_t)r * P.ld;
   const int n = P.vocab_valid ? clampi(P.vocab_valid[r], 1, P.V) : P.V;
@@ -255,186 +272,174 @@ __global__ __launch_bounds__(kT) void sample_kernel(SampleArgs P) {
   if (threadIdx.x == 0) P.tokens[r] = tok;
 }
 
-// Statistics of one row, by one wave: max of x[0:n] and, when T > 0, the
-// softmax normaliser sum_j exp(x_j / T - max / T); the lowest index of the
-// max as well.  float4 reads when the row is 16-byte aligned.
-struct RowStat { float m, sum; int amax; };
-
-__device__ RowStat wave_row_stat(const float* __restrict__ x, int n, float T) {
-  constexpr int U = 8;                       // float4 loads in flight per lane
-  const int lane = threadIdx.x & 63;
-  const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-  const int n4 = vec ? (n >> 2) : 0;
-  const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x);
-  const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int j0 = 0; j0 < n4; j0 += 64 * U) {
-    float4 v[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int j = j0 + 64 * k + lane;
-      v[k] = j < n4 ? x4[j] : ninf;
-    }
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int i = 4 * (j0 + 64 * k + lane);
-      if (v[k].x > bv) { bv = v[k].x; bi = i; }
-      if (v[k].y > bv) { bv = v[k].y; bi = i + 1; }
-      if (v[k].z > bv) { bv = v[k].z; bi = i + 2; }
-      if (v[k].w > bv) { bv = v[k].w; bi = i + 3; }
-    }
-  }
-  for (int i = 4 * n4 + lane; i < n; i += 64)
-    if (x[i] > bv) { bv = x[i]; bi = i; }
-  wave_argmax(bv, bi);
-  RowStat r{bv, 0.f, bi == 0x7fffffff ? 0 : bi};
-  if (T > 0.f) {
-    const float c = softmax_c(T);
-    float sum = 0.f;
-    for (int j0 = 0; j0 < n4; j0 += 64 * U) {
-      float4 v[U];
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int j = j0 + 64 * k + lane;
-        v[k] = j < n4 ? x4[j] : ninf;
-      }
-#pragma unroll
-      for (int k = 0; k < U; ++k)
-        sum += softmax_w(v[k].x, bv, c) + softmax_w(v[k].y, bv, c) + softmax_w(v[k].z, bv, c) +
-               softmax_w(v[k].w, bv, c);
-    }
-    for (int i = 4 * n4 + lane; i < n; i += 64) sum += softmax_w(x[i], bv, c);
-    r.sum = wave_sum(sum);
-  }
+// Sum over the block, combined in a fixed order (waves in index order).
+template <int NT>
+__device__ __forceinline__ float block_sum(float x, Scratch<NT>& sc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  x = wave_sum(x);
+  __syncthreads();
+  if (lane == 0) sc.wf[w] = x;
+  __syncthreads();
+  float r = sc.wf[0];
+  for (int i = 1; i < Blk<NT>::W; ++i) r += sc.wf[i];
   return r;
 }
 
-// One workgroup per stream.  (1) The K target rows' statistics in parallel,
-// one wave per row, while the drafted token of each row is looked up.  (2)
-// The accept chain, which needs only p[x] = exp(x[x]/T - m)/S for the
-// drafted token of each row, walked in order by one lane.  (3) On the first
-// rejection, the residual draw over that one row; with the bonus variant,
-// when every draft is accepted, a draw from the target row after them.
-__global__ __launch_bounds__(kT) void verify_kernel(VerifyArgs P) {
-  __shared__ Scratch sc;
-  __shared__ float s_m[kMaxDraft], s_sum[kMaxDraft];
-  __shared__ int s_amax[kMaxDraft];
-  __shared__ int s_first_reject, s_emitted;
-  __shared__ int s_xt[kMaxDraft];
-  __shared__ float s_qx[kMaxDraft], s_xx[kMaxDraft], s_ua[kMaxDraft];
-  const int b = blockIdx.x;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float T = P.temperature;
+// Speculative verification, phase 1: one workgroup per (stream, target row),
+// so a batch of B streams x K drafts spreads over B*K workgroups instead of
+// B.  Row i < K decides its own draft: accept iff q[x] > 0 and
+// u_accept < p[x] / q[x] (T = 0: iff x is the row's argmax); a rejected row
+// also draws its residual token from max(p - q, 0) (from p if that is all
+// zero) at u_resample, and the bonus row (i = K) draws from p.  The row's
+// outcome goes into its own out_tokens slot: the drafted token (>= 0) if
+// accepted, else -(token + 2), so phase 2 needs no other memory.
+template <int NT>
+__global__ __launch_bounds__(NT) void verify_rows_kernel(VerifyArgs P) {
+  constexpr int kPass = Blk<NT>::PASS;
+  __shared__ Scratch<NT> sc;
+  __shared__ float s_px;
   const int V = P.V, K = P.K;
-  const int TK = K + P.bonus;            // target rows (and output rows) per stream
-
-  auto lookup = [&]() {                  // the drafted token of each row and its numbers
-    const size_t row = (size_t)b * K + lane;
-    const int xt = clampi(P.draft_tokens[row], 0, V - 1);
-    s_xt[lane] = xt;
-    s_qx[lane] = P.draft_probs[row * V + xt];
-    s_xx[lane] = P.target_logits[((size_t)b * TK + lane) * V + xt];
-    s_ua[lane] = P.u_accept[row];
-  };
-  if (w < TK) {
-    const RowStat st = wave_row_stat(P.target_logits + ((size_t)b * TK + w) * V, V, T);
-    if (lane == 0) { s_m[w] = st.m; s_sum[w] = st.sum; s_amax[w] = st.amax; }
-  } else if (w == kW - 1 && lane < K) {
-    lookup();
-  }
-  if (TK >= kW && w == 0 && lane < K) lookup();   // every wave held a row: wave 0 looks up after
-  __syncthreads();
-
-  if (threadIdx.x == 0) {
-    int rej = -1;
-    for (int i = 0; i < K; ++i) {
-      const int xt = s_xt[i];
-      const float qx = s_qx[i];
-      bool accept;
-      if (T > 0.f) {
-        const float px = softmax_w(s_xx[i], s_m[i], softmax_c(T)) / s_sum[i];
-        accept = qx > 0.f && s_ua[i] < px / qx;
-      } else {
-        accept = qx > 0.f && xt == s_amax[i];
-      }
-      if (!accept) { rej = i; break; }
-      P.out_tokens[(size_t)b * TK + i] = xt;
-    }
-    s_first_reject = rej;
-    s_emitted = rej < 0 ? TK : rej + 1;
-  }
-  __syncthreads();
-  const int rej = s_first_reject, emitted = s_emitted;
-
-  if (rej >= 0) {
-    const size_t row = (size_t)b * K + rej;            // draft row
-    const size_t trow = (size_t)b * TK + rej;          // target row
-    int tok;
-    if (T > 0.f) {
-      const float* __restrict__ x = P.target_logits + trow * V;
-      const float* __restrict__ q = P.draft_probs + row * V;
-      const float mx = s_m[rej], c = softmax_c(T), inv_s = 1.f / s_sum[rej];
-      const float ur = P.u_resample[b];
-      float e[kCH];
-      auto resid = [&](int i0, float (&wgt)[kCH]) {
-        float y[kCH], z[kCH];
-        load16(x, i0, V, y, 0.f);
-        load16(q, i0, V, z, 0.f);
+  const int TK = K + P.bonus;
+  const int b = blockIdx.x / TK, i = blockIdx.x - b * TK;
+  const float T = P.temperature;
+  const float* __restrict__ x = P.target_logits + ((size_t)b * TK + i) * V;
+  const bool draft_row = i < K;
+  const size_t drow = (size_t)b * K + (draft_row ? i : 0);
+  const float* __restrict__ q = P.draft_probs + drow * V;
+  // every load the row needs is issued up front: the drafted token and its
+  // draft probability, the uniforms, the row itself and (one-pass rows) the
+  // draft row, so the row costs one round trip to memory
+  const int xt = draft_row ? clampi(P.draft_tokens[drow], 0, V - 1) : 0;
+  const float qx = draft_row ? q[xt] : 0.f;
+  const float ua = draft_row ? P.u_accept[drow] : 0.f;
+  const float ur = P.u_resample[b];
+  int result;
+  if (!(T > 0.f)) {
+    const int amax = row_argmax(x, V, sc);
+    result = (draft_row && qx > 0.f && xt == amax) ? xt : -(amax + 2);
+  } else {
+    const bool one = V <= kPass;
+    const int t0 = threadIdx.x * kCH;
+    float v[kCH], qv[kCH], e[kCH];
+    float xx = 0.f;
+    if (draft_row && threadIdx.x == 0) xx = x[xt];
+    float mx = -INFINITY;
+    if (one) {
+      load16(x, t0, V, v, -INFINITY);
+      if (draft_row) load16(q, t0, V, qv, 0.f);
 #pragma unroll
-        for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? fmaxf(softmax_w(y[k], mx, c) * inv_s - z[k], 0.f) : 0.f;
-      };
-      tok = block_draw(V, ur, resid, e, false, sc);
-      if (tok < 0) {
-        auto target = [&](int i0, float (&wgt)[kCH]) {
-          float y[kCH];
-          load16(x, i0, V, y, 0.f);
-#pragma unroll
-          for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? softmax_w(y[k], mx, c) * inv_s : 0.f;
-        };
-        tok = block_draw(V, ur, target, e, false, sc);
-      }
-      if (tok < 0) tok = 0;
+      for (int k = 0; k < kCH; ++k) mx = fmaxf(mx, v[k]);
     } else {
-      // the residual max(onehot(amax) - q, 0) is positive only at amax (or
-      // zero everywhere, then the draw is from the one-hot target): amax
-      tok = s_amax[rej];
+      for (int i0 = t0; i0 < V; i0 += kPass) {
+        float y[kCH];
+        load16(x, i0, V, y, -INFINITY);
+#pragma unroll
+        for (int k = 0; k < kCH; ++k) mx = fmaxf(mx, y[k]);
+      }
     }
-    if (threadIdx.x == 0) P.out_tokens[trow] = tok;
-  } else if (P.bonus) {
-    // every draft accepted: one more token from the target row after them
-    const size_t trow = (size_t)b * TK + K;
-    int tok;
-    if (T > 0.f) {
-      const float* __restrict__ x = P.target_logits + trow * V;
-      const float mx = s_m[K], c = softmax_c(T), inv_s = 1.f / s_sum[K];
-      float e[kCH];
+    mx = block_max(mx, sc);
+    const float c = softmax_c(T);
+    float part = 0.f;
+    if (one) {
+#pragma unroll
+      for (int k = 0; k < kCH; ++k) part += t0 + k < V ? softmax_w(v[k], mx, c) : 0.f;
+    } else {
+      for (int i0 = t0; i0 < V; i0 += kPass) {
+        float y[kCH];
+        load16(x, i0, V, y, -INFINITY);
+#pragma unroll
+        for (int k = 0; k < kCH; ++k) part += i0 + k < V ? softmax_w(y[k], mx, c) : 0.f;
+      }
+    }
+    const float S = block_sum(part, sc);
+    const float inv_s = 1.f / S;
+    bool accept = false;
+    if (draft_row) {
+      if (threadIdx.x == 0) s_px = softmax_w(xx, mx, c) / S;
+      __syncthreads();
+      accept = qx > 0.f && ua < s_px / qx;
+    }
+    if (accept) {
+      result = xt;
+    } else {
+      // target weights p = e / S; residual weights max(p - q, 0)
       auto target = [&](int i0, float (&wgt)[kCH]) {
         float y[kCH];
         load16(x, i0, V, y, 0.f);
 #pragma unroll
         for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? softmax_w(y[k], mx, c) * inv_s : 0.f;
       };
-      tok = block_draw(V, P.u_resample[b], target, e, false, sc);
-      if (tok < 0) tok = 0;
-    } else {
-      tok = s_amax[K];
+      auto resid = [&](int i0, float (&wgt)[kCH]) {
+        float y[kCH], z[kCH];
+        load16(x, i0, V, y, 0.f);
+        load16(q, i0, V, z, 0.f);
+#pragma unroll
+        for (int k = 0; k < kCH; ++k)
+          wgt[k] = i0 + k < V ? fmaxf(softmax_w(y[k], mx, c) * inv_s - z[k], 0.f) : 0.f;
+      };
+      int tok = -1;
+      if (draft_row) {
+        if (one) {
+#pragma unroll
+          for (int k = 0; k < kCH; ++k)
+            e[k] = t0 + k < V ? fmaxf(softmax_w(v[k], mx, c) * inv_s - qv[k], 0.f) : 0.f;
+        }
+        tok = block_draw(V, ur, resid, e, one, sc);
+      }
+      if (tok < 0) {
+        if (one) {
+#pragma unroll
+          for (int k = 0; k < kCH; ++k) e[k] = t0 + k < V ? softmax_w(v[k], mx, c) * inv_s : 0.f;
+        }
+        tok = block_draw(V, ur, target, e, one, sc);
+      }
+      result = -((tok < 0 ? 0 : tok) + 2);
     }
-    if (threadIdx.x == 0) P.out_tokens[trow] = tok;
   }
-  for (int i = emitted + threadIdx.x; i < TK; i += kT) P.out_tokens[(size_t)b * TK + i] = -1;
-  if (threadIdx.x == 0) P.num_emitted[b] = emitted;
+  if (threadIdx.x == 0) P.out_tokens[(size_t)b * TK + i] = result;
+}
+
+// Phase 2: one thread per stream walks its rows in order: the first row with
+// a negative slot was rejected (its residual token is decoded in place) and
+// ends the stream; all K accepted emits K tokens, plus the decoded bonus
+// draw with the bonus variant.  Later slots are padded with -1.
+__global__ __launch_bounds__(256) void verify_chain_kernel(VerifyArgs P) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= P.B) return;
+  const int K = P.K, TK = K + P.bonus;
+  int32_t* out = P.out_tokens + (size_t)b * TK;
+  int emitted = K;
+  for (int i = 0; i < K; ++i) {
+    const int v = out[i];
+    if (v < 0) {
+      out[i] = -v - 2;
+      emitted = i + 1;
+      break;
+    }
+  }
+  if (emitted == K && P.bonus) {
+    out[K] = -out[K] - 2;
+    emitted = K + 1;
+  }
+  for (int i = emitted; i < TK; ++i) out[i] = -1;
+  P.num_emitted[b] = emitted;
 }
 
 }  // namespace
 
 hipError_t launch_sample_or_argmax(const SampleArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(sample_kernel, dim3(a.M), dim3(kT), 0, s, a);
+  if (a.V <= Blk<256>::PASS) hipLaunchKernelGGL(sample_kernel<256>, dim3(a.M), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(sample_kernel<1024>, dim3(a.M), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_spec_verify(const VerifyArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(verify_kernel, dim3(a.B), dim3(kT), 0, s, a);
+  const dim3 rows((unsigned)a.B * (unsigned)(a.K + a.bonus));
+  if (a.V <= Blk<256>::PASS) hipLaunchKernelGGL(verify_rows_kernel<256>, rows, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(verify_rows_kernel<1024>, rows, dim3(1024), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_chain_kernel, dim3((a.B + 255) / 256), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
