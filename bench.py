@@ -76,6 +76,13 @@ def parse():
                     help="steps per captured decode loop with --graph on")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
+    ap.add_argument("--measuring-stick", action="store_true",
+                    help="no decode step: time hipBLASLt (torch.mm, bf16) on a large square GEMM and on the "
+                         "codebook head's shapes, weights rotated over replicas, as the box's practical "
+                         "matrix-core ceiling")
+    ap.add_argument("--pmc-table", metavar="COUNTER_CSV",
+                    help="no GPU work: per-kernel averages of every counter in a rocprofv3 "
+                         "counter_collection.csv")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-calibration run into the attention traffic record")
@@ -160,6 +167,63 @@ def pmc_summary(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
     print("\n".join(lines))
 
 
+def pmc_table(path):
+    """Per-kernel averages of each counter of a rocprofv3 counter CSV, plus the
+    matrix-core figures derived from them where the counters are present:
+    bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, rocprofv3's own
+    MfmaFlopsBF16 expression) and MFMA busy share (SQ_VALU_MFMA_BUSY_CYCLES over
+    GRBM_GUI_ACTIVE x 1024 SIMDs, its MfmaUtil expression)."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        vals[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    kernels = sorted({k for k, _ in vals})
+    for k in kernels:
+        row = {c: sum(v) / len(v) for (kk, c), v in vals.items() if kk == k}
+        n = max(len(v) for (kk, _), v in vals.items() if kk == k)
+        short = re.sub(r"\(.*", "", k.replace("clm::(anonymous namespace)::", ""))[:80]
+        parts = [f"{c} {row[c]:.6g}" for c in sorted(row)]
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in row:
+            parts.append(f"bf16 MFMA GFLOP {row['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.4g}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in row and row.get("GRBM_GUI_ACTIVE"):
+            parts.append(f"MFMA busy {100 * row['SQ_VALU_MFMA_BUSY_CYCLES'] / (row['GRBM_GUI_ACTIVE'] * 1024):.1f}%")
+        print(f"{short} [{n} dispatches]: " + "; ".join(parts))
+
+
+def measuring_stick():
+    """hipBLASLt through torch.mm in bf16: one large square GEMM and the codebook
+    head's own shapes (fp32 accumulate, bf16 out), weights rotated over
+    replicas so they come from HBM.  The box's practical matrix-core figure."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(7)
+    out = []
+    for name, M, K, N, reps in (("square 8192^3", 8192, 8192, 8192, 2),
+                                ("head 256 x 2048 -> 16384", 256, 2048, 16384, 5),
+                                ("head 192 x 2048 -> 4096", 192, 2048, 4096, 5),
+                                ("head 16 x 2048 -> 16384", 16, 2048, 16384, 5)):
+        a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        ws = [torch.randn((N, K), generator=g, device=dev).to(torch.bfloat16) for _ in range(reps)]
+        for i in range(3):
+            torch.mm(a, ws[i % reps].t())
+        torch.cuda.synchronize()
+        iters = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            torch.mm(a, ws[i % reps].t())
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / iters * 1e3
+        tf = 2.0 * M * K * N / (us * 1e-6) / 1e12
+        line = {"gemm": name, "us": round(us, 2), "tflops": round(tf, 1), "frac_of_2500": round(tf / 2500, 4)}
+        print(json.dumps(line), flush=True)
+        out.append(line)
+        del a, ws
+    return out
+
+
 def traffic_for_current_kernel():
     """HBM bytes per attention launch measured by rocprofv3 PMC counters, if
     the record was taken on the current attention source; else None."""
@@ -224,6 +288,12 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.pmc_table:
+        pmc_table(args.pmc_table)
+        return
+    if args.measuring_stick:
+        measuring_stick()
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
