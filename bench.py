@@ -171,8 +171,11 @@ def pmc_table(path):
     """Per-kernel averages of each counter of a rocprofv3 counter CSV, plus the
     matrix-core figures derived from them where the counters are present:
     bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, rocprofv3's own
-    MfmaFlopsBF16 expression) and MFMA busy share (SQ_VALU_MFMA_BUSY_CYCLES over
-    GRBM_GUI_ACTIVE x 1024 SIMDs, its MfmaUtil expression)."""
+    MfmaFlopsBF16 expression) and the MFMA busy share per SIMD: the busy
+    cycles, summed over the 1024 SIMDs, per SIMD, over the kernel's elapsed
+    cycles.  GRBM_GUI_ACTIVE reads as the sum over the 8 XCDs (divided by 8 it
+    matches each kernel's traced duration at the shader clock), so the
+    elapsed cycles are GRBM_GUI_ACTIVE / 8."""
     import csv
     from collections import defaultdict
     vals = defaultdict(list)
@@ -187,7 +190,9 @@ def pmc_table(path):
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in row:
             parts.append(f"bf16 MFMA GFLOP {row['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.4g}")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in row and row.get("GRBM_GUI_ACTIVE"):
-            parts.append(f"MFMA busy {100 * row['SQ_VALU_MFMA_BUSY_CYCLES'] / (row['GRBM_GUI_ACTIVE'] * 1024):.1f}%")
+            busy = row["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024
+            elapsed = row["GRBM_GUI_ACTIVE"] / 8
+            parts.append(f"MFMA busy per SIMD {busy:.0f} of {elapsed:.0f} cycles = {100 * busy / elapsed:.1f}%")
         print(f"{short} [{n} dispatches]: " + "; ".join(parts))
 
 
