@@ -248,10 +248,36 @@ def traffic_for_current_kernel():
         return None
 
 
-def cpu_baseline(x, n_streams, min_seconds):
+def host_info():
+    """The host the oracle ran on: model, logical CPUs, this process's
+    affinity and RAM (from /proc on Linux)."""
+    info = {"cpu_count": os.cpu_count()}
+    try:
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                info["ram_gb"] = round(int(line.split()[1]) / 2**20, 1)
+                break
+    except OSError:
+        pass
+    return info
+
+
+def cpu_baseline(x, n_streams, min_seconds, threads=None):
     """The oracle, as it stands, on n_streams streams spread over the length
     distribution (all of them when n_streams is 0 or >= B): attention, head
-    and token choice per stream, repeated until min_seconds have passed."""
+    and token choice per stream, repeated until min_seconds have passed.
+    threads: BLAS/OpenMP thread limit for the run (None: the library default,
+    all cores)."""
+    import contextlib
+
     import numpy as np
 
     import oracle
@@ -265,26 +291,29 @@ def cpu_baseline(x, n_streams, min_seconds):
     q = x.f32(x.q)
     W = x.f32(x.W)
     scale = 1.0 / math.sqrt(c.D)
-    t0 = time.perf_counter()
-    reps = 0
-    while reps == 0 or time.perf_counter() - t0 < min_seconds:
-        oracle.decode_step(q, keys, vals, x.kv_len, scale, c.H_kv, W, x.head_id if c.G > 1 else None,
-                           c.dtype == "bf16", streams=streams)
-        reps += 1
-    dt = time.perf_counter() - t0
-    threads = os.cpu_count()
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        blas = [i["num_threads"] for i in info if i.get("user_api") == "blas"]
-        if blas:
-            threads = max(blas)
-    except Exception:
-        pass
+    except ImportError:
+        threadpoolctl = None
+    limit = (threadpoolctl.threadpool_limits(limits=threads) if threadpoolctl is not None and threads
+             else contextlib.nullcontext())
+    with limit:
+        t0 = time.perf_counter()
+        reps = 0
+        while reps == 0 or time.perf_counter() - t0 < min_seconds:
+            oracle.decode_step(q, keys, vals, x.kv_len, scale, c.H_kv, W, x.head_id if c.G > 1 else None,
+                               c.dtype == "bf16", streams=streams)
+            reps += 1
+        dt = time.perf_counter() - t0
+        used = os.cpu_count()
+        if threadpoolctl is not None:
+            blas = [i["num_threads"] for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+            if blas:
+                used = max(blas)
     rows = len(streams) * c.Kq * reps
     what = "the whole batch" if len(streams) == c.B else \
         f"{len(streams)} of {c.B} streams (spread over the KV-length order)"
-    return {"value": round(rows / dt, 3), "unit": "stream-steps/s", "cores": threads, "kind": "oracle",
+    return {"value": round(rows / dt, 3), "unit": "stream-steps/s", "cores": used, "kind": "oracle",
             "sample": f"{what}, {int(sum(x.kv_len[b] for b in streams))} cached tokens, full head, "
                       f"{reps} repetitions: {dt:.1f} s"}
 
@@ -514,9 +543,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle ...")
+        log("[bench] timing the CPU oracle on all cores, then on one ...")
         cpu = cpu_baseline(x, args.cpu_streams, args.cpu_seconds)
-        log(f"[bench] cpu oracle: {cpu['value']:.2f} {cpu['unit']} ({cpu['sample']})")
+        one = cpu_baseline(x, args.cpu_streams, args.cpu_seconds, threads=1)
+        cpu["single_core"] = {"value": one["value"], "cores": one["cores"], "sample": one["sample"]}
+        cpu["host"] = host_info()
+        log(f"[bench] cpu oracle: {cpu['value']:.2f} {cpu['unit']} on {cpu['cores']} threads, "
+            f"{one['value']:.2f} on {one['cores']} ({cpu['host']})")
 
     head_flops = 2.0 * c.M * c.d_model * c.V if mlp is None else 2.0 * c.M * mlp[3] * (c.d_model + c.V)
     out = {

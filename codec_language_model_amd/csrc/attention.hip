@@ -1055,43 +1055,9 @@ hipError_t launch_nr(const KParams& P, int nr_tmpl, int grid, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
-bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_len, AttnPlan* p) {
-  if (B < 1 || Kq < 1 || H_kv < 1 || H_q % H_kv || max_kv_len < 1) return false;
-  const int nr = (H_q / H_kv) * Kq;
-  if (nr > 16) return false;
-  p->nr = nr;
-  p->nr_tmpl = nr <= 1 ? 1 : nr <= 2 ? 2 : nr <= 4 ? 4 : nr <= 8 ? 8 : nr <= 12 ? 12 : 16;
-  // Split length: the largest power of two <= (expected token-heads / c),
-  // clamped to [64, 1024] tokens, taking lengths to average half the maximum;
-  // c = 512, or 256 for blocks of more than 2 query rows (the matrix-core
-  // kernel, whose tiles cost more per token).  Long splits cost less per
-  // token (fewer partial results, fewer pipeline restarts); short ones keep
-  // small batches spread over the CUs.  Measured on MI355X: 256 streams x
-  // log-uniform 64..8192 keys run 8% faster at 1024 than at 256 tokens, 64
-  // streams x 200..3000 keys 25% faster at 512-1024, 16 streams x 100..1500
-  // keys best at 128, and 32 streams x 6-query blocks over 300..2000 keys
-  // best at 512.  An item then spans at most 64 blocks of 16 tokens (one
-  // block id per lane).
-  // The matrix-core kernel stops at 512: its items carry 3..16 query rows,
-  // and 32 streams x 6-query blocks over 300..2000 keys took 39.9 us at 512
-  // against 59.8 us at 1024 (a max_kv_len 4.5% larger tipped the rule over).
-  const double est = (double)B * H_kv * (max_kv_len > 1 ? max_kv_len / 2.0 : 1.0);
-  const double per = nr > 2 ? 256.0 : 512.0;
-  const long top = nr > 2 ? 512 : 1024;
-  long split = 64;
-  while (split < top && (double)(split * 2) * per <= est) split *= 2;
-  p->split = (int)split;
-  p->max_splits = (int)((max_kv_len + split - 1) / split);
-  const size_t slots = (size_t)B * H_kv * p->max_splits * p->nr_tmpl;
-  p->ml_offset = 0;
-  p->acc_offset = p->ml_offset + align256(slots * 2 * sizeof(float));
-  p->total_bytes = p->acc_offset + align256(slots * (size_t)D * sizeof(float));
-  return true;
-}
 
 hipError_t attention_scratch(void** ptr) {
   constexpr int kMaxDev = 64;

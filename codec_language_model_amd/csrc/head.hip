@@ -30,7 +30,6 @@ namespace clm {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kHeadWGs = 256;           // workgroups the tile choice aims for
 
 struct HeadP {
   const uint16_t* h;
@@ -317,30 +316,6 @@ __global__ __launch_bounds__(256) void head_gemv_f32_kernel(GemvP P) {
 
 }  // namespace
 
-HeadPlan plan_codebook_head(int M, int V, int G) {
-  // MR in {32, 64, 96, 128}: the fewest padded rows for the rows one stage
-  // is expected to hold (all M for one stage; M/G on average otherwise), the
-  // larger on ties; NV in {128, 64, 32}: the widest that still gives
-  // kHeadWGs working workgroups; 8 waves where the tile is tall enough to
-  // keep two waves per SIMD busy (and its rows split into 64-row DMA rounds).
-  HeadPlan p{};
-  const int m_est = G == 1 ? M : (M + G - 1) / G;
-  int mr = 128;
-  for (int c : {96, 64, 32})
-    if ((m_est + c - 1) / c * c < (m_est + mr - 1) / mr * mr) mr = c;
-  const int rc_est = (m_est + mr - 1) / mr;
-  int nv = 32;
-  for (int c : {128, 64})
-    if ((long)((V + c - 1) / c) * rc_est * G >= kHeadWGs) { nv = c; break; }
-  p.mr = mr;
-  p.nv = nv;
-  p.nw = (mr >= 96 && (nv + mr) % 64 == 0) ? 8 : 4;
-  p.row_chunks = (M + mr - 1) / mr;
-  p.nvt = (V + nv - 1) / nv;
-  p.nvt_pad = (p.nvt + kXcds - 1) / kXcds * kXcds;
-  p.workspace_bytes = 0;
-  return p;
-}
 
 hipError_t launch_codebook_head(const HeadArgs& a, hipStream_t s) {
   if (a.bf16) {

@@ -132,26 +132,26 @@ int clm_decode_loop_create(const clm_decode_step_desc* desc, int n_steps, clm_de
   if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return CLM_ERR_HIP;
   hipGraph_t graph = nullptr;
   if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
-    hipStreamDestroy(cs);
+    (void)hipStreamDestroy(cs);
     return CLM_ERR_HIP;
   }
   for (int s = 0; s < n_steps && rc == CLM_OK; ++s) rc = record_step(d, s, cs);
   const hipError_t ec = hipStreamEndCapture(cs, &graph);
-  hipStreamDestroy(cs);
+  (void)hipStreamDestroy(cs);
   if (rc == CLM_OK && ec != hipSuccess) rc = CLM_ERR_HIP;
   if (rc != CLM_OK) {
-    if (graph) hipGraphDestroy(graph);
+    if (graph) (void)hipGraphDestroy(graph);
     return rc;
   }
   hipGraphExec_t exec = nullptr;
   if (hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
-    hipGraphDestroy(graph);
+    (void)hipGraphDestroy(graph);
     return CLM_ERR_HIP;
   }
   clm_decode_loop* l = new (std::nothrow) clm_decode_loop;
   if (!l) {
-    hipGraphExecDestroy(exec);
-    hipGraphDestroy(graph);
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
     return CLM_ERR_HIP;
   }
   l->graph = graph;

@@ -277,3 +277,34 @@ def test_decode_loop_host_checks(lib):
     assert lib.clm_advance_lengths(N, P, N, N, 4, 1, S) == INVALID
     assert lib.clm_advance_lengths(P, P, N, N, 0, 1, S) == INVALID
     assert lib.clm_advance_lengths(P, P, N, N, 4, 0, S) == INVALID
+
+
+def test_host_validation_under_sanitizers(tmp_path):
+    """The host code of the library (argument validation, launch planning,
+    checked-mode plumbing, the decode-loop builder) built for the CPU alone
+    with AddressSanitizer and UndefinedBehaviorSanitizer, kernel launches
+    replaced by stubs that report no device, and driven through every entry
+    point with good and bad arguments (tests/host_sanitize/main.cpp).  Any
+    sanitizer finding aborts the run; every status must be the documented one."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime.h"):
+        pytest.skip("needs g++ and the ROCm headers")
+    csrc = os.path.join(ROOT, "codec_language_model_amd", "csrc")
+    here = os.path.join(ROOT, "tests", "host_sanitize")
+    exe = str(tmp_path / "clm_host_sanitize")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-I" + os.path.join(ROOT, "include"),
+           os.path.join(csrc, "abi.cpp"), os.path.join(csrc, "loop.cpp"), os.path.join(csrc, "plan.cpp"),
+           os.path.join(here, "stubs.cpp"), os.path.join(here, "main.cpp"),
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1", HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-4000:]
+    assert "ok: 0 mismatches" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
