@@ -39,6 +39,8 @@ if ROOT not in sys.path:
 
 METRIC = "codec decode steps/s (streams×tokens) and % HBM roofline of KV attention"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+DEFAULT_WORKLOAD = "c5"          # 256 streams, log-uniform 64..8192 keys (the metric's workload)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_c5_traffic.txt")
 ATTN_SRCS = [os.path.join(ROOT, "codec_language_model_amd", "csrc", f) for f in ("attention.hip", "clm_device.h")]
 COPY_BYTES = 1 << 30
@@ -53,7 +55,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c5")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-streams", type=int, default=0,
                     help="streams in the oracle's timed sample (0 = the whole batch)")
@@ -107,6 +109,12 @@ def attention_source_hash():
     return h.hexdigest()[:16]
 
 
+def _synth():
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import synth
+    return synth
+
+
 def pmc_summary(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
     """HBM bytes per decode_attention launch from two PMC runs.  FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch) are averaged per kernel over its dispatches,
@@ -157,6 +165,7 @@ def pmc_summary(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
     lines += [
         f"# 1 GiB copy: FETCH_SIZE {f_copy:.1f} KiB, WRITE_SIZE {w_copy:.1f} KiB per dispatch",
         f"attention_source_sha256_16 = {attention_source_hash()}",
+        f"workload = {_synth().get_config(DEFAULT_WORKLOAD).workload}",
         f"fetch_scale = {f_scale:.4f}",
         f"write_scale = {w_scale:.4f}",
         f"hbm_fetch_bytes_per_launch = {fetch:.0f}",
@@ -222,16 +231,17 @@ def measuring_stick():
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / iters * 1e3
         tf = 2.0 * M * K * N / (us * 1e-6) / 1e12
-        line = {"gemm": name, "us": round(us, 2), "tflops": round(tf, 1), "frac_of_2500": round(tf / 2500, 4)}
+        line = {"gemm": name, "us": round(us, 2), "tflops": round(tf, 1), "frac_of_2500": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
         print(json.dumps(line), flush=True)
         out.append(line)
         del a, ws
     return out
 
 
-def traffic_for_current_kernel():
+def traffic_for_current_kernel(workload):
     """HBM bytes per attention launch measured by rocprofv3 PMC counters, if
-    the record was taken on the current attention source; else None."""
+    the record was taken on the current attention source and on this workload;
+    else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     src_hash = attention_source_hash()
@@ -240,7 +250,7 @@ def traffic_for_current_kernel():
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("attention_source_sha256_16") != src_hash:
+    if vals.get("attention_source_sha256_16") != src_hash or vals.get("workload") != workload:
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -527,7 +537,7 @@ def main():
     attn_s = per_us[1] * 1e-6
     attn_bytes = attention_bytes(c, x.kv_len, fp8=f8 is not None)
     achieved = attn_bytes / attn_s / 1e9
-    traffic = traffic_for_current_kernel() if f8 is None else None
+    traffic = traffic_for_current_kernel(c.workload) if f8 is None else None
     log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; per call (us): append {per_us[0]:.1f}, "
         f"attention {per_us[1]:.1f}, head {per_us[2]:.1f}, token {per_us[3]:.1f}; attention "
         f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
@@ -591,6 +601,14 @@ def main():
         "codebook_head_tflops": round(head_flops / (per_us[2] * 1e-6) / 1e12, 2),
         "cpu_baseline": cpu,
     }
+    if bf:
+        out["codebook_head_mfma_frac"] = round(head_flops / (per_us[2] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+    if spec is not None:
+        # verified positions are B*Kq per step; the tokens kept are what the
+        # verification emitted (the same every step: the inputs do not change)
+        emitted = int(num_em.sum().item())
+        out["emitted_tokens_per_s"] = round(emitted / (wall / timed_steps), 1)
+        out["emitted_per_stream"] = round(emitted / c.B, 3)
     print(json.dumps(out), flush=True)
 
 

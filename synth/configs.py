@@ -16,7 +16,7 @@ import math
 @dataclasses.dataclass(frozen=True)
 class DecodeConfig:
     name: str
-    index: int              # 1-based; the seed is 1000 + index
+    index: int              # 1-based; the seed is 1000 + index (+ 100000 per trial)
     B: int                  # streams
     Kq: int                 # queries per stream (= rows appended per step)
     H_q: int
@@ -33,6 +33,7 @@ class DecodeConfig:
     block_size: int = 16
     draft_logit_std: float = 2.0
     description: str = ""
+    trial: int = 0          # independent redraws of the same workload (0: the standard draw)
 
     @property
     def d_model(self) -> int:
@@ -44,7 +45,7 @@ class DecodeConfig:
 
     @property
     def seed(self) -> int:
-        return 1000 + self.index
+        return 1000 + self.index + 100000 * self.trial
 
     @property
     def workload(self) -> str:

@@ -54,6 +54,14 @@ def check_close(gpu, ref, what, atol=ATOL, rtol=RTOL):
     return float(err.max()) if err.size else 0.0
 
 
+def tolerance_used(gpu, ref, atol=ATOL, rtol=RTOL):
+    """The largest |gpu - ref| / (atol + rtol |ref|): 1.0 is the edge of the bar."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    r = np.abs(gpu - ref) / (atol + rtol * np.abs(ref))
+    return float(r.max()) if r.size else 0.0
+
+
 def check_argmax(gpu_tok, ref_logits, what, vocab_valid=None):
     """Returns the number of exempt rows."""
     exempt = 0

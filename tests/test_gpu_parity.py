@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from parity import (bf16_tensor_to_f32, check_argmax, check_close, check_sampled, check_verify,
+from parity import (bf16_tensor_to_f32, tolerance_used, check_argmax, check_close, check_sampled, check_verify,
                     to_torch)
 
 pytestmark = pytest.mark.gpu
@@ -460,8 +460,11 @@ def test_chained_step(clm_gpu, cfg):
     ref = oracle.decode_step(x.f32(x.q), keys, vals, x.kv_len, scale, c.H_kv, x.f32(x.W), x.head_id,
                              c.dtype == "bf16", mode=c.mode,
                              temperature=(c.temperature if c.mode == "spec" else temp), uniforms=u, spec=spec)
-    check_close(bf16_tensor_to_f32(o), ref["o"], f"chained attention c{cfg}")
-    check_close(logits.cpu().numpy(), ref["logits"], f"chained logits c{cfg}")
+    o_f = bf16_tensor_to_f32(o)
+    l_f = logits.cpu().numpy()
+    err_o = check_close(o_f, ref["o"], f"chained attention c{cfg}")
+    err_l = check_close(l_f, ref["logits"], f"chained logits c{cfg}")
+    use_o, use_l = tolerance_used(o_f, ref["o"]), tolerance_used(l_f, ref["logits"])
     if c.mode == "spec":
         dp, dtok, ua, ur = _spec_inputs_torch(spec)
         toks, num = clm_gpu.spec_verify(logits.view(c.B, c.Kq, c.V), dp, dtok, ua, ur, c.temperature)
@@ -474,8 +477,41 @@ def test_chained_step(clm_gpu, cfg):
     else:
         tok = clm_gpu.sample_or_argmax(logits).cpu().numpy()
         ex = check_argmax(tok, ref["logits"], f"chained argmax c{cfg}")
-    print(f"chained c{cfg}: exempt {ex}")
+    print(f"chained c{cfg} (B {c.B}): max |o err| {err_o:.3g} ({use_o:.2f} of the bar), "
+          f"max |logit err| {err_l:.3g} ({use_l:.2f} of the bar), exempt {ex}")
     del torch
+
+
+def test_tiny_workload_many_draws(clm_gpu):
+    """The tiny fp32 workload over 200 independent draws (its greedy tokens
+    often sit within the 1e-3 top-2 gap of the argmax rule, so one draw says
+    little): the chained step against the oracle's on every draw."""
+    import dataclasses
+    base = synth.get_config(1)
+    exempt = 0
+    worst_o = worst_l = 0.0
+    for t in range(200):
+        x = synth.make_inputs(dataclasses.replace(base, trial=t))
+        c = x.cfg
+        d = Dev(x, include_new=False)
+        scale = 1.0 / math.sqrt(c.D)
+        clm_gpu.kv_cache_append(d.k_new, d.v_new, d.k_cache, d.v_cache, d.block_table, d.len_before,
+                                block_size=c.block_size)
+        o = clm_gpu.decode_attention(d.q, d.k_cache, d.v_cache, d.block_table, d.kv_len, d.max_kv_len,
+                                     scale=scale)
+        logits = clm_gpu.codebook_head(o.view(c.M, c.d_model), d.W)
+        tok = clm_gpu.sample_or_argmax(logits).cpu().numpy()
+        keys, vals = logical(x)
+        ref = oracle.decode_step(x.f32(x.q), keys, vals, x.kv_len, scale, c.H_kv, x.f32(x.W), None, False)
+        o_f = o.cpu().numpy()
+        l_f = logits.cpu().numpy()
+        check_close(o_f, ref["o"], f"tiny attention, draw {t}")
+        check_close(l_f, ref["logits"], f"tiny logits, draw {t}")
+        worst_o = max(worst_o, tolerance_used(o_f, ref["o"]))
+        worst_l = max(worst_l, tolerance_used(l_f, ref["logits"]))
+        exempt += check_argmax(tok, ref["logits"], f"tiny argmax, draw {t}")
+    print(f"tiny workload, 200 draws: worst {worst_o:.2g} (o) and {worst_l:.2g} (logits) of the bar, "
+          f"argmax exempt {exempt}/200")
 
 
 def test_full_size_high_concurrency(clm_gpu):
@@ -493,10 +529,14 @@ def test_full_size_high_concurrency(clm_gpu):
     tok = clm_gpu.sample_or_argmax(logits).cpu().numpy()
     keys, vals = logical(x)
     ref = oracle.decode_step(x.f32(x.q), keys, vals, x.kv_len, scale, c.H_kv, x.f32(x.W), None, True)
-    err_o = check_close(bf16_tensor_to_f32(o), ref["o"], "full-size attention, all 256 streams")
-    err_l = check_close(logits.cpu().numpy(), ref["logits"], "full-size logits, all 256 streams")
+    o_f = bf16_tensor_to_f32(o)
+    l_f = logits.cpu().numpy()
+    err_o = check_close(o_f, ref["o"], "full-size attention, all 256 streams")
+    err_l = check_close(l_f, ref["logits"], "full-size logits, all 256 streams")
     ex = check_argmax(tok, ref["logits"], "full-size argmax, all 256 streams")
-    print(f"full size: max |o err| {err_o:.3g}, max |logit err| {err_l:.3g}, argmax exempt {ex}/{c.M}")
+    print(f"full size: max |o err| {err_o:.3g} ({tolerance_used(o_f, ref['o']):.2f} of the bar), "
+          f"max |logit err| {err_l:.3g} ({tolerance_used(l_f, ref['logits']):.2f} of the bar), "
+          f"argmax exempt {ex}/{c.M}")
     # the append at full size: the whole pool against the oracle's append
     rk, rv = oracle.kv_cache_append(d.k_pool_host, d.v_pool_host, x.block_table, x.len_before,
                                     x.k_new, x.v_new, c.block_size)
