@@ -162,9 +162,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // ---- streaming loads ----------------------------------------------------------
-// Non-temporal global loads (the nt bit): for data read once per call (the
-// KV cache, head weights, logits).  On gfx950 they sustain a higher HBM read
-// rate than default-policy loads on scattered 4 KiB pages.
+// Non-temporal global loads (the nt bit): for data streamed once per call
+// from HBM (the KV cache).  On gfx950 they sustain a higher HBM read rate
+// than default-policy loads on scattered 4 KiB pages.
 typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned nt_u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 ld_nt(const uint4* p) {
