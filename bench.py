@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only the chosen workload (by default the 256-stream step is followed by "
+                         "short eager runs of the four smaller workloads, reported under other_workloads; "
+                         "profiler runs of one workload pass this flag)")
     ap.add_argument("--cpu-streams", type=int, default=0,
                     help="streams in the oracle's timed sample (0 = the whole batch)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -359,256 +363,280 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    cfg = synth.get_config(args.workload)
-    graph = args.graph == "on"
-    if graph and (args.kv != "bf16" or args.head != "linear"):
-        print("--graph on runs the decode loop of the bf16/fp32 cache and the linear head", file=sys.stderr)
-        sys.exit(2)
-    t_gen = time.perf_counter()
-    x = synth.make_inputs(cfg)
-    c = x.cfg
-    bf = c.dtype == "bf16"
-    n_loop = max(1, args.graph_steps) if graph else 1
-    # pages for the loop's later steps (the same pages as the step's own for
-    # every position the eager step touches)
-    kp, vp, bt_np, _ = x.pool_with_room((n_loop - 1) * c.Kq)
-    log(f"[bench] {c.workload}: inputs drawn in {time.perf_counter() - t_gen:.1f} s "
-        f"(sum kv_len {int(x.kv_len.sum())}, pool {kp.nbytes * 2 / 2**30:.2f} GiB)")
-
-    def dev_t(a, bf16):
-        a = np.ascontiguousarray(a)
-        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
-        return t.to(dev)
-
-    k_cache, v_cache = dev_t(kp, bf), dev_t(vp, bf)
-    f8 = None
-    if args.kv == "fp8":
-        if not bf:
-            print("--kv fp8 needs a bf16 workload", file=sys.stderr)
+    def run_one(args):
+        """One workload: draw inputs, time the steps, return the JSON object."""
+        cfg = synth.get_config(args.workload)
+        graph = args.graph == "on"
+        if graph and (args.kv != "bf16" or args.head != "linear"):
+            print("--graph on runs the decode loop of the bf16/fp32 cache and the linear head", file=sys.stderr)
             sys.exit(2)
-        # synthetic E4M3 cache of the pool's shapes: uniform codes without the
-        # two NaN codes, row scales uniform in [0.002, 0.01] (max|x|/448 for
-        # rows of N(0,1) values is ~0.007)
-        g = torch.Generator(device=dev).manual_seed(4321)
-        def codes(shape):
-            cde = torch.randint(0, 254, shape, generator=g, device=dev, dtype=torch.int32)
-            cde = cde + (cde >= 0x7F).to(torch.int32)
-            return cde.to(torch.uint8)
-        nb_, hk_, bs_ = kp.shape[0], kp.shape[1], kp.shape[2]
-        f8 = (codes((nb_, hk_, c.D // 8, bs_, 8)), codes(tuple(vp.shape)),
-              torch.empty((nb_, hk_, bs_), device=dev).uniform_(0.002, 0.01, generator=g),
-              torch.empty((nb_, hk_, bs_), device=dev).uniform_(0.002, 0.01, generator=g))
-        del k_cache, v_cache
-        k_cache = v_cache = None
-    del kp, vp
-    bt, kv_len, len_before = dev_t(bt_np, False), dev_t(x.kv_len, False), dev_t(x.len_before, False)
-    k_new, v_new, q = dev_t(x.k_new, bf), dev_t(x.v_new, bf), dev_t(x.q, bf)
-    W = dev_t(x.W, bf)
-    head_id = dev_t(x.head_id, False) if c.G > 1 else None
-    mlp = None
-    if args.head == "mlp":
-        if not bf:
-            print("--head mlp needs a bf16 workload", file=sys.stderr)
-            sys.exit(2)
-        F = 4096
-        gen = torch.Generator(device=dev).manual_seed(1234)
-        W1 = (torch.randn((c.G, F, c.d_model), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
-        W2 = (torch.randn((c.G, c.V, F), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
-        act = torch.empty((c.M, F), dtype=torch.bfloat16, device=dev)
-        mlp = (W1, W2, act, F)
-    max_kv = int(x.kv_len.max()) + (n_loop - 1) * c.Kq
-    rope_pos = None
-    if args.append == "rope":
-        rope_pos = dev_t((x.len_before[:, None] + 1000 + np.arange(c.Kq)[None, :]).astype(np.int32), False)
-    scale = 1.0 / math.sqrt(c.D)
-    o = torch.empty_like(q)
-    logits = torch.empty((c.M, c.V), dtype=torch.float32, device=dev)
-    tokens = torch.empty(c.M, dtype=torch.int32, device=dev)
-    ws = clm.Workspace.get(clm.decode_attention_workspace_size(c.B, c.Kq, c.H_q, c.H_kv, c.D, max_kv), dev)
-    temp = uni = None
-    if c.mode == "sample":
-        temp = torch.full((c.M,), c.temperature, dtype=torch.float32, device=dev)
-        uni = dev_t(x.uniforms(), False)
-    spec = None
-    if c.mode == "spec":
-        s = x.spec_inputs()
-        spec = tuple(dev_t(s[k], False) for k in ("draft_probs", "draft_tokens", "u_accept", "u_resample"))
-        out_tok = torch.empty((c.B, c.Kq), dtype=torch.int32, device=dev)
-        num_em = torch.empty(c.B, dtype=torch.int32, device=dev)
-    torch.cuda.synchronize()
+        t_gen = time.perf_counter()
+        x = synth.make_inputs(cfg)
+        c = x.cfg
+        bf = c.dtype == "bf16"
+        n_loop = max(1, args.graph_steps) if graph else 1
+        # pages for the loop's later steps (the same pages as the step's own for
+        # every position the eager step touches)
+        kp, vp, bt_np, _ = x.pool_with_room((n_loop - 1) * c.Kq)
+        log(f"[bench] {c.workload}: inputs drawn in {time.perf_counter() - t_gen:.1f} s "
+            f"(sum kv_len {int(x.kv_len.sum())}, pool {kp.nbytes * 2 / 2**30:.2f} GiB)")
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        if f8 is not None:
-            clm.kv_cache_append_fp8(k_new, v_new, *f8, bt, len_before, block_size=c.block_size)
-        elif rope_pos is None:
-            clm.kv_cache_append(k_new, v_new, k_cache, v_cache, bt, len_before, block_size=c.block_size)
-        else:
-            clm.rope_kv_cache_append(q, k_new, v_new, k_cache, v_cache, bt, len_before, rope_pos, 1.0e6,
-                                     block_size=c.block_size)
-        if ev is not None:
-            ev[1].record()
-        if f8 is None:
-            clm.decode_attention(q, k_cache, v_cache, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
-        else:
-            clm.decode_attention_fp8(q, *f8, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
-        if ev is not None:
-            ev[2].record()
-        if mlp is None:
-            clm.codebook_head(o.view(c.M, c.d_model), W, head_id, out=logits)
-        else:
-            clm.codebook_head_mlp(o.view(c.M, c.d_model), mlp[0], mlp[1], head_id, act=mlp[2], out=logits)
-        if ev is not None:
-            ev[3].record()
-        if spec is not None:
-            clm.spec_verify(logits.view(c.B, c.Kq, c.V), *spec, c.temperature, out_tokens=out_tok,
-                            num_emitted=num_em)
-        else:
-            clm.sample_or_argmax(logits, temp, uni, out=tokens)
-        if ev is not None:
-            ev[4].record()
+        def dev_t(a, bf16):
+            a = np.ascontiguousarray(a)
+            t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
+            return t.to(dev)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # The decode loop: n_loop steps captured natively as one HIP graph
-    # (clm_decode_loop_*), the lengths (and positions) advancing on the
-    # device between steps.  Each launch runs n_loop steps; the lengths are
-    # then reset by two small device copies so every launch sees the same
-    # workload.
-    run = step
-    steps_per_run = 1
-    if graph:
-        rep = lambda t: t.unsqueeze(0).expand((n_loop,) + tuple(t.shape)).contiguous()
-        lg_all = torch.empty((n_loop, c.M, c.V), dtype=torch.float32, device=dev)
-        lp = dict(k_cache=k_cache, v_cache=v_cache, block_table=bt, len_before=len_before, kv_len=kv_len,
-                  max_kv_len=max_kv, k_new=rep(k_new), v_new=rep(v_new), q=rep(q), W=W, head_id=head_id,
-                  o=torch.empty_like(rep(q)), logits=lg_all, mode=c.mode, attn_workspace=ws,
-                  block_size=c.block_size)
-        if rope_pos is not None:
-            lp.update(positions=rope_pos, rope_base=1.0e6)
+        k_cache, v_cache = dev_t(kp, bf), dev_t(vp, bf)
+        f8 = None
+        if args.kv == "fp8":
+            if not bf:
+                print("--kv fp8 needs a bf16 workload", file=sys.stderr)
+                sys.exit(2)
+            # synthetic E4M3 cache of the pool's shapes: uniform codes without the
+            # two NaN codes, row scales uniform in [0.002, 0.01] (max|x|/448 for
+            # rows of N(0,1) values is ~0.007)
+            g = torch.Generator(device=dev).manual_seed(4321)
+            def codes(shape):
+                cde = torch.randint(0, 254, shape, generator=g, device=dev, dtype=torch.int32)
+                cde = cde + (cde >= 0x7F).to(torch.int32)
+                return cde.to(torch.uint8)
+            nb_, hk_, bs_ = kp.shape[0], kp.shape[1], kp.shape[2]
+            f8 = (codes((nb_, hk_, c.D // 8, bs_, 8)), codes(tuple(vp.shape)),
+                  torch.empty((nb_, hk_, bs_), device=dev).uniform_(0.002, 0.01, generator=g),
+                  torch.empty((nb_, hk_, bs_), device=dev).uniform_(0.002, 0.01, generator=g))
+            del k_cache, v_cache
+            k_cache = v_cache = None
+        del kp, vp
+        bt, kv_len, len_before = dev_t(bt_np, False), dev_t(x.kv_len, False), dev_t(x.len_before, False)
+        k_new, v_new, q = dev_t(x.k_new, bf), dev_t(x.v_new, bf), dev_t(x.q, bf)
+        W = dev_t(x.W, bf)
+        head_id = dev_t(x.head_id, False) if c.G > 1 else None
+        mlp = None
+        if args.head == "mlp":
+            if not bf:
+                print("--head mlp needs a bf16 workload", file=sys.stderr)
+                sys.exit(2)
+            F = 4096
+            gen = torch.Generator(device=dev).manual_seed(1234)
+            W1 = (torch.randn((c.G, F, c.d_model), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            W2 = (torch.randn((c.G, c.V, F), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            act = torch.empty((c.M, F), dtype=torch.bfloat16, device=dev)
+            mlp = (W1, W2, act, F)
+        max_kv = int(x.kv_len.max()) + (n_loop - 1) * c.Kq
+        rope_pos = None
+        if args.append == "rope":
+            rope_pos = dev_t((x.len_before[:, None] + 1000 + np.arange(c.Kq)[None, :]).astype(np.int32), False)
+        scale = 1.0 / math.sqrt(c.D)
+        o = torch.empty_like(q)
+        logits = torch.empty((c.M, c.V), dtype=torch.float32, device=dev)
+        tokens = torch.empty(c.M, dtype=torch.int32, device=dev)
+        ws = clm.Workspace.get(clm.decode_attention_workspace_size(c.B, c.Kq, c.H_q, c.H_kv, c.D, max_kv), dev)
+        temp = uni = None
+        if c.mode == "sample":
+            temp = torch.full((c.M,), c.temperature, dtype=torch.float32, device=dev)
+            uni = dev_t(x.uniforms(), False)
+        spec = None
         if c.mode == "spec":
-            lp.update(spec_temperature=c.temperature, draft_probs=rep(spec[0].view(c.B, c.Kq, c.V)),
-                      draft_tokens=rep(spec[1]), u_accept=rep(spec[2]), u_resample=rep(spec[3]),
-                      out_tokens=torch.empty((n_loop, c.B, c.Kq), dtype=torch.int32, device=dev),
-                      num_emitted=torch.empty((n_loop, c.B), dtype=torch.int32, device=dev))
-        else:
-            lp.update(tokens=torch.empty((n_loop, c.M), dtype=torch.int32, device=dev))
-            if c.mode == "sample":
-                lp.update(temperature=rep(temp), uniforms=rep(uni))
-        state0 = [t.clone() for t in (len_before, kv_len) + ((rope_pos,) if rope_pos is not None else ())]
-        loop = clm.DecodeLoop(**lp)
+            s = x.spec_inputs()
+            spec = tuple(dev_t(s[k], False) for k in ("draft_probs", "draft_tokens", "u_accept", "u_resample"))
+            out_tok = torch.empty((c.B, c.Kq), dtype=torch.int32, device=dev)
+            num_em = torch.empty(c.B, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
 
-        def run():
-            loop.launch()
-            for t, t0 in zip((len_before, kv_len, rope_pos), state0):
-                t.copy_(t0)
-        steps_per_run = n_loop
-        for _ in range(max(1, args.warmup // n_loop)):
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record()
+            if f8 is not None:
+                clm.kv_cache_append_fp8(k_new, v_new, *f8, bt, len_before, block_size=c.block_size)
+            elif rope_pos is None:
+                clm.kv_cache_append(k_new, v_new, k_cache, v_cache, bt, len_before, block_size=c.block_size)
+            else:
+                clm.rope_kv_cache_append(q, k_new, v_new, k_cache, v_cache, bt, len_before, rope_pos, 1.0e6,
+                                         block_size=c.block_size)
+            if ev is not None:
+                ev[1].record()
+            if f8 is None:
+                clm.decode_attention(q, k_cache, v_cache, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
+            else:
+                clm.decode_attention_fp8(q, *f8, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
+            if ev is not None:
+                ev[2].record()
+            if mlp is None:
+                clm.codebook_head(o.view(c.M, c.d_model), W, head_id, out=logits)
+            else:
+                clm.codebook_head_mlp(o.view(c.M, c.d_model), mlp[0], mlp[1], head_id, act=mlp[2], out=logits)
+            if ev is not None:
+                ev[3].record()
+            if spec is not None:
+                clm.spec_verify(logits.view(c.B, c.Kq, c.V), *spec, c.temperature, out_tokens=out_tok,
+                                num_emitted=num_em)
+            else:
+                clm.sample_or_argmax(logits, temp, uni, out=tokens)
+            if ev is not None:
+                ev[4].record()
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+
+        # The decode loop: n_loop steps captured natively as one HIP graph
+        # (clm_decode_loop_*), the lengths (and positions) advancing on the
+        # device between steps.  Each launch runs n_loop steps; the lengths are
+        # then reset by two small device copies so every launch sees the same
+        # workload.
+        run = step
+        steps_per_run = 1
+        if graph:
+            rep = lambda t: t.unsqueeze(0).expand((n_loop,) + tuple(t.shape)).contiguous()
+            lg_all = torch.empty((n_loop, c.M, c.V), dtype=torch.float32, device=dev)
+            lp = dict(k_cache=k_cache, v_cache=v_cache, block_table=bt, len_before=len_before, kv_len=kv_len,
+                      max_kv_len=max_kv, k_new=rep(k_new), v_new=rep(v_new), q=rep(q), W=W, head_id=head_id,
+                      o=torch.empty_like(rep(q)), logits=lg_all, mode=c.mode, attn_workspace=ws,
+                      block_size=c.block_size)
+            if rope_pos is not None:
+                lp.update(positions=rope_pos, rope_base=1.0e6)
+            if c.mode == "spec":
+                lp.update(spec_temperature=c.temperature, draft_probs=rep(spec[0].view(c.B, c.Kq, c.V)),
+                          draft_tokens=rep(spec[1]), u_accept=rep(spec[2]), u_resample=rep(spec[3]),
+                          out_tokens=torch.empty((n_loop, c.B, c.Kq), dtype=torch.int32, device=dev),
+                          num_emitted=torch.empty((n_loop, c.B), dtype=torch.int32, device=dev))
+            else:
+                lp.update(tokens=torch.empty((n_loop, c.M), dtype=torch.int32, device=dev))
+                if c.mode == "sample":
+                    lp.update(temperature=rep(temp), uniforms=rep(uni))
+            state0 = [t.clone() for t in (len_before, kv_len) + ((rope_pos,) if rope_pos is not None else ())]
+            loop = clm.DecodeLoop(**lp)
+
+            def run():
+                loop.launch()
+                for t, t0 in zip((len_before, kv_len, rope_pos), state0):
+                    t.copy_(t0)
+            steps_per_run = n_loop
+            for _ in range(max(1, args.warmup // n_loop)):
+                run()
+            torch.cuda.synchronize()
+
+        # whole-step throughput: K steps back to back, no events inside
+        n_runs = max(1, -(-args.steps // steps_per_run))
+        t0 = time.perf_counter()
+        for _ in range(n_runs):
             run()
         torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        timed_steps = n_runs * steps_per_run
 
-    # whole-step throughput: K steps back to back, no events inside
-    n_runs = max(1, -(-args.steps // steps_per_run))
-    t0 = time.perf_counter()
-    for _ in range(n_runs):
-        run()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    timed_steps = n_runs * steps_per_run
-
-    # per-call durations: the same K steps again with HIP events between the
-    # calls, recorded on the stream the kernels run on (torch's current stream)
-    # and read after one synchronisation at the end, so the host stays ahead of
-    # the GPU and no launch gap is timed
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    per = np.zeros(4)
-    for e in evs:
-        per += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
-    per_us = per / args.steps * 1e3
-
-    ms_per_step = wall / timed_steps * 1e3
-    value = c.B * c.Kq / (wall / timed_steps)
-    attn_s = per_us[1] * 1e-6
-    attn_bytes = attention_bytes(c, x.kv_len, fp8=f8 is not None)
-    achieved = attn_bytes / attn_s / 1e9
-    traffic = traffic_for_current_kernel(c.workload) if f8 is None else None
-    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; per call (us): append {per_us[0]:.1f}, "
-        f"attention {per_us[1]:.1f}, head {per_us[2]:.1f}, token {per_us[3]:.1f}; attention "
-        f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
-
-    if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
+        # per-call durations: the same K steps again with HIP events between the
+        # calls, recorded on the stream the kernels run on (torch's current stream)
+        # and read after one synchronisation at the end, so the host stays ahead of
+        # the GPU and no launch gap is timed
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(evs[i])
         torch.cuda.synchronize()
-        log("[bench] copy calibration: 5 x 1 GiB device-to-device copies done")
-        del src, dst
+        per = np.zeros(4)
+        for e in evs:
+            per += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
+        per_us = per / args.steps * 1e3
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on all cores, then on one ...")
-        cpu = cpu_baseline(x, args.cpu_streams, args.cpu_seconds)
-        one = cpu_baseline(x, args.cpu_streams, args.cpu_seconds, threads=1)
-        cpu["single_core"] = {"value": one["value"], "cores": one["cores"], "sample": one["sample"]}
-        cpu["host"] = host_info()
-        log(f"[bench] cpu oracle: {cpu['value']:.2f} {cpu['unit']} on {cpu['cores']} threads, "
-            f"{one['value']:.2f} on {one['cores']} ({cpu['host']})")
+        ms_per_step = wall / timed_steps * 1e3
+        value = c.B * c.Kq / (wall / timed_steps)
+        attn_s = per_us[1] * 1e-6
+        attn_bytes = attention_bytes(c, x.kv_len, fp8=f8 is not None)
+        achieved = attn_bytes / attn_s / 1e9
+        traffic = traffic_for_current_kernel(c.workload) if f8 is None else None
+        log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; per call (us): append {per_us[0]:.1f}, "
+            f"attention {per_us[1]:.1f}, head {per_us[2]:.1f}, token {per_us[3]:.1f}; attention "
+            f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
-    head_flops = 2.0 * c.M * c.d_model * c.V if mlp is None else 2.0 * c.M * mlp[3] * (c.d_model + c.V)
-    out = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "stream-steps/s",
-        "n_gpus": 1,
-        "steps": timed_steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": ("bf16" if bf else "f32") if f8 is None else "bf16 q/o, e4m3 kv",
-        "data": "synthetic (seeded N(0,1) q/K/V, N(0,0.02) head weights; no dataset or checkpoint)",
-        "config": {
-            "workload": c.workload,
-            "streams": c.B, "queries_per_stream": c.Kq, "q_heads": c.H_q, "kv_heads": c.H_kv,
-            "head_dim": c.D, "kv_len": "x".join(str(a) for a in c.kv_len_dist), "block_size": c.block_size,
-            "d_model": c.d_model, "codebook": c.V, "heads": c.G, "decoding": c.mode,
-            "launch": f"decode loop: {n_loop} steps per HIP graph" if graph else "eager",
-            "head": "linear" if mlp is None else "two-layer d->4096->Mish->V",
-            "append": "plain" if rope_pos is None else "rope at logical positions",
-            "kv_cache": "bf16" if f8 is None else "e4m3 + fp32 row scales",
-        },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": "decode_attention",
-            "algorithmic_bytes_per_launch": attn_bytes,
-        },
-        "per_call_us": {("kv_cache_append" if rope_pos is None else "rope_kv_cache_append"): round(per_us[0], 2), "decode_attention": round(per_us[1], 2),
-                        ("codebook_head" if mlp is None else "codebook_head_mlp"): round(per_us[2], 2),
-                        ("spec_verify" if spec is not None else "sample_or_argmax"): round(per_us[3], 2)},
-        "codebook_head_tflops": round(head_flops / (per_us[2] * 1e-6) / 1e12, 2),
-        "cpu_baseline": cpu,
-    }
-    if bf:
-        out["codebook_head_mfma_frac"] = round(head_flops / (per_us[2] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
-    if spec is not None:
-        # verified positions are B*Kq per step; the tokens kept are what the
-        # verification emitted (the same every step: the inputs do not change)
-        emitted = int(num_em.sum().item())
-        out["emitted_tokens_per_s"] = round(emitted / (wall / timed_steps), 1)
-        out["emitted_per_stream"] = round(emitted / c.B, 3)
+        if args.copy_calibration:
+            src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(5):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log("[bench] copy calibration: 5 x 1 GiB device-to-device copies done")
+            del src, dst
+
+        cpu = None
+        if not args.no_cpu_baseline:
+            log("[bench] timing the CPU oracle on all cores, then on one ...")
+            cpu = cpu_baseline(x, args.cpu_streams, args.cpu_seconds)
+            one = cpu_baseline(x, args.cpu_streams, args.cpu_seconds, threads=1)
+            cpu["single_core"] = {"value": one["value"], "cores": one["cores"], "sample": one["sample"]}
+            cpu["host"] = host_info()
+            log(f"[bench] cpu oracle: {cpu['value']:.2f} {cpu['unit']} on {cpu['cores']} threads, "
+                f"{one['value']:.2f} on {one['cores']} ({cpu['host']})")
+
+        head_flops = 2.0 * c.M * c.d_model * c.V if mlp is None else 2.0 * c.M * mlp[3] * (c.d_model + c.V)
+        out = {
+            "metric": METRIC,
+            "value": round(value, 1),
+            "unit": "stream-steps/s",
+            "n_gpus": 1,
+            "steps": timed_steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": ("bf16" if bf else "f32") if f8 is None else "bf16 q/o, e4m3 kv",
+            "data": "synthetic (seeded N(0,1) q/K/V, N(0,0.02) head weights; no dataset or checkpoint)",
+            "config": {
+                "workload": c.workload,
+                "streams": c.B, "queries_per_stream": c.Kq, "q_heads": c.H_q, "kv_heads": c.H_kv,
+                "head_dim": c.D, "kv_len": "x".join(str(a) for a in c.kv_len_dist), "block_size": c.block_size,
+                "d_model": c.d_model, "codebook": c.V, "heads": c.G, "decoding": c.mode,
+                "launch": f"decode loop: {n_loop} steps per HIP graph" if graph else "eager",
+                "head": "linear" if mlp is None else "two-layer d->4096->Mish->V",
+                "append": "plain" if rope_pos is None else "rope at logical positions",
+                "kv_cache": "bf16" if f8 is None else "e4m3 + fp32 row scales",
+            },
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "kernel": "decode_attention",
+                "algorithmic_bytes_per_launch": attn_bytes,
+            },
+            "per_call_us": {("kv_cache_append" if rope_pos is None else "rope_kv_cache_append"): round(per_us[0], 2), "decode_attention": round(per_us[1], 2),
+                            ("codebook_head" if mlp is None else "codebook_head_mlp"): round(per_us[2], 2),
+                            ("spec_verify" if spec is not None else "sample_or_argmax"): round(per_us[3], 2)},
+            "codebook_head_tflops": round(head_flops / (per_us[2] * 1e-6) / 1e12, 2),
+            "cpu_baseline": cpu,
+        }
+        if bf:
+            out["codebook_head_mfma_frac"] = round(head_flops / (per_us[2] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        if spec is not None:
+            # verified positions are B*Kq per step; the tokens kept are what the
+            # verification emitted (the same every step: the inputs do not change)
+            emitted = int(num_em.sum().item())
+            out["emitted_tokens_per_s"] = round(emitted / (wall / timed_steps), 1)
+            out["emitted_per_stream"] = round(emitted / c.B, 3)
+        return out
+
+    out = run_one(args)
+    default_step = (args.workload == DEFAULT_WORKLOAD and args.kv == "bf16" and args.head == "linear"
+                    and args.append == "plain" and args.graph == "off" and not args.copy_calibration)
+    if default_step and not args.no_other_workloads:
+        # the four smaller workloads, eager, after the main measurement: each
+        # one's own step time and attention rate (not part of `value`)
+        import copy
+        others = {}
+        for w in ("c1", "c2", "c3", "c4"):
+            a = copy.copy(args)
+            a.workload, a.no_cpu_baseline = w, True
+            a.steps, a.warmup = min(args.steps, 50), min(args.warmup, 10)
+            torch.cuda.empty_cache()
+            o = run_one(a)
+            keep = {k: o[k] for k in ("value", "unit", "ms_per_step", "steps", "dtype", "per_call_us",
+                                     "codebook_head_tflops", "codebook_head_mfma_frac",
+                                     "emitted_tokens_per_s", "emitted_per_stream") if k in o}
+            keep["attention_hbm_frac"] = o["roofline"]["frac"]
+            others[o["config"]["workload"]] = keep
+        out["other_workloads"] = others
     print(json.dumps(out), flush=True)
 
 

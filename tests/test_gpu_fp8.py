@@ -150,6 +150,56 @@ def test_fp8_attention_many_streams(clm_gpu):
 
 
 
+def _random_fp8_pool(rng, nb, Hk, D, bs):
+    """Uniform E4M3 codes without the two NaN codes, and row scales in
+    [0.002, 0.01] (max|x|/448 for rows of N(0,1) values is about 0.007)."""
+    def codes(shape):
+        c = rng.integers(0, 254, size=shape, dtype=np.uint8)
+        return c + (c >= 0x7F).astype(np.uint8)
+    return (codes((nb, Hk, D // 8, bs, 8)), codes((nb, Hk, D, bs)),
+            rng.uniform(0.002, 0.01, size=(nb, Hk, bs)).astype(np.float32),
+            rng.uniform(0.002, 0.01, size=(nb, Hk, bs)).astype(np.float32))
+
+
+# the oracle's decoder applied once to every code: a lookup table of its values
+_E4M3 = fp8.e4m3_decode(np.arange(256, dtype=np.uint8))
+
+
+def _stream_rows(kc, vc, ks, vs, block_table, b, n, bs):
+    """Stream b's first n positions as dequantized K, V [n, H, D] float64:
+    code value (the oracle's decoder) times the row's scale, as the oracle's
+    dequantize_rows computes it."""
+    pos = np.arange(n)
+    blk = block_table[b, pos // bs]
+    slot = pos % bs
+    H = kc.shape[1]
+    kr = kc[blk, :, :, slot, :].reshape(n, H, -1)                 # [n, H, D]
+    vr = vc[blk, :, :, slot]                                      # [n, H, D]
+    return (_E4M3[kr] * ks[blk, :, slot].astype(np.float64)[..., None],
+            _E4M3[vr] * vs[blk, :, slot].astype(np.float64)[..., None])
+
+
+def test_fp8_attention_full_size(clm_gpu):
+    """The 256-stream launch that the FP8 benchmark times (log-uniform
+    64..8192 keys, 1024-token splits, LDS-staged matrix-core kernel, merge
+    pass) over random E4M3 codes and scales of the pool's shapes: every
+    stream's output against the oracle on the dequantized rows."""
+    x = synth.make_inputs(5)
+    c = x.cfg
+    rng = np.random.default_rng(256)
+    kc, vc, ks, vs = _random_fp8_pool(rng, x.num_blocks, c.H_kv, c.D, c.block_size)
+    scale = 1.0 / math.sqrt(c.D)
+    o = clm_gpu.decode_attention_fp8(to_torch(x.q, bf16=True), dev(kc), dev(vc), dev(ks), dev(vs),
+                                     dev(x.block_table), dev(x.kv_len), int(x.kv_len.max()), scale=scale)
+    q = synth.bf16_bits_to_f32(x.q)
+    ref = np.empty(q.shape, np.float64)
+    for b in range(c.B):                 # one stream at a time keeps the host memory small
+        K, V = _stream_rows(kc, vc, ks, vs, x.block_table, b, int(x.kv_len[b]), c.block_size)
+        ref[b:b + 1] = oracle.decode_attention(q[b:b + 1], [K], [V], x.kv_len[b:b + 1], scale, c.H_kv)
+    err = check_close(bf16_tensor_to_f32(o), ref, "fp8 attention, all 256 streams")
+    print(f"fp8 attention full size: max abs err {err:.3g}")
+
+
 @pytest.mark.parametrize("cfg,bs,D", [(2, 32, 128), (4, 64, 128), (2, 16, 64), (4, 32, 64)])
 def test_fp8_block_sizes(clm_gpu, cfg, bs, D):
     """The FP8 append and attention with pages of 16 to 64 slots and head
