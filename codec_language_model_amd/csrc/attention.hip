@@ -44,6 +44,7 @@
 // on the MFMA units.  Up to kRingMaxB streams, its tiles reach LDS by
 // global-to-LDS DMA into a per-wave ring of kRingStages stages, so three tiles
 // are in flight per wave without holding registers.
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -992,15 +993,15 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(KParams P) {
 }
 
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];   // 0 until queried; calls may come from any host thread
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (!n) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 template <typename T, int D, int NR>

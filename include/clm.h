@@ -414,8 +414,8 @@ int clm_advance_lengths(int32_t* len_before, int32_t* kv_len, int32_t* positions
 /*
  * One decode step per loop iteration, as the calls above would run it:
  *   append (rotary at logical positions when positions != NULL) ->
- *   attention -> head -> token choice (greedy, sampling or speculative
- *   verification) -> clm_advance_lengths.
+ *   attention (score scale 1/sqrt(D)) -> head -> token choice (greedy,
+ *   sampling or speculative verification) -> clm_advance_lengths.
  * Step s (0 <= s < n_steps) reads and writes slice s of each per-step array
  * (base + s * one step's elements).  All pointers are device memory owned by
  * the caller and must stay valid while the loop exists; the graph bakes them
