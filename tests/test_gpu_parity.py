@@ -178,6 +178,75 @@ def test_decode_attention_multi_query_many_streams(clm_gpu):
     check_close(bf16_tensor_to_f32(o)[idx], ref[idx], "6-query attention, 520 streams (sampled)")
 
 
+def _random_pool_case(rng, kv_len, Kq, Hq, Hk, D, bs):
+    """bf16 N(0, 1) keys, values and queries for streams of the given lengths in
+    a shuffled page pool.  Returns the host arrays and the logical per-stream
+    K, V (float32) the oracle reads."""
+    kv_len = np.asarray(kv_len, np.int32)
+    B = kv_len.size
+    pages = (kv_len + bs - 1) // bs
+    nb = int(pages.sum()) + 2
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.zeros((B, int(pages.max())), np.int32)
+    o_ = 0
+    for b in range(B):
+        bt[b, :pages[b]] = perm[o_:o_ + pages[b]]
+        o_ += pages[b]
+    kc = synth.f32_to_bf16_bits(rng.standard_normal((nb, Hk, bs, D), dtype=np.float32))
+    vc = synth.f32_to_bf16_bits(rng.standard_normal((nb, Hk, D, bs), dtype=np.float32))
+    q = synth.f32_to_bf16_bits(rng.standard_normal((B, Kq, Hq, D), dtype=np.float32))
+    kf, vf = synth.bf16_bits_to_f32(kc), synth.bf16_bits_to_f32(vc)
+    keys, vals = [], []
+    for b in range(B):
+        pos = np.arange(int(kv_len[b]))
+        blk, slot = bt[b, pos // bs], pos % bs
+        keys.append(kf[blk, :, slot, :])       # [n, H_kv, D]
+        vals.append(vf[blk, :, :, slot])       # [n, H_kv, D]
+    return kv_len, bt, kc, vc, q, keys, vals
+
+
+def test_decode_attention_max_streams(clm_gpu):
+    """The largest batch a call takes: 4096 streams (B * H_kv = 32768) of 1..48
+    keys, one query each; every stream against the oracle."""
+    rng = np.random.default_rng(4096)
+    Hq, Hk, D, bs = 16, 8, 128, 16
+    kv_len, bt, kc, vc, q, keys, vals = _random_pool_case(rng, rng.integers(1, 49, size=4096), 1, Hq, Hk, D, bs)
+    scale = 1.0 / math.sqrt(D)
+    o = clm_gpu.decode_attention(to_torch(q, bf16=True), to_torch(kc, bf16=True), to_torch(vc, bf16=True),
+                                 to_torch(bt), to_torch(kv_len), int(kv_len.max()), scale=scale)
+    ref = oracle.decode_attention(synth.bf16_bits_to_f32(q), keys, vals, kv_len, scale, Hk)
+    check_close(bf16_tensor_to_f32(o), ref, "attention, 4096 streams")
+
+
+def test_decode_attention_long_context(clm_gpu):
+    """One stream of 100,000 keys next to one of a single key: 98 splits of
+    1024 tokens for the long stream, so the merge pass combines more splits
+    than one wave has lanes (two passes over the split partials)."""
+    rng = np.random.default_rng(100000)
+    Hq, Hk, D, bs = 16, 8, 128, 16
+    kv_len, bt, kc, vc, q, keys, vals = _random_pool_case(rng, [100000, 1], 1, Hq, Hk, D, bs)
+    scale = 1.0 / math.sqrt(D)
+    o = clm_gpu.decode_attention(to_torch(q, bf16=True), to_torch(kc, bf16=True), to_torch(vc, bf16=True),
+                                 to_torch(bt), to_torch(kv_len), 100000, scale=scale)
+    ref = oracle.decode_attention(synth.bf16_bits_to_f32(q), keys, vals, kv_len, scale, Hk)
+    check_close(bf16_tensor_to_f32(o), ref, "attention, 100,000 keys")
+
+
+def test_decode_attention_shortest_blocks(clm_gpu):
+    """6-query causal blocks whose first query sees a single key (kv_len = Kq)
+    and blocks of every length up to two tiles, on the LDS-staged
+    matrix-core kernel."""
+    rng = np.random.default_rng(606)
+    Kq, Hq, Hk, D, bs = 6, 16, 8, 128, 16
+    lens = np.concatenate([np.full(8, Kq), np.arange(Kq, 40)])
+    kv_len, bt, kc, vc, q, keys, vals = _random_pool_case(rng, lens, Kq, Hq, Hk, D, bs)
+    scale = 1.0 / math.sqrt(D)
+    o = clm_gpu.decode_attention(to_torch(q, bf16=True), to_torch(kc, bf16=True), to_torch(vc, bf16=True),
+                                 to_torch(bt), to_torch(kv_len), int(kv_len.max()), scale=scale)
+    ref = oracle.decode_attention(synth.bf16_bits_to_f32(q), keys, vals, kv_len, scale, Hk)
+    check_close(bf16_tensor_to_f32(o), ref, "6-query attention, shortest blocks")
+
+
 @pytest.mark.parametrize("cfg,bs,B,D", [(2, 32, None, 128), (3, 64, 16, 128), (4, 32, None, 128), (4, 128, 12, 128),
                                         (2, 16, None, 64), (4, 16, None, 64), (4, 32, 12, 64)])
 def test_block_sizes(clm_gpu, cfg, bs, B, D):
