@@ -51,21 +51,36 @@ __device__ __forceinline__ float softmax_w(float x, float mx, float c) {
 template <int NT>
 struct Scratch {
   float wf[Blk<NT>::W];
+  float once[3][Blk<NT>::W];
   int wi[Blk<NT>::W];
   float ptot[kMaxPasses];
   int pick, psel;
   float target, total;
 };
 
-template <int NT>
+// The per-wave slots of a block-wide round.  Slot 0 (sc.wf) is reused, so a
+// round on it first waits at a barrier for the previous round's readers;
+// slots 1..3 are each used by at most one round of a kernel and skip that
+// barrier, leaving one barrier per round.
+template <int S, int NT>
+__device__ __forceinline__ float* round_slot(Scratch<NT>& sc) {
+  if constexpr (S == 0) {
+    __syncthreads();
+    return sc.wf;
+  } else {
+    return sc.once[S - 1];
+  }
+}
+
+template <int NT, int S = 0>
 __device__ __forceinline__ float block_max(float x, Scratch<NT>& sc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   x = wave_max(x);
-  __syncthreads();                      // earlier readers of sc.wf are done
-  if (lane == 0) sc.wf[w] = x;
+  float* slot = round_slot<S>(sc);
+  if (lane == 0) slot[w] = x;
   __syncthreads();
-  float r = sc.wf[0];
-  for (int i = 1; i < Blk<NT>::W; ++i) r = fmaxf(r, sc.wf[i]);
+  float r = slot[0];
+  for (int i = 1; i < Blk<NT>::W; ++i) r = fmaxf(r, slot[i]);
   return r;
 }
 
@@ -100,19 +115,19 @@ __device__ __forceinline__ int block_argmax_pair(float bv, int bi, Scratch<NT>& 
 // [start, end) of the running total, and the total.  Lane l's start is
 // computed as the same expression as lane l-1's end (and a wave's base as
 // the previous wave's last end), so consecutive intervals share their bound.
-template <int NT>
+template <int NT, int S = 0>
 __device__ __forceinline__ void block_scan(float s, float& start, float& end, float& tot, Scratch<NT>& sc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float incl = wave_incl_scan(s, lane);
   float prev = __shfl_up(incl, 1, 64);
   if (lane == 0) prev = 0.f;
-  __syncthreads();
-  if (lane == 63) sc.wf[w] = incl;
+  float* slot = round_slot<S>(sc);
+  if (lane == 63) slot[w] = incl;
   __syncthreads();
   float base = 0.f, bw = 0.f;
   for (int i = 0; i < Blk<NT>::W; ++i) {
     if (i == w) bw = base;
-    base += sc.wf[i];
+    base += slot[i];
   }
   start = lane == 0 ? bw : bw + prev;
   end = bw + incl;
@@ -234,57 +249,121 @@ __device__ int block_draw(int n, float u, const WF& wf, float (&e)[kCH], bool ha
   return block_max_int(last, sc);
 }
 
+// block_draw for a row that fits one pass, with e already holding this
+// thread's weights.  Every thread gets the scan total, so each computes the
+// target u*S itself and the round in which one thread publishes it is not
+// needed; the numbers compared and the token chosen are those of block_draw.
+template <int NT, int S>
+__device__ int block_draw_one(float u, const float (&e)[kCH], Scratch<NT>& sc) {
+  const int tid = threadIdx.x;
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < kCH; ++k) s += e[k];
+  if (tid == 0) sc.pick = -1;           // before block_scan's barriers, so before any write below
+  float start, end, tot;
+  block_scan<NT, S>(s, start, end, tot, sc);
+  if (!(tot > 0.f)) return -1;
+  const float tgt = u * tot;
+  if (s > 0.f && start <= tgt && tgt < end) {
+    float run = start;
+    int pick = -1, lastpos = 0;
+#pragma unroll
+    for (int k = 0; k < kCH; ++k) {
+      run += e[k];
+      if (e[k] > 0.f) {
+        lastpos = k;
+        if (pick < 0 && tgt < run) pick = k;
+      }
+    }
+    sc.pick = tid * kCH + (pick < 0 ? lastpos : pick);
+  }
+  __syncthreads();
+  const int pick = sc.pick;
+  if (pick >= 0) return pick;
+  int last = -1;
+#pragma unroll
+  for (int k = 0; k < kCH; ++k)
+    if (e[k] > 0.f) last = tid * kCH + k;
+  return block_max_int(last, sc);
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void sample_kernel(SampleArgs P) {
   constexpr int kPass = Blk<NT>::PASS;
   __shared__ Scratch<NT> sc;
   const int r = blockIdx.x;
   const float* __restrict__ x = P.logits + (size_t)r * P.ld;
+  const bool one = P.V <= kPass;
+  const int t0 = threadIdx.x * kCH;
+  // a row of one pass is loaded before its length and temperature arrive
+  // (the row is readable up to V), so the call costs one round trip
+  float v[kCH];
+  if (one) load16(x, t0, P.V, v, -INFINITY);
   const int n = P.vocab_valid ? clampi(P.vocab_valid[r], 1, P.V) : P.V;
   const float T = P.temperature ? P.temperature[r] : 0.f;
+  if (one) {
+#pragma unroll
+    for (int k = 0; k < kCH; ++k)
+      if (t0 + k >= n) v[k] = -INFINITY;
+  }
   int tok;
   if (!(T > 0.f)) {
-    tok = row_argmax(x, n, sc);
+    if (one) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int k = 0; k < kCH; ++k)
+        if (v[k] > bv) { bv = v[k]; bi = t0 + k; }   // increasing index: first occurrence wins
+      tok = block_argmax_pair(bv, bi, sc);
+      if (tok == 0x7fffffff) tok = 0;
+    } else {
+      tok = row_argmax(x, n, sc);
+    }
   } else {
-    // row maximum; a row of one pass keeps its logits in registers
-    float v[kCH], e[kCH];
+    float e[kCH];
     float mx = -INFINITY;
-    const bool one = n <= kPass;
-    for (int i0 = threadIdx.x * kCH; i0 < n; i0 += kPass) {
-      load16(x, i0, n, v, -INFINITY);
+    if (one) {
 #pragma unroll
       for (int k = 0; k < kCH; ++k) mx = fmaxf(mx, v[k]);
+    } else {
+      for (int i0 = t0; i0 < n; i0 += kPass) {
+        float y[kCH];
+        load16(x, i0, n, y, -INFINITY);
+#pragma unroll
+        for (int k = 0; k < kCH; ++k) mx = fmaxf(mx, y[k]);
+      }
     }
-    mx = block_max(mx, sc);
+    mx = block_max<NT, 1>(mx, sc);
     const float c = softmax_c(T);
     const float u = P.uniforms[r];
-    auto wf = [&](int i0, float (&w)[kCH]) {
-      float y[kCH];
-      load16(x, i0, n, y, 0.f);
-#pragma unroll
-      for (int k = 0; k < kCH; ++k) w[k] = i0 + k < n ? softmax_w(y[k], mx, c) : 0.f;
-    };
     if (one) {
-      const int i0 = threadIdx.x * kCH;
 #pragma unroll
-      for (int k = 0; k < kCH; ++k) e[k] = i0 + k < n ? softmax_w(v[k], mx, c) : 0.f;
+      for (int k = 0; k < kCH; ++k) e[k] = t0 + k < n ? softmax_w(v[k], mx, c) : 0.f;
+      tok = block_draw_one<NT, 2>(u, e, sc);
+    } else {
+      auto wf = [&](int i0, float (&w)[kCH]) {
+        float y[kCH];
+        load16(x, i0, n, y, 0.f);
+#pragma unroll
+        for (int k = 0; k < kCH; ++k) w[k] = i0 + k < n ? softmax_w(y[k], mx, c) : 0.f;
+      };
+      tok = block_draw(n, u, wf, e, false, sc);
     }
-    tok = block_draw(n, u, wf, e, one, sc);
     if (tok < 0) tok = 0;
   }
   if (threadIdx.x == 0) P.tokens[r] = tok;
 }
 
 // Sum over the block, combined in a fixed order (waves in index order).
-template <int NT>
+template <int NT, int S = 0>
 __device__ __forceinline__ float block_sum(float x, Scratch<NT>& sc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   x = wave_sum(x);
+  float* slot = round_slot<S>(sc);
+  if (lane == 0) slot[w] = x;
   __syncthreads();
-  if (lane == 0) sc.wf[w] = x;
-  __syncthreads();
-  float r = sc.wf[0];
-  for (int i = 1; i < Blk<NT>::W; ++i) r += sc.wf[i];
+  float r = slot[0];
+  for (int i = 1; i < Blk<NT>::W; ++i) r += slot[i];
   return r;
 }
 
@@ -300,7 +379,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void verify_rows_kernel(VerifyArgs P) {
   constexpr int kPass = Blk<NT>::PASS;
   __shared__ Scratch<NT> sc;
-  __shared__ float s_px;
+  __shared__ float s_xq[2];
   const int V = P.V, K = P.K;
   const int TK = K + P.bonus;
   const int b = blockIdx.x / TK, i = blockIdx.x - b * TK;
@@ -309,30 +388,41 @@ __global__ __launch_bounds__(NT) void verify_rows_kernel(VerifyArgs P) {
   const bool draft_row = i < K;
   const size_t drow = (size_t)b * K + (draft_row ? i : 0);
   const float* __restrict__ q = P.draft_probs + drow * V;
-  // every load the row needs is issued up front: the drafted token and its
-  // draft probability, the uniforms, the row itself and (one-pass rows) the
-  // draft row, so the row costs one round trip to memory
+  const bool one = V <= kPass;
+  const bool sampled = T > 0.f;
+  const int t0 = threadIdx.x * kCH;
+  // A sampled row of one pass issues all its loads at once - the row, the
+  // draft row, the drafted token and the uniforms - and takes the drafted
+  // entry's logit and draft probability from the registers of the thread
+  // that holds them, so the row costs one round trip to memory.
+  float v[kCH], qv[kCH], e[kCH];
+  if (sampled && one) {
+    load16(x, t0, V, v, -INFINITY);
+    if (draft_row) load16(q, t0, V, qv, 0.f);
+  }
   const int xt = draft_row ? clampi(P.draft_tokens[drow], 0, V - 1) : 0;
-  const float qx = draft_row ? q[xt] : 0.f;
   const float ua = draft_row ? P.u_accept[drow] : 0.f;
   const float ur = P.u_resample[b];
   int result;
-  if (!(T > 0.f)) {
+  if (!sampled) {
+    const float qx = draft_row ? q[xt] : 0.f;
     const int amax = row_argmax(x, V, sc);
     result = (draft_row && qx > 0.f && xt == amax) ? xt : -(amax + 2);
   } else {
-    const bool one = V <= kPass;
-    const int t0 = threadIdx.x * kCH;
-    float v[kCH], qv[kCH], e[kCH];
-    float xx = 0.f;
-    if (draft_row && threadIdx.x == 0) xx = x[xt];
-    float mx = -INFINITY;
+    float mx = -INFINITY, xx = 0.f, qx = 0.f;
     if (one) {
-      load16(x, t0, V, v, -INFINITY);
-      if (draft_row) load16(q, t0, V, qv, 0.f);
 #pragma unroll
       for (int k = 0; k < kCH; ++k) mx = fmaxf(mx, v[k]);
+      if (draft_row && xt / kCH == (int)threadIdx.x) {
+        float a = 0.f, bq = 0.f;
+#pragma unroll
+        for (int k = 0; k < kCH; ++k)
+          if (t0 + k == xt) { a = v[k]; bq = qv[k]; }
+        s_xq[0] = a;
+        s_xq[1] = bq;
+      }
     } else {
+      if (draft_row) { xx = x[xt]; qx = q[xt]; }
       for (int i0 = t0; i0 < V; i0 += kPass) {
         float y[kCH];
         load16(x, i0, V, y, -INFINITY);
@@ -340,7 +430,8 @@ __global__ __launch_bounds__(NT) void verify_rows_kernel(VerifyArgs P) {
         for (int k = 0; k < kCH; ++k) mx = fmaxf(mx, y[k]);
       }
     }
-    mx = block_max(mx, sc);
+    mx = block_max<NT, 1>(mx, sc);        // its barrier also publishes s_xq
+    if (one && draft_row) { xx = s_xq[0]; qx = s_xq[1]; }
     const float c = softmax_c(T);
     float part = 0.f;
     if (one) {
@@ -354,47 +445,44 @@ __global__ __launch_bounds__(NT) void verify_rows_kernel(VerifyArgs P) {
         for (int k = 0; k < kCH; ++k) part += i0 + k < V ? softmax_w(y[k], mx, c) : 0.f;
       }
     }
-    const float S = block_sum(part, sc);
+    const float S = block_sum<NT, 2>(part, sc);
     const float inv_s = 1.f / S;
-    bool accept = false;
-    if (draft_row) {
-      if (threadIdx.x == 0) s_px = softmax_w(xx, mx, c) / S;
-      __syncthreads();
-      accept = qx > 0.f && ua < s_px / qx;
-    }
+    // every thread evaluates the accept test on the same numbers
+    const bool accept = draft_row && qx > 0.f && ua < (softmax_w(xx, mx, c) / S) / qx;
     if (accept) {
       result = xt;
     } else {
-      // target weights p = e / S; residual weights max(p - q, 0)
-      auto target = [&](int i0, float (&wgt)[kCH]) {
-        float y[kCH];
-        load16(x, i0, V, y, 0.f);
-#pragma unroll
-        for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? softmax_w(y[k], mx, c) * inv_s : 0.f;
-      };
-      auto resid = [&](int i0, float (&wgt)[kCH]) {
-        float y[kCH], z[kCH];
-        load16(x, i0, V, y, 0.f);
-        load16(q, i0, V, z, 0.f);
-#pragma unroll
-        for (int k = 0; k < kCH; ++k)
-          wgt[k] = i0 + k < V ? fmaxf(softmax_w(y[k], mx, c) * inv_s - z[k], 0.f) : 0.f;
-      };
       int tok = -1;
-      if (draft_row) {
-        if (one) {
+      if (one) {
+        // residual weights max(p - q, 0), p = e / S; from p if all are zero
+        if (draft_row) {
 #pragma unroll
           for (int k = 0; k < kCH; ++k)
             e[k] = t0 + k < V ? fmaxf(softmax_w(v[k], mx, c) * inv_s - qv[k], 0.f) : 0.f;
+          tok = block_draw_one<NT, 3>(ur, e, sc);
         }
-        tok = block_draw(V, ur, resid, e, one, sc);
-      }
-      if (tok < 0) {
-        if (one) {
+        if (tok < 0) {
 #pragma unroll
           for (int k = 0; k < kCH; ++k) e[k] = t0 + k < V ? softmax_w(v[k], mx, c) * inv_s : 0.f;
+          tok = block_draw_one<NT, 0>(ur, e, sc);
         }
-        tok = block_draw(V, ur, target, e, one, sc);
+      } else {
+        auto target = [&](int i0, float (&wgt)[kCH]) {
+          float y[kCH];
+          load16(x, i0, V, y, 0.f);
+#pragma unroll
+          for (int k = 0; k < kCH; ++k) wgt[k] = i0 + k < V ? softmax_w(y[k], mx, c) * inv_s : 0.f;
+        };
+        auto resid = [&](int i0, float (&wgt)[kCH]) {
+          float y[kCH], z[kCH];
+          load16(x, i0, V, y, 0.f);
+          load16(q, i0, V, z, 0.f);
+#pragma unroll
+          for (int k = 0; k < kCH; ++k)
+            wgt[k] = i0 + k < V ? fmaxf(softmax_w(y[k], mx, c) * inv_s - z[k], 0.f) : 0.f;
+        };
+        if (draft_row) tok = block_draw(V, ur, resid, e, false, sc);
+        if (tok < 0) tok = block_draw(V, ur, target, e, false, sc);
       }
       result = -((tok < 0 ? 0 : tok) + 2);
     }
