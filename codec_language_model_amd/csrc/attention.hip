@@ -178,11 +178,42 @@ __device__ __forceinline__ int find_stream(const int* s, int B, int u) {
 
 // The streams whose last split is shorter than `split`, ordered by that
 // split's length bin (1..16, 16 = longest) descending, then by stream index:
-// s[0..n).  A counting sort with one block-wide scan per bin, so every
-// workgroup builds the same list.  bin(b) = 0 means no short split.  Returns n.
+// s[0..n).  A counting sort (ballots per bin up to one stream per thread,
+// else one block-wide scan per bin), so every workgroup builds the same list.
+// bin(b) = 0 means no short split.  Returns n.
 template <class F>
 __device__ int short_splits_sorted(int* s, int (*s_bins)[16], int B, F bin) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (B <= kThreads) {
+    // one stream per thread: per bin, one ballot gives the wave's count and
+    // each lane's rank among the wave's lanes in that bin (lanes in stream
+    // order), so the list comes out of one barrier and no scans
+    const int t = tid < B ? bin(tid) : 0;
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    int rank = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(t == 16 - k);
+      if (lane == 0) s_bins[w][k] = __popcll(m);
+      if (t == 16 - k) rank = __popcll(m & below);
+    }
+    __syncthreads();
+    int total = 0, pos = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      int tot = 0, before = 0;
+      for (int i = 0; i < kWaves; ++i) {
+        const int c = s_bins[i][k];
+        before += i < w ? c : 0;
+        tot += c;
+      }
+      if (t == 16 - k) pos = total + before + rank;
+      total += tot;
+    }
+    if (t > 0) s[pos] = tid;
+    __syncthreads();
+    return total;
+  }
   const int per = (B + kThreads - 1) / kThreads;
   const int b0 = tid * per;
   int cnt[16];

@@ -22,25 +22,37 @@ bool plan_decode_attention(int B, int Kq, int H_q, int H_kv, int D, int max_kv_l
   if (nr > 16) return false;
   p->nr = nr;
   p->nr_tmpl = nr <= 1 ? 1 : nr <= 2 ? 2 : nr <= 4 ? 4 : nr <= 8 ? 8 : nr <= 12 ? 12 : 16;
-  // Split length: the largest power of two <= (expected token-heads / c),
-  // clamped to [64, 1024] tokens, taking lengths to average half the maximum;
-  // c = 512, or 256 for blocks of more than 2 query rows (the matrix-core
-  // kernel, whose tiles cost more per token).  Long splits cost less per
-  // token (fewer partial results, fewer pipeline restarts); short ones keep
-  // small batches spread over the CUs.  Measured on MI355X: 256 streams x
-  // log-uniform 64..8192 keys run 8% faster at 1024 than at 256 tokens, 64
-  // streams x 200..3000 keys 25% faster at 512-1024, 16 streams x 100..1500
-  // keys best at 128, and 32 streams x 6-query blocks over 300..2000 keys
-  // best at 512.  An item then spans at most 64 blocks of 16 tokens (one
-  // block id per lane).
-  // The matrix-core kernel stops at 512: its items carry 3..16 query rows,
-  // and 32 streams x 6-query blocks over 300..2000 keys took 39.9 us at 512
-  // against 59.8 us at 1024 (a max_kv_len 4.5% larger tipped the rule over).
+  // Split length, taking lengths to average half the maximum (est = expected
+  // token-heads).  Long splits cost less per token (fewer partial results,
+  // fewer pipeline restarts); short ones keep small batches spread over the
+  // CUs.  An item spans at most 64 blocks of 16 tokens (one block id per lane).
+  // 1-2 query rows (vector kernel; FP8 matrix-core kernel): the largest power
+  // of two <= est / 512, clamped to [64, 1024].  Measured on MI355X: 256
+  // streams x log-uniform 64..8192 keys run 8% faster at 1024 than at 256
+  // tokens, 64 streams x 200..3000 keys 25% faster at 512-1024, 16 streams x
+  // 100..1500 keys best at 128.
+  // 3-16 rows (matrix-core kernel, whose tiles cost more per token): the
+  // smallest of 64, 128, 192, 256, 384, 512 at or above est / 768 (about 768
+  // items for the chip).  The coarse steps keep a plan over a range of batch
+  // sizes, so compacting a batch leaves results bit-identical more often
+  // (384 tokens from 26 to 37 streams of up to ~2000 keys).  Blocks of 6
+  // queries, bf16 and FP8 caches, against the earlier power-of-two rule
+  // (est / 256): 32 streams x 300..2000 keys 384 tokens, 35.1 against 36.0 us
+  // (FP8 27.6 against 32.2); 32 x 100..800 keys 192 tokens, 22.5 against
+  // 24.5 us (FP8 20.3 against 22.4); 16 x 300..2000 keys 192 tokens, 24.2
+  // against 24.7 us (FP8 20.2 against 22.4); 8, 64 and 128 streams and 32 x
+  // 2000..8000 keys keep their split.  1024 tokens took 59.8 against 39.9 us
+  // at 512 for 32 x 300..2000 keys.
   const double est = (double)B * H_kv * (max_kv_len > 1 ? max_kv_len / 2.0 : 1.0);
-  const double per = nr > 2 ? 256.0 : 512.0;
-  const long top = nr > 2 ? 512 : 1024;
   long split = 64;
-  while (split < top && (double)(split * 2) * per <= est) split *= 2;
+  if (nr > 2) {
+    const double want = est / 768.0;
+    split = 512;
+    for (int c : {64, 128, 192, 256, 384})
+      if ((double)c >= want) { split = c; break; }
+  } else {
+    while (split < 1024 && (double)(split * 2) * 512.0 <= est) split *= 2;
+  }
   p->split = (int)split;
   p->max_splits = (int)((max_kv_len + split - 1) / split);
   const size_t slots = (size_t)B * H_kv * p->max_splits * p->nr_tmpl;

@@ -634,14 +634,14 @@ def test_append_partitions_bit_identical(clm_gpu):
         np.testing.assert_array_equal(as_bits(d.v_cache), ref_v.view(np.int16), err_msg=str(parts))
 
 
-@pytest.mark.parametrize("cfg,sub", [(5, 100), (4, 24)])
+@pytest.mark.parametrize("cfg,sub", [(5, 100), (4, 28)])
 def test_batch_compaction_bit_identical(clm_gpu, cfg, sub):
     """Dropping streams from a batch (a serving engine compacting finished or
     cancelled streams away) leaves every remaining stream's attention output,
     logits and token bits unchanged.  The attention split length depends on
     streams x KV heads x max_kv_len; it is the same for the full and the
     compacted batch here (1024 tokens for the 256-stream mix and its 100-stream
-    subset, 512 for the 32 x 6-query batch and its 24-stream subset), and the
+    subset, 384 for the 32 x 6-query batch and its 28-stream subset), and the
     head's arithmetic does not depend on the row count.  The subset keeps the
     streams in a shuffled order."""
     import torch
