@@ -160,6 +160,39 @@ def test_workspace_size_query(lib):
     assert f(4096, 1, 16, 32, 128, 100) == 0            # H_q not a multiple of H_kv
 
 
+def _attn_ws(B, Hk, max_splits, nr_tmpl, D):
+    """Bytes of the split partials: (m, l) and D accumulators per (stream, KV
+    head, split, row), each array rounded up to 256 bytes."""
+    slots = B * Hk * max_splits * nr_tmpl
+    up = lambda x: (x + 255) // 256 * 256
+    return up(slots * 2 * 4) + up(slots * D * 4)
+
+
+def test_split_plan_rules(lib):
+    """The split length, read back through the workspace size.  1-2 query rows
+    per KV head: the largest power of two <= est / 512 in [64, 1024], with
+    est = B * H_kv * max_kv_len / 2.  3-16 rows: the smallest of 64, 128,
+    192, 256, 384, 512 at or above est / 768."""
+    f = lib.clm_decode_attention_workspace_size
+    # 256 x 1 query, max 8192: est 8.4 M -> 1024 tokens, 8 splits
+    assert f(256, 1, 16, 8, 128, 8192) == _attn_ws(256, 8, 8, 2, 128)
+    # 16 x 1 query, max 1500: est 96,000 -> 128 tokens, 12 splits
+    assert f(16, 1, 16, 8, 128, 1500) == _attn_ws(16, 8, 12, 2, 128)
+    # 32 x 6 queries (12 rows), max 1965: est 251,520 -> want 327.5 -> 384, 6 splits
+    assert f(32, 6, 16, 8, 128, 1965) == _attn_ws(32, 8, 6, 12, 128)
+    # 26 and 37 streams keep 384 tokens; 25 and 38 do not
+    assert f(26, 6, 16, 8, 128, 1965) == _attn_ws(26, 8, 6, 12, 128)
+    assert f(37, 6, 16, 8, 128, 1965) == _attn_ws(37, 8, 6, 12, 128)
+    assert f(25, 6, 16, 8, 128, 1965) == _attn_ws(25, 8, 8, 12, 128)       # 256 tokens
+    assert f(38, 6, 16, 8, 128, 1965) == _attn_ws(38, 8, 4, 12, 128)       # 512 tokens
+    # 16 x 6 queries, max 2000: want 166.7 -> 192 tokens, 11 splits
+    assert f(16, 6, 16, 8, 128, 2000) == _attn_ws(16, 8, 11, 12, 128)
+    # long streams: 2 streams x 8 KV heads, max 100,000 keys: est 800,000 ->
+    # 1024 tokens, 98 splits; one such stream alone: est 400,000 -> 512, 196
+    assert f(2, 1, 16, 8, 128, 100000) == _attn_ws(2, 8, 98, 2, 128)
+    assert f(1, 1, 16, 8, 128, 100000) == _attn_ws(1, 8, 196, 2, 128)
+
+
 def test_head_workspace_size_queries(lib):
     """Every tile plan of the workloads' shapes runs without scratch (the
     workspace argument is accepted and may be NULL); invalid sizes give 0."""
