@@ -414,6 +414,54 @@ def test_sampler_closed_forms(clm_gpu):
     assert int(t0.cpu()[0]) == 3000
 
 
+@pytest.mark.parametrize("V", [16385, 50000, 100003])
+def test_sampler_rows_longer_than_one_pass(clm_gpu, V):
+    """Vocabularies past one pass of 16,384 entries (2, 4 and 7 passes): every
+    pass is totalled, then the one holding u*S is redone.  Sampled rows at
+    T 0.7 and 1.5 with and without a vocabulary mask, and greedy rows, against
+    the oracle."""
+    rng = np.random.default_rng(V)
+    M = 8
+    logits = (rng.standard_normal((M, V)) * 3.0).astype(np.float32)
+    logits[0, V - 1] = 40.0                       # peaked at the very last entry
+    u = rng.random(M, dtype=np.float32)
+    temp = np.where(np.arange(M) % 2 == 0, 0.7, 1.5).astype(np.float32)
+    vv = np.where(np.arange(M) % 3 == 1, V // 3 + 5, V).astype(np.int32)
+    lt = to_torch(logits)
+    tok = clm_gpu.sample_or_argmax(lt, to_torch(temp), to_torch(u)).cpu().numpy()
+    ex = check_sampled(tok, logits, temp, u, f"sample V={V}")
+    tok = clm_gpu.sample_or_argmax(lt, to_torch(temp), to_torch(u), to_torch(vv)).cpu().numpy()
+    ex += check_sampled(tok, logits, temp, u, f"sample masked V={V}", vocab_valid=vv)
+    greedy = clm_gpu.sample_or_argmax(lt, to_torch(np.zeros(M, np.float32)), to_torch(u), to_torch(vv)).cpu().numpy()
+    ex2 = check_argmax(greedy, logits, f"argmax masked V={V}", vocab_valid=vv)
+    print(f"long rows V={V}: exempt sampled {ex}/{2 * M}, argmax {ex2}/{M}")
+
+
+@pytest.mark.parametrize("T", [0.7, 0.0])
+def test_spec_verify_rows_longer_than_one_pass(clm_gpu, T):
+    """Verification over a 40,000-entry vocabulary (3 passes per row), with and
+    without the bonus row: target rows N(0, 3), draft rows softmax of N(0, 2)
+    logits, drafted tokens drawn from the draft rows."""
+    rng = np.random.default_rng(40000 + int(T * 10))
+    B, K, V = 6, 4, 40000
+    tl = (rng.standard_normal((B, K + 1, V)) * 3.0).astype(np.float32)
+    z = rng.standard_normal((B, K, V)) * 2.0
+    q = np.exp(z - z.max(axis=-1, keepdims=True))
+    q = (q / q.sum(axis=-1, keepdims=True)).astype(np.float32)
+    q64 = q.astype(np.float64)
+    drafts = np.array([[rng.choice(V, p=q64[b, i] / q64[b, i].sum()) for i in range(K)]
+                       for b in range(B)], np.int32)
+    ua = rng.random((B, K), dtype=np.float32)
+    ur = rng.random(B, dtype=np.float32)
+    tl_k = np.ascontiguousarray(tl[:, :K])
+    toks, num = clm_gpu.spec_verify(to_torch(tl_k), to_torch(q), to_torch(drafts), to_torch(ua), to_torch(ur), T)
+    ex = check_verify(toks.cpu().numpy(), num.cpu().numpy(), tl_k, q, drafts, ua, ur, T, f"verify V={V} T={T}")
+    toks, num = clm_gpu.spec_verify_bonus(to_torch(tl), to_torch(q), to_torch(drafts), to_torch(ua), to_torch(ur), T)
+    ex += check_verify(toks.cpu().numpy(), num.cpu().numpy(), tl, q, drafts, ua, ur, T, f"verify bonus V={V} T={T}",
+                       bonus=True)
+    print(f"verify V={V} T={T}: exempt {ex}/{2 * B}")
+
+
 def test_argmax_ties_alignment_and_tails(clm_gpu):
     """Greedy rows whose maximum is planted at two or three positions (the
     lowest must win), rows that are not 16-byte aligned (ld not a multiple of
