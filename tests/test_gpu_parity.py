@@ -462,6 +462,32 @@ def test_spec_verify_rows_longer_than_one_pass(clm_gpu, T):
     print(f"verify V={V} T={T}: exempt {ex}/{2 * B}")
 
 
+@pytest.mark.parametrize("K,V", [(16, 4096), (8, 100), (3, 1)])
+def test_spec_verify_draft_counts_and_small_vocabularies(clm_gpu, K, V):
+    """The most drafts a call takes (16; 15 with the bonus row), a vocabulary
+    shorter than one thread's 16 entries per lane group (100), and a single
+    token (every draft is token 0), at T 0.7 and 0, against the oracle."""
+    rng = np.random.default_rng(K * 1000 + V)
+    B = 5
+    for T in (0.7, 0.0):
+        for bonus in (False, True):
+            k = min(K, 15) if bonus else K
+            tl = (rng.standard_normal((B, k + (1 if bonus else 0), V)) * 2.0).astype(np.float32)
+            z = rng.standard_normal((B, k, V)) * 2.0
+            q64 = np.exp(z - z.max(axis=-1, keepdims=True))
+            q64 /= q64.sum(axis=-1, keepdims=True)
+            q = q64.astype(np.float32)
+            drafts = np.array([[rng.choice(V, p=q64[b, i] / q64[b, i].sum()) for i in range(k)] for b in range(B)],
+                              np.int32)
+            ua = rng.random((B, k), dtype=np.float32)
+            ur = rng.random(B, dtype=np.float32)
+            f = clm_gpu.spec_verify_bonus if bonus else clm_gpu.spec_verify
+            toks, num = f(to_torch(tl), to_torch(q), to_torch(drafts), to_torch(ua), to_torch(ur), T)
+            ex = check_verify(toks.cpu().numpy(), num.cpu().numpy(), tl, q, drafts, ua, ur, T,
+                              f"verify K={k} V={V} T={T} bonus={bonus}", bonus=bonus)
+            print(f"verify K={k} V={V} T={T} bonus={bonus}: exempt {ex}/{B}")
+
+
 def test_argmax_ties_alignment_and_tails(clm_gpu):
     """Greedy rows whose maximum is planted at two or three positions (the
     lowest must win), rows that are not 16-byte aligned (ld not a multiple of
