@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 METRIC = "codec decode steps/s (streams×tokens) and % HBM roofline of KV attention"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (the fp32 workload's GEMV)
 DEFAULT_WORKLOAD = "c5"          # 256 streams, log-uniform 64..8192 keys (the metric's workload)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_c5_traffic.txt")
 ATTN_SRCS = [os.path.join(ROOT, "codec_language_model_amd", "csrc", f) for f in ("attention.hip", "clm_device.h")]
@@ -80,6 +81,9 @@ def parse():
                          "calls (off)")
     ap.add_argument("--graph-steps", type=int, default=16,
                     help="steps per captured decode loop with --graph on")
+    ap.add_argument("--no-copy-check", action="store_true",
+                    help="skip timing a plain 1 GiB device copy after the main measurement (reported as "
+                         "hbm_copy: the box's practical copy bandwidth and attention's share of it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
     ap.add_argument("--measuring-stick", action="store_true",
@@ -93,6 +97,27 @@ def parse():
                     help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-calibration run into the attention traffic record")
     return ap.parse_args()
+
+
+def copy_bandwidth(dev, reps=5):
+    """GB/s (read + write bytes) of a plain 1 GiB device-to-device copy
+    (torch's copy kernel), timed with HIP events on the current stream: the
+    box's practical HBM rate for a streaming copy."""
+    import torch
+    src = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = reps * 2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def attention_bytes(cfg, kv_len, fp8=False):
@@ -441,37 +466,55 @@ def main():
             spec = tuple(dev_t(s[k], False) for k in ("draft_probs", "draft_tokens", "u_accept", "u_resample"))
             out_tok = torch.empty((c.B, c.Kq), dtype=torch.int32, device=dev)
             num_em = torch.empty(c.B, dtype=torch.int32, device=dev)
+        # Input replicas: eager steps rotate over R copies of the KV pool, the
+        # head weights and the logits, so that the bytes a step touches are
+        # at least 512 MiB, twice the 256 MiB Infinity Cache, and every step
+        # reads from HBM as a serving step would.  The 256-stream pool alone
+        # is 1.6 GB (R = 1).  The decode loop captures one set (R = 1).
+        def nbytes(t):
+            return 0 if t is None else t.numel() * t.element_size()
+        kv_set = (k_cache, v_cache) if f8 is None else f8
+        per_set = sum(nbytes(t) for t in kv_set) + nbytes(W) + nbytes(logits) + \
+            (0 if mlp is None else nbytes(mlp[0]) + nbytes(mlp[1]))
+        n_rep = 1 if graph else int(min(8, max(1, -(-(512 << 20) // per_set))))
+        reps = [(kv_set, W, logits, mlp)]
+        for _ in range(n_rep - 1):
+            reps.append((tuple(t.clone() for t in kv_set), W.clone(), torch.empty_like(logits),
+                         None if mlp is None else (mlp[0].clone(), mlp[1].clone(), mlp[2], mlp[3])))
+        rep_i = [0]
         torch.cuda.synchronize()
 
         def step(ev=None):
+            kvs, W_, logits_, mlp_ = reps[rep_i[0] % n_rep]
+            rep_i[0] += 1
             if ev is not None:
                 ev[0].record()
             if f8 is not None:
-                clm.kv_cache_append_fp8(k_new, v_new, *f8, bt, len_before, block_size=c.block_size)
+                clm.kv_cache_append_fp8(k_new, v_new, *kvs, bt, len_before, block_size=c.block_size)
             elif rope_pos is None:
-                clm.kv_cache_append(k_new, v_new, k_cache, v_cache, bt, len_before, block_size=c.block_size)
+                clm.kv_cache_append(k_new, v_new, kvs[0], kvs[1], bt, len_before, block_size=c.block_size)
             else:
-                clm.rope_kv_cache_append(q, k_new, v_new, k_cache, v_cache, bt, len_before, rope_pos, 1.0e6,
+                clm.rope_kv_cache_append(q, k_new, v_new, kvs[0], kvs[1], bt, len_before, rope_pos, 1.0e6,
                                          block_size=c.block_size)
             if ev is not None:
                 ev[1].record()
             if f8 is None:
-                clm.decode_attention(q, k_cache, v_cache, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
+                clm.decode_attention(q, kvs[0], kvs[1], bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
             else:
-                clm.decode_attention_fp8(q, *f8, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
+                clm.decode_attention_fp8(q, *kvs, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
             if ev is not None:
                 ev[2].record()
-            if mlp is None:
-                clm.codebook_head(o.view(c.M, c.d_model), W, head_id, out=logits)
+            if mlp_ is None:
+                clm.codebook_head(o.view(c.M, c.d_model), W_, head_id, out=logits_)
             else:
-                clm.codebook_head_mlp(o.view(c.M, c.d_model), mlp[0], mlp[1], head_id, act=mlp[2], out=logits)
+                clm.codebook_head_mlp(o.view(c.M, c.d_model), mlp_[0], mlp_[1], head_id, act=mlp_[2], out=logits_)
             if ev is not None:
                 ev[3].record()
             if spec is not None:
-                clm.spec_verify(logits.view(c.B, c.Kq, c.V), *spec, c.temperature, out_tokens=out_tok,
+                clm.spec_verify(logits_.view(c.B, c.Kq, c.V), *spec, c.temperature, out_tokens=out_tok,
                                 num_emitted=num_em)
             else:
-                clm.sample_or_argmax(logits, temp, uni, out=tokens)
+                clm.sample_or_argmax(logits_, temp, uni, out=tokens)
             if ev is not None:
                 ev[4].record()
 
@@ -533,10 +576,10 @@ def main():
         for i in range(args.steps):
             step(evs[i])
         torch.cuda.synchronize()
-        per = np.zeros(4)
-        for e in evs:
-            per += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
-        per_us = per / args.steps * 1e3
+        dur = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs]) * 1e3   # [steps, 4] us
+        per_us = dur.mean(axis=0)
+        pct = np.percentile(dur, [10, 50, 90], axis=0)                                          # [3, 4]
+        step_pct = np.percentile(dur.sum(axis=1), [10, 50, 90])
 
         ms_per_step = wall / timed_steps * 1e3
         value = c.B * c.Kq / (wall / timed_steps)
@@ -568,6 +611,21 @@ def main():
                 f"{one['value']:.2f} on {one['cores']} ({cpu['host']})")
 
         head_flops = 2.0 * c.M * c.d_model * c.V if mlp is None else 2.0 * c.M * mlp[3] * (c.d_model + c.V)
+        head_roof = None
+        if mlp is None:
+            # the head's own roofline: min(matrix-core peak, arithmetic intensity x HBM peak),
+            # with W, h and the fp32 logits each moved once
+            e = 2 if bf else 4
+            hb = c.G * c.V * c.d_model * e + c.M * c.d_model * e + c.M * c.V * 4
+            peak = MFMA_BF16_PEAK_TFLOPS if bf else FP32_VECTOR_PEAK_TFLOPS
+            roof = min(peak, head_flops / hb * HBM_PEAK_GBS / 1e3)
+            got = head_flops / (per_us[2] * 1e-6) / 1e12
+            head_roof = {"roofline_tflops": round(roof, 1), "bound": "mfma" if roof == peak else "hbm",
+                         "frac": round(got / roof, 4), "bytes": hb}
+        copy = None
+        if args.copy_check:
+            copy = copy_bandwidth(dev)
+            log(f"[bench] device copy: {copy:.0f} GB/s (read + write bytes); attention at {achieved / copy:.1%} of it")
         out = {
             "metric": METRIC,
             "value": round(value, 1),
@@ -604,7 +662,14 @@ def main():
             "per_call_us": {("kv_cache_append" if rope_pos is None else "rope_kv_cache_append"): round(per_us[0], 2), "decode_attention": round(per_us[1], 2),
                             ("codebook_head" if mlp is None else "codebook_head_mlp"): round(per_us[2], 2),
                             ("spec_verify" if spec is not None else "sample_or_argmax"): round(per_us[3], 2)},
+            "per_call_us_p10_median_p90": {k: [round(float(v), 2) for v in pct[:, i]] for i, k in enumerate(
+                ("append", "decode_attention", "head", "verify" if spec is not None else "token"))},
+            "step_us_p10_median_p90_events": [round(float(v), 2) for v in step_pct],
+            "input_replicas": n_rep,
             "codebook_head_tflops": round(head_flops / (per_us[2] * 1e-6) / 1e12, 2),
+            "codebook_head_roofline": head_roof,
+            "hbm_copy": None if copy is None else {"copy_GBs": round(copy, 1),
+                                                   "attention_frac_of_copy": round(achieved / copy, 4)},
             "cpu_baseline": cpu,
         }
         if bf:
@@ -617,6 +682,7 @@ def main():
             out["emitted_per_stream"] = round(emitted / c.B, 3)
         return out
 
+    args.copy_check = not args.no_copy_check
     out = run_one(args)
     default_step = (args.workload == DEFAULT_WORKLOAD and args.kv == "bf16" and args.head == "linear"
                     and args.append == "plain" and args.graph == "off" and not args.copy_calibration)
@@ -627,12 +693,13 @@ def main():
         others = {}
         for w in ("c1", "c2", "c3", "c4"):
             a = copy.copy(args)
-            a.workload, a.no_cpu_baseline = w, True
+            a.workload, a.no_cpu_baseline, a.copy_check = w, True, False
             a.steps, a.warmup = min(args.steps, 50), min(args.warmup, 10)
             torch.cuda.empty_cache()
             o = run_one(a)
             keep = {k: o[k] for k in ("value", "unit", "ms_per_step", "steps", "dtype", "per_call_us",
-                                     "codebook_head_tflops", "codebook_head_mfma_frac",
+                                     "per_call_us_p10_median_p90", "input_replicas",
+                                     "codebook_head_tflops", "codebook_head_mfma_frac", "codebook_head_roofline",
                                      "emitted_tokens_per_s", "emitted_per_stream") if k in o}
             keep["attention_hbm_frac"] = o["roofline"]["frac"]
             others[o["config"]["workload"]] = keep
