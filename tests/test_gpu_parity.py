@@ -248,13 +248,16 @@ def test_decode_attention_shortest_blocks(clm_gpu):
 
 
 @pytest.mark.parametrize("cfg,bs,B,D", [(2, 32, None, 128), (3, 64, 16, 128), (4, 32, None, 128), (4, 128, 12, 128),
-                                        (2, 16, None, 64), (4, 16, None, 64), (4, 32, 12, 64)])
+                                        (2, 16, None, 64), (4, 16, None, 64), (4, 32, 12, 64),
+                                        (4, 128, 16, 128), (2, 128, 8, 128)])
 def test_block_sizes(clm_gpu, cfg, bs, B, D):
     """Pages of 16 to 128 slots and head widths 128 and 64 (the block-size-
     generic kernels and the D = 64 instantiations): the append bit-exact, then
     attention over the cache it wrote, against the oracle.  Single-query rows
     take the vector kernel; the 6-query blocks the matrix-core kernel with its
-    LDS ring."""
+    LDS ring.  The last two cases start splits inside a page: 192-token
+    splits over 128-slot pages (16 x 6-query blocks) and 64-token splits over
+    128-slot pages (8 single-query streams)."""
     import dataclasses
     c = dataclasses.replace(synth.get_config(cfg), block_size=bs, D=D)
     x = synth.make_inputs(c, B=B)
