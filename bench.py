@@ -90,6 +90,10 @@ def parse():
                     help="no decode step: time hipBLASLt (torch.mm, bf16) on a large square GEMM and on the "
                          "codebook head's shapes, weights rotated over replicas, as the box's practical "
                          "matrix-core ceiling")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="no GPU work: the CPU oracle's time per call (append, attention, head, token choice "
+                         "or verification) and for the chained step, on all five workloads, with every host "
+                         "thread and with one (the CPU baseline protocol); prints a markdown table")
     ap.add_argument("--pmc-table", metavar="COUNTER_CSV",
                     help="no GPU work: per-kernel averages of every counter in a rocprofv3 "
                          "counter_collection.csv")
@@ -357,8 +361,81 @@ def cpu_baseline(x, n_streams, min_seconds, threads=None):
                       f"{reps} repetitions: {dt:.1f} s"}
 
 
+def cpu_baseline_table(reps=3):
+    """The CPU baseline protocol over every workload: the oracle as it stands,
+    one call at a time and chained, one warm-up then `reps` timed runs (the
+    median), with all host threads and with one.  Prints a markdown table."""
+    import contextlib
+
+    import numpy as np
+
+    import oracle
+    synth = _synth()
+    try:
+        import threadpoolctl
+    except ImportError:
+        threadpoolctl = None
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)) * 1e3
+
+    print(f"host: {host_info()}; {reps} timed runs after one warm-up, median ms", flush=True)
+    print("| workload | threads | append | attention | head | token / verify | chained step | stream-steps/s |")
+    print("|---|---|---|---|---|---|---|---|")
+    for i in range(1, 6):
+        x = synth.make_inputs(i)
+        c = x.cfg
+        kp, vp = x.build_pool(include_new=False)
+        keys = [x.logical_k(b) for b in range(c.B)]
+        vals = [x.logical_v(b) for b in range(c.B)]
+        q, W = x.f32(x.q), x.f32(x.W)
+        hid = x.head_id if c.G > 1 else None
+        scale = 1.0 / math.sqrt(c.D)
+        bf = c.dtype == "bf16"
+        temp = np.full(c.M, c.temperature, np.float32) if c.mode == "sample" else None
+        uni = x.uniforms() if c.mode == "sample" else None
+        spec = x.spec_inputs() if c.mode == "spec" else None
+        o = oracle.decode_attention(q, keys, vals, x.kv_len, scale, c.H_kv)
+        h = (oracle.round_to_bf16(o) if bf else o.astype(np.float32)).reshape(c.M, c.H_q * c.D)
+        logits = oracle.codebook_head(h, W, hid).astype(np.float32)
+
+        def token():
+            if spec is not None:
+                oracle.spec_verify(logits.reshape(c.B, c.Kq, c.V), spec["draft_probs"], spec["draft_tokens"],
+                                   spec["u_accept"], spec["u_resample"], c.temperature)
+            else:
+                oracle.sample_or_argmax(logits, temp, uni)
+
+        def chained():
+            t = temp if c.mode == "sample" else (c.temperature if c.mode == "spec" else None)
+            oracle.decode_step(q, keys, vals, x.kv_len, scale, c.H_kv, W, hid, bf, mode=c.mode,
+                               temperature=t, uniforms=uni, spec=spec)
+
+        for threads in (None, 1):
+            limit = (threadpoolctl.threadpool_limits(limits=threads) if threadpoolctl is not None and threads
+                     else contextlib.nullcontext())
+            with limit:
+                t_app = timed(lambda: oracle.kv_cache_append(kp, vp, x.block_table, x.len_before, x.k_new, x.v_new,
+                                                             c.block_size))
+                t_att = timed(lambda: oracle.decode_attention(q, keys, vals, x.kv_len, scale, c.H_kv))
+                t_head = timed(lambda: oracle.codebook_head(h, W, hid))
+                t_tok = timed(token)
+                t_step = timed(chained)
+            print(f"| {c.workload} | {'all' if threads is None else threads} | {t_app:.1f} | {t_att:.1f} | "
+                  f"{t_head:.1f} | {t_tok:.1f} | {t_step:.1f} | {c.B * c.Kq / (t_step * 1e-3):.1f} |", flush=True)
+
+
 def main():
     args = parse()
+    if args.cpu_table:
+        cpu_baseline_table()
+        return
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
         return
