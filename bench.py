@@ -79,6 +79,8 @@ def parse():
                     help="time the steps as launches of the native decode loop - --graph-steps steps "
                          "captured as one HIP graph, lengths advancing on the device (on) - or as eager "
                          "calls (off)")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="KV pages of this many slots instead of the workload's 16 (a multiple of 16, <= 128)")
     ap.add_argument("--graph-steps", type=int, default=16,
                     help="steps per captured decode loop with --graph on")
     ap.add_argument("--no-copy-check", action="store_true",
@@ -468,6 +470,9 @@ def main():
     def run_one(args):
         """One workload: draw inputs, time the steps, return the JSON object."""
         cfg = synth.get_config(args.workload)
+        if args.block_size:
+            import dataclasses
+            cfg = dataclasses.replace(cfg, block_size=args.block_size)
         graph = args.graph == "on"
         if graph and (args.kv != "bf16" or args.head != "linear"):
             print("--graph on runs the decode loop of the bf16/fp32 cache and the linear head", file=sys.stderr)
@@ -576,7 +581,8 @@ def main():
             if ev is not None:
                 ev[1].record()
             if f8 is None:
-                clm.decode_attention(q, kvs[0], kvs[1], bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
+                clm.decode_attention(q, kvs[0], kvs[1], bt, kv_len, max_kv, scale=scale, out=o, workspace=ws,
+                                     block_size=c.block_size)
             else:
                 clm.decode_attention_fp8(q, *kvs, bt, kv_len, max_kv, scale=scale, out=o, workspace=ws)
             if ev is not None:

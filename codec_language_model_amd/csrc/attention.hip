@@ -136,6 +136,17 @@ struct KParams {
   float scale_log2;
 };
 
+// Values are stored [D][bs] inside a block, so a 16-token tile reads 16 of a
+// head dimension's bs slots.  With 16-slot pages that is the whole row and
+// the load streams (non-temporal); with longer pages the rest of each line
+// belongs to the item's next tiles, so it is loaded with the default policy
+// and stays in L2 for them.
+template <int BS, class V>
+__device__ __forceinline__ V ld_values(const V* p) {
+  if constexpr (BS == 16) return ld_nt(p);
+  else return *p;
+}
+
 __device__ __forceinline__ int stream_len(int len, const KParams& P) { return clampi(len, 1, P.cap); }
 __device__ __forceinline__ int full_splits(int n, const KParams& P) { return min(n / P.split, P.max_splits); }
 __device__ __forceinline__ int split_count(int n, const KParams& P) {
@@ -399,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(KParams P) {
           kr[i][cc] = ld_nt(reinterpret_cast<const uint4*>(kp + i * D + cc * LPR * VE));
 #pragma unroll
       for (int jj = 0; jj < DPL; ++jj)
-        vr[jj] = ld_nt(reinterpret_cast<const VT*>(vp + (size_t)jj * LPR * bs));
+        vr[jj] = ld_values<BS>(reinterpret_cast<const VT*>(vp + (size_t)jj * LPR * bs));
     };
 
     // P.V for one tile; MASK zeroes value lanes of keys past `vis` (slots
@@ -736,7 +747,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
 #pragma unroll
         for (int k = 0; k < NS; ++k) kr[k] = ld_nt(reinterpret_cast<const uint2*>(kg + (size_t)32 * k * bs));
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) vr[j] = ld_nt(reinterpret_cast<const uint32_t*>(vp + (size_t)16 * j * bs));
+        for (int j = 0; j < NJ; ++j) vr[j] = ld_values<BS>(reinterpret_cast<const uint32_t*>(vp + (size_t)16 * j * bs));
         ks = *reinterpret_cast<const float4*>(P.k_scale + hb * bs + slot0 + 4 * lg);
         vs = *reinterpret_cast<const float4*>(P.v_scale + hb * bs + slot0 + 4 * lg);
       } else {
@@ -746,7 +757,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(KParams P) {
           kr[k] = __builtin_bit_cast(bf16x8_t, w);
         }
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) vr[j] = ld_nt(reinterpret_cast<const uint2*>(vp + (size_t)16 * j * bs));
+        for (int j = 0; j < NJ; ++j) vr[j] = ld_values<BS>(reinterpret_cast<const uint2*>(vp + (size_t)16 * j * bs));
       }
     };
 
