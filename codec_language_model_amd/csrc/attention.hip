@@ -988,6 +988,40 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(KParams P) {
   if (ns <= 1) return;
   const size_t base = (size_t)bh * P.max_splits * NR + r;
 
+  const int j = r / P.G, gi = r - (r / P.G) * P.G;
+  T* orow = static_cast<T*>(P.o) + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D;
+  if (ns <= 16) {
+    // every split's (m, l) and accumulator loads issued together: one round
+    // trip; the same arithmetic, in the same order, as the general form below
+    const float mi = lane < ns ? P.part_ml[2 * (base + (size_t)lane * NR)] : kNegBig;
+    const float li = lane < ns ? P.part_ml[2 * (base + (size_t)lane * NR) + 1] : 0.f;
+    float v[16][DL];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float* a = P.part_acc + (base + (size_t)min(k, ns - 1) * NR) * D + lane;
+#pragma unroll
+      for (int e = 0; e < DL; ++e) v[k][e] = a[64 * e];
+    }
+    const float M = fmaxf(kNegBig, wave_max(mi));
+    const float f = lane < ns ? __builtin_amdgcn_exp2f(mi - M) : 0.f;
+    const float L = 0.f + wave_sum(f * li);
+    float A[DL];
+#pragma unroll
+    for (int e = 0; e < DL; ++e) A[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float fk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), k));
+      if (k < ns) {
+#pragma unroll
+        for (int e = 0; e < DL; ++e) A[e] = fmaf(fk, v[k][e], A[e]);
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) store_out(orow + lane + 64 * e, A[e] * inv);
+    return;
+  }
+
   // (m, l) of up to 64 splits per lane-parallel pass; accumulators in
   // batches of 16 splits whose loads are all issued before any is used
   float M = kNegBig;
@@ -1027,8 +1061,6 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(KParams P) {
       }
     }
   }
-  const int j = r / P.G, gi = r - (r / P.G) * P.G;
-  T* orow = static_cast<T*>(P.o) + ((size_t)(b * P.Kq + j) * P.H_q + h * P.G + gi) * D;
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
   for (int e = 0; e < DL; ++e) store_out(orow + lane + 64 * e, A[e] * inv);
