@@ -53,11 +53,15 @@ def log(*a):
 
 def parse():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gpus", type=int, default=1,
+                    help="GPUs (1 only: the step runs on one GPU; more exits with a message)")
+    ap.add_argument("--steps", type=int, default=100, help="timed steps")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps before them")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="c1 (1 stream, fp32), c2 (16 streams, sampling), c3 (64 streams, 3 stage heads), "
+                         "c4 (32 x 6-query speculative verification) or c5 (256 streams, the default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle (cpu_baseline is then null)")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="time only the chosen workload (by default the 256-stream step is followed by "
                          "short eager runs of the four smaller workloads, reported under other_workloads; "
