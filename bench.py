@@ -478,8 +478,11 @@ def main():
             import dataclasses
             cfg = dataclasses.replace(cfg, block_size=args.block_size)
         graph = args.graph == "on"
-        if graph and (args.kv != "bf16" or args.head != "linear"):
-            print("--graph on runs the decode loop of the bf16/fp32 cache and the linear head", file=sys.stderr)
+        if graph and args.head != "linear":
+            print("--graph on runs the decode loop of the linear head", file=sys.stderr)
+            sys.exit(2)
+        if args.kv == "fp8" and args.append == "rope":
+            print("--append rope has no FP8 form (the rotary append writes bf16 or fp32 rows)", file=sys.stderr)
             sys.exit(2)
         t_gen = time.perf_counter()
         x = synth.make_inputs(cfg)
@@ -619,7 +622,9 @@ def main():
         if graph:
             rep = lambda t: t.unsqueeze(0).expand((n_loop,) + tuple(t.shape)).contiguous()
             lg_all = torch.empty((n_loop, c.M, c.V), dtype=torch.float32, device=dev)
-            lp = dict(k_cache=k_cache, v_cache=v_cache, block_table=bt, len_before=len_before, kv_len=kv_len,
+            kv_args = dict(k_cache=k_cache, v_cache=v_cache) if f8 is None else \
+                dict(k_cache=f8[0], v_cache=f8[1], k_scale=f8[2], v_scale=f8[3])
+            lp = dict(**kv_args, block_table=bt, len_before=len_before, kv_len=kv_len,
                       max_kv_len=max_kv, k_new=rep(k_new), v_new=rep(v_new), q=rep(q), W=W, head_id=head_id,
                       o=torch.empty_like(rep(q)), logits=lg_all, mode=c.mode, attn_workspace=ws,
                       block_size=c.block_size)

@@ -499,6 +499,10 @@ class DecodeLoop:
     u_accept, out_tokens [n, B, Kq]; u_resample, num_emitted [n, B].  The
     cache, block table, lengths (and positions) are as for the single
     calls; the lengths and positions advance on the device after each step.
+    With k_scale / v_scale the cache is FP8 (E4M3) as for
+    kv_cache_append_fp8 (uint8 k_cache [nb, H_kv, D/8, bs, 8], v_cache [nb,
+    H_kv, D, bs], float32 scales [nb, H_kv, bs]); q, k_new and v_new are then
+    bf16, an attention workspace is required and positions are not taken.
     mode: "greedy", "sample" or "spec".  Every tensor must stay alive while
     the loop exists (this object keeps references); launch() enqueues all
     n_steps steps on torch's current stream."""
@@ -509,7 +513,7 @@ class DecodeLoop:
                  logits, head_id=None, positions=None, rope_base=1.0e6, mode="greedy", tokens=None,
                  temperature=None, uniforms=None, spec_temperature=0.0, draft_probs=None, draft_tokens=None,
                  u_accept=None, u_resample=None, out_tokens=None, num_emitted=None, attn_workspace=None,
-                 block_size=16):
+                 block_size=16, k_scale=None, v_scale=None):
         torch = _torch()
         self._lib = load()
         self._h = None
@@ -523,8 +527,18 @@ class DecodeLoop:
         _cuda("q", q, dt, 5)
         _out("o", o, q.shape, dt)
         nb = k_cache.shape[0]
-        _out("k_cache", k_cache, (nb, H_kv, block_size, D), dt)
-        _out("v_cache", v_cache, (nb, H_kv, D, block_size), dt)
+        if (k_scale is None) != (v_scale is None):
+            raise ValueError("DecodeLoop: k_scale and v_scale go together")
+        if k_scale is not None:
+            if dt != torch.bfloat16 or D % 8:
+                raise ValueError("DecodeLoop: an FP8 cache takes bf16 queries and rows, D a multiple of 8")
+            _out("k_cache", k_cache, (nb, H_kv, D // 8, block_size, 8), torch.uint8)
+            _out("v_cache", v_cache, (nb, H_kv, D, block_size), torch.uint8)
+            _out("k_scale", k_scale, (nb, H_kv, block_size), torch.float32)
+            _out("v_scale", v_scale, (nb, H_kv, block_size), torch.float32)
+        else:
+            _out("k_cache", k_cache, (nb, H_kv, block_size, D), dt)
+            _out("v_cache", v_cache, (nb, H_kv, D, block_size), dt)
         _cuda("block_table", block_table, torch.int32, 2)
         if block_table.shape[0] != B:
             raise ValueError("DecodeLoop: block_table rows")
@@ -560,7 +574,7 @@ class DecodeLoop:
         self._warr = (C.c_void_p * G)(*[w.data_ptr() for w in Ws])
         self._keep = [k_cache, v_cache, block_table, len_before, kv_len, positions, k_new, v_new, q, Ws, head_id,
                       o, logits, tokens, temperature, uniforms, draft_probs, draft_tokens, u_accept, u_resample,
-                      out_tokens, num_emitted, attn_workspace]
+                      out_tokens, num_emitted, attn_workspace, k_scale, v_scale]
         p = lambda t: 0 if t is None else t.data_ptr()
         d = _lib.DecodeStepDesc(
             B=B, Kq=Kq, H_q=H_q, H_kv=H_kv, D=D, block_size=block_size, num_blocks=nb,
@@ -571,7 +585,8 @@ class DecodeLoop:
             attn_workspace=p(attn_workspace), attn_workspace_bytes=_nbytes(attn_workspace),
             mode=self._MODES[mode], temperature=p(temperature), uniforms=p(uniforms), tokens=p(tokens),
             spec_temperature=float(spec_temperature), draft_probs=p(draft_probs), draft_tokens=p(draft_tokens),
-            u_accept=p(u_accept), u_resample=p(u_resample), out_tokens=p(out_tokens), num_emitted=p(num_emitted))
+            u_accept=p(u_accept), u_resample=p(u_resample), out_tokens=p(out_tokens), num_emitted=p(num_emitted),
+            k_scale=p(k_scale), v_scale=p(v_scale))
         h = C.c_void_p()
         _check("clm_decode_loop_create", self._lib.clm_decode_loop_create(C.byref(d), n, C.byref(h)))
         self._h = h

@@ -69,7 +69,7 @@ const char* clm_status_string(int status) {
   return "CLM_ERR_UNKNOWN";
 }
 
-int clm_version(void) { return 200; }
+int clm_version(void) { return 300; }
 
 int clm_set_checked(int on) { return g_checked_flag.exchange(on ? 1 : 0) ; }
 

@@ -43,8 +43,12 @@ int record_step(const clm_decode_step_desc& d, int s, hipStream_t st) {
   void* q = step_ptr(d.q, s, q_step);
   const void* kn = step_ptr(d.k_new, s, kv_step);
   const void* vn = step_ptr(d.v_new, s, kv_step);
+  const bool f8 = d.k_scale != nullptr;
   int rc;
-  if (d.positions)
+  if (f8)
+    rc = clm_kv_cache_append_fp8(kn, vn, d.k_cache, d.v_cache, d.k_scale, d.v_scale, d.block_table, d.max_blocks,
+                                 d.len_before, d.B, d.Kq, d.H_kv, d.D, d.block_size, d.num_blocks, st);
+  else if (d.positions)
     rc = clm_rope_kv_cache_append(q, kn, vn, d.k_cache, d.v_cache, d.block_table, d.max_blocks, d.len_before,
                                   d.positions, d.rope_base, d.B, d.Kq, d.H_q, d.H_kv, d.D, d.block_size,
                                   d.num_blocks, d.dt, st);
@@ -54,7 +58,11 @@ int record_step(const clm_decode_step_desc& d, int s, hipStream_t st) {
   if (rc != CLM_OK) return rc;
   void* o = step_ptr(d.o, s, q_step);
   const float scale = 1.0f / __builtin_sqrtf((float)d.D);
-  if (d.attn_workspace)
+  if (f8)
+    rc = clm_decode_attention_fp8(q, d.k_cache, d.v_cache, d.k_scale, d.v_scale, d.block_table, d.max_blocks,
+                                  d.kv_len, d.max_kv_len, o, d.B, d.Kq, d.H_q, d.H_kv, d.D, d.block_size,
+                                  d.num_blocks, scale, d.attn_workspace, d.attn_workspace_bytes, st);
+  else if (d.attn_workspace)
     rc = clm_decode_attention(q, d.k_cache, d.v_cache, d.block_table, d.max_blocks, d.kv_len, d.max_kv_len, o, d.B,
                               d.Kq, d.H_q, d.H_kv, d.D, d.block_size, d.num_blocks, scale, d.dt, d.attn_workspace,
                               d.attn_workspace_bytes, st);
@@ -99,6 +107,8 @@ int check_desc(const clm_decode_step_desc& d) {
   } else {
     return CLM_ERR_INVALID_ARG;
   }
+  if (!d.k_scale != !d.v_scale) return CLM_ERR_INVALID_ARG;
+  if (d.k_scale && (d.dt != CLM_BF16 || d.positions || !d.attn_workspace)) return CLM_ERR_UNSUPPORTED;
   return CLM_OK;
 }
 

@@ -413,9 +413,11 @@ int clm_advance_lengths(int32_t* len_before, int32_t* kv_len, int32_t* positions
 
 /*
  * One decode step per loop iteration, as the calls above would run it:
- *   append (rotary at logical positions when positions != NULL) ->
- *   attention (score scale 1/sqrt(D)) -> head -> token choice (greedy,
- *   sampling or speculative verification) -> clm_advance_lengths.
+ *   append (rotary at logical positions when positions != NULL; the
+ *   quantizing append when k_scale != NULL) -> attention (score scale
+ *   1/sqrt(D); over the FP8 cache when k_scale != NULL) -> head -> token
+ *   choice (greedy, sampling or speculative verification) ->
+ *   clm_advance_lengths.
  * Step s (0 <= s < n_steps) reads and writes slice s of each per-step array
  * (base + s * one step's elements).  All pointers are device memory owned by
  * the caller and must stay valid while the loop exists; the graph bakes them
@@ -454,6 +456,12 @@ typedef struct clm_decode_step_desc {
   const float* u_resample;          /* mode 2: [n_steps][B] */
   int32_t* out_tokens;              /* mode 2: [n_steps][B, Kq] */
   int32_t* num_emitted;             /* mode 2: [n_steps][B]; the lengths advance by these */
+  float* k_scale;                   /* FP8 (E4M3) cache: the per-row key and value scales */
+  float* v_scale;                   /*   [num_blocks, H_kv, block_size] of clm_kv_cache_append_fp8,
+                                       with k_cache / v_cache in its byte layouts; both NULL for a
+                                       cache of element type dt.  FP8 needs dt = CLM_BF16 and a
+                                       caller attn_workspace; positions must be NULL (UNSUPPORTED
+                                       otherwise: there is no rotary FP8 append) */
 } clm_decode_step_desc;
 
 typedef struct clm_decode_loop clm_decode_loop;   /* opaque */
@@ -465,7 +473,9 @@ typedef struct clm_decode_loop clm_decode_loop;   /* opaque */
  * would validate it, before or during capture; on an error nothing is kept.
  * Checked mode must be off (it synchronises): UNSUPPORTED otherwise.
  * Errors: INVALID_ARG (null desc/loop, n_steps out of range, a null array the
- *   mode needs, mode not 0..2), the individual calls' errors, HIP.
+ *   mode needs, mode not 0..2, one FP8 scale array without the other),
+ *   UNSUPPORTED (an FP8 cache with dt other than CLM_BF16, with positions or
+ *   without attn_workspace), the individual calls' errors, HIP.
  */
 int clm_decode_loop_create(const clm_decode_step_desc* desc, int n_steps, clm_decode_loop** loop);
 

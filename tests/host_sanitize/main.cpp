@@ -116,6 +116,13 @@ int main() {
   d.mode = 2;
   EXPECT(clm_decode_loop_create(&d, 4, &loop), INV);
   d.mode = 0;
+  d.k_scale = F;                                           // FP8 cache: one scale array alone
+  EXPECT(clm_decode_loop_create(&d, 4, &loop), INV);
+  d.v_scale = F;                                           // no caller workspace
+  EXPECT(clm_decode_loop_create(&d, 4, &loop), UNS);
+  d.attn_workspace = P; d.attn_workspace_bytes = 1 << 20;
+  EXPECT(clm_decode_loop_create(&d, 4, &loop), HIP);       // FP8 loop: no device either
+  d.k_scale = d.v_scale = nullptr; d.attn_workspace = nullptr; d.attn_workspace_bytes = 0;
   EXPECT(clm_decode_loop_create(&d, 4, &loop), HIP);       // no device: capture cannot start
   EXPECT((int)(loop == nullptr), 1);
   EXPECT(clm_decode_loop_launch(nullptr, S), INV);

@@ -300,6 +300,16 @@ def test_decode_loop_host_checks(lib):
     d.mode = 7
     assert create(C.byref(d), 4, C.byref(h)) == INVALID
     d.mode = 0
+    d.k_scale = 0x100000                                         # FP8 cache: both scale arrays ...
+    assert create(C.byref(d), 4, C.byref(h)) == INVALID
+    d.v_scale = 0x100000
+    assert create(C.byref(d), 4, C.byref(h)) == UNSUPPORTED      # ... and a caller workspace
+    d.attn_workspace, d.attn_workspace_bytes = 0x100000, 1 << 20
+    d.positions = 0x100000
+    assert create(C.byref(d), 4, C.byref(h)) == UNSUPPORTED      # no rotary FP8 append
+    d.positions, d.dt = 0, 0
+    assert create(C.byref(d), 4, C.byref(h)) == UNSUPPORTED      # bf16 queries only
+    d.dt, d.k_scale, d.v_scale, d.attn_workspace, d.attn_workspace_bytes = 1, 0, 0, 0, 0
     prev = lib.clm_set_checked(1)
     try:
         assert create(C.byref(d), 4, C.byref(h)) == UNSUPPORTED  # checked mode synchronises

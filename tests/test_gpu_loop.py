@@ -220,3 +220,128 @@ def test_loop_grouped_heads_and_fp32(clm_gpu):
     """Three stage heads (64 streams, 3 steps), and the one-stream fp32 step (5 steps)."""
     _loop_case(clm_gpu, 3, 64, 64, 3)
     _loop_case(clm_gpu, 1, 1, 1, 5, replay=True)
+
+
+def _fp8_quantize_pool(kp, vp):
+    """The bf16 pool (keys [nb, H, bs, D], values [nb, H, D, bs]) quantized row
+    by row with the oracle's quantizer into the FP8 cache layouts: keys [nb,
+    H, D/8, bs, 8], values [nb, H, D, bs], scales [nb, H, bs].  Slots holding
+    NaN (never written) become NaN codes with NaN scales."""
+    from oracle import fp8
+    out = []
+    for rows in (synth.bf16_bits_to_f32(kp), synth.bf16_bits_to_f32(vp).transpose(0, 1, 3, 2)):
+        empty = np.isnan(rows).any(axis=-1)
+        codes, sc = fp8.quantize_rows(np.where(empty[..., None], 0.0, rows).astype(np.float32))
+        codes[empty] = 0x7F
+        sc = sc.astype(np.float32)
+        sc[empty] = np.nan
+        out.append((codes, sc))
+    (kc, ks), (vc, vs) = out
+    nb, H, bs, D = kc.shape
+    kc = np.ascontiguousarray(kc.reshape(nb, H, bs, D // 8, 8).transpose(0, 1, 3, 2, 4))
+    return kc, np.ascontiguousarray(vc.transpose(0, 1, 3, 2)), ks, vs
+
+
+def _fp8_stream_rows(kc, vc, ks, vs, bt, b, n, bs):
+    """Stream b's first n positions of the FP8 pool, dequantized by the oracle:
+    K, V [n, H, D] (pages gathered at once rather than slot by slot)."""
+    from oracle import fp8
+    nb, H, G8, _, _ = kc.shape
+    D = G8 * 8
+    pages = bt[b, :(n + bs - 1) // bs]
+    kcodes = kc[pages].transpose(0, 3, 1, 2, 4).reshape(-1, H, D)[:n]      # [pos, H, D]
+    vcodes = vc[pages].transpose(0, 3, 1, 2).reshape(-1, H, D)[:n]
+    ksc = ks[pages].transpose(0, 2, 1).reshape(-1, H)[:n]
+    vsc = vs[pages].transpose(0, 2, 1).reshape(-1, H)[:n]
+    return fp8.dequantize_rows(kcodes, ksc), fp8.dequantize_rows(vcodes, vsc)
+
+
+def _fp8_loop_case(clm_gpu, cfg, B_live, n_steps):
+    """The loop over an FP8 (E4M3) cache: every step's quantizing append
+    against the oracle's quantizer (the whole cache bit for bit at the end),
+    attention, logits and tokens against the oracle on the dequantized rows,
+    following the oracle's own decisions."""
+    import torch
+    from oracle import fp8
+    x = synth.make_inputs(cfg, B=B_live)
+    c = x.cfg
+    bs, Kq, Hk, Hq, D, V = c.block_size, c.Kq, c.H_kv, c.H_q, c.D, c.V
+    f32 = x.f32
+    kp, vp, bt, nb = x.pool_with_room((n_steps - 1) * Kq)
+    kc, vc, ks, vs = _fp8_quantize_pool(kp, vp)
+    steps = [x.step_arrays(s) for s in range(n_steps)]
+    T = lambda a, b16=False: to_torch(np.ascontiguousarray(a), bf16=b16)
+    lb0 = x.len_before.astype(np.int32)
+    g = dict(k_cache=T(kc), v_cache=T(vc), k_scale=T(ks), v_scale=T(vs), block_table=T(bt), len_before=T(lb0),
+             kv_len=T(lb0 + Kq), k_new=T(np.stack([k for k, _, _ in steps]), True),
+             v_new=T(np.stack([v for _, v, _ in steps]), True), q=T(np.stack([q for _, _, q in steps]), True),
+             W=T(x.W, True))
+    dev = torch.device("cuda")
+    g["o"] = torch.empty_like(g["q"])
+    g["logits"] = torch.empty((n_steps, c.M, V), dtype=torch.float32, device=dev)
+    spec_np = None
+    if c.mode == "spec":
+        spec_np = [x.spec_inputs(s) for s in range(n_steps)]
+        for k in ("draft_probs", "draft_tokens", "u_accept", "u_resample"):
+            g[k] = T(np.stack([sp[k] for sp in spec_np]))
+        g["out_tokens"] = torch.empty((n_steps, c.B, Kq), dtype=torch.int32, device=dev)
+        g["num_emitted"] = torch.empty((n_steps, c.B), dtype=torch.int32, device=dev)
+    else:
+        g["tokens"] = torch.empty((n_steps, c.M), dtype=torch.int32, device=dev)
+    max_kv = int((lb0 + n_steps * Kq).max())
+    need_ws = clm_gpu.decode_attention_workspace_size(c.B, Kq, Hq, Hk, D, max_kv)
+    ws = torch.empty(need_ws + 256, dtype=torch.uint8, device=dev)
+    ws = ws[(-ws.data_ptr()) % 256:]
+    loop = clm_gpu.DecodeLoop(max_kv_len=max_kv, mode=c.mode, spec_temperature=c.temperature, attn_workspace=ws,
+                              block_size=bs, **g)
+    loop.launch()
+    torch.cuda.synchronize()
+
+    scale = 1.0 / math.sqrt(D)
+    lb = x.len_before.astype(np.int64).copy()
+    live = np.ones(c.B, bool)
+    Wf = f32(x.W)
+    for s in range(n_steps):
+        kn, vn, qs = steps[s]
+        kc, vc, ks, vs = fp8.fp8_kv_cache_append(kc, vc, ks, vs, bt, lb.astype(np.int32), f32(kn), f32(vn), bs)
+        kv_len = (lb + Kq).astype(np.int32)
+        rows_kv = [_fp8_stream_rows(kc, vc, ks, vs, bt, b, int(kv_len[b]), bs) for b in range(c.B)]
+        sp = spec_np[s] if spec_np else None
+        ref = oracle.decode_step(f32(qs), [r[0] for r in rows_kv], [r[1] for r in rows_kv], kv_len, scale, Hk, Wf,
+                                 None, True, mode=c.mode,
+                                 temperature=c.temperature if c.mode == "spec" else None, spec=sp)
+        sel = np.nonzero(live)[0]
+        rows = (sel[:, None] * Kq + np.arange(Kq)[None, :]).reshape(-1)
+        check_close(bf16_tensor_to_f32(g["o"][s])[sel], ref["o"][sel], f"fp8 loop c{cfg} step {s} attention")
+        check_close(g["logits"][s].cpu().numpy()[rows], ref["logits"][rows], f"fp8 loop c{cfg} step {s} logits")
+        if c.mode == "spec":
+            ot, ne = g["out_tokens"][s].cpu().numpy(), g["num_emitted"][s].cpu().numpy()
+            check_verify(ot[sel], ne[sel], ref["logits"].reshape(c.B, Kq, V)[sel], sp["draft_probs"][sel],
+                         sp["draft_tokens"][sel], sp["u_accept"][sel], sp["u_resample"][sel], c.temperature,
+                         f"fp8 loop c{cfg} step {s} verify")
+            add = ref["num_emitted"].astype(np.int64)
+            for b in sel:
+                if ne[b] != add[b] or not np.array_equal(ot[b], ref["out_tokens"][b]):
+                    live[b] = False
+        else:
+            check_argmax(g["tokens"][s].cpu().numpy()[rows], ref["logits"][rows], f"fp8 loop c{cfg} step {s} argmax")
+            add = np.full(c.B, Kq, np.int64)
+        lb = lb + add
+    assert np.array_equal(g["len_before"].cpu().numpy()[live], lb[live]), "lengths after the loop"
+    if live.all():
+        blocks = np.unique(bt)
+        np.testing.assert_array_equal(g["k_cache"].cpu().numpy()[blocks], kc[blocks], err_msg="fp8 key codes")
+        np.testing.assert_array_equal(g["v_cache"].cpu().numpy()[blocks], vc[blocks], err_msg="fp8 value codes")
+        for name, ref_sc in (("k_scale", ks), ("v_scale", vs)):
+            np.testing.assert_array_equal(g[name].cpu().numpy()[blocks].view(np.uint32),
+                                          ref_sc[blocks].view(np.uint32), err_msg=f"fp8 {name}")
+    loop.close()
+    print(f"fp8 loop c{cfg}: {n_steps} steps, {c.B} streams, {int((~live).sum())} parted on exempt decisions")
+
+
+def test_loop_fp8_cache(clm_gpu):
+    """FP8 cache in the loop: 24 streams of the 256-stream mix, greedy, 3
+    steps (one or two query rows per KV head), and the 6-query blocks with
+    verification, 3 steps (12 rows)."""
+    _fp8_loop_case(clm_gpu, 5, 24, 3)
+    _fp8_loop_case(clm_gpu, 4, 32, 3)
