@@ -493,22 +493,26 @@ __global__ __launch_bounds__(NT) void verify_rows_kernel(VerifyArgs P) {
 // Phase 2: one thread per stream walks its rows in order: the first row with
 // a negative slot was rejected (its residual token is decoded in place) and
 // ends the stream; all K accepted emits K tokens, plus the decoded bonus
-// draw with the bonus variant.  Later slots are padded with -1.
+// draw with the bonus variant.  A rejection at the last draft also emits K
+// tokens, so the bonus follows only when no row was rejected.  Later slots
+// are padded with -1.
 __global__ __launch_bounds__(256) void verify_chain_kernel(VerifyArgs P) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= P.B) return;
   const int K = P.K, TK = K + P.bonus;
   int32_t* out = P.out_tokens + (size_t)b * TK;
   int emitted = K;
+  bool rejected = false;
   for (int i = 0; i < K; ++i) {
     const int v = out[i];
     if (v < 0) {
       out[i] = -v - 2;
       emitted = i + 1;
+      rejected = true;
       break;
     }
   }
-  if (emitted == K && P.bonus) {
+  if (!rejected && P.bonus) {
     out[K] = -out[K] - 2;
     emitted = K + 1;
   }

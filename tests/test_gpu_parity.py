@@ -585,6 +585,44 @@ def test_spec_verify_bonus_after_all_accepts(clm_gpu, T):
     print(f"bonus all-accept T={T}: exempt {ex}/{x.cfg.B}")
 
 
+@pytest.mark.parametrize("bonus", [False, True])
+def test_spec_verify_first_rejection_at_every_position(clm_gpu, bonus):
+    """Stream b's first rejection is planted at draft b % (K+1) (K+1: none):
+    drafts before it come from the target distribution itself (ratio 1,
+    accepted at u < 0.999), the rejected draft has all its draft mass on one
+    token (ratio p(x) << u = 0.5).  Every stream must emit exactly its
+    accepted drafts and one residual token; the bonus variant adds a bonus
+    token only after K accepts, also when the rejection is at the last draft."""
+    x = inputs(4)
+    s = x.spec_inputs()
+    tl = s["target_logits_bonus_iso"]
+    B, K, V, T = x.cfg.B, x.cfg.Kq, x.cfg.V, 0.7
+    if not bonus:
+        tl = np.ascontiguousarray(tl[:, :K])
+    q = np.stack([[oracle.target_probs(tl[b, i], T) for i in range(K)] for b in range(B)]).astype(np.float32)
+    drafts = s["draft_tokens"].copy()
+    ua = (s["u_accept"] * np.float32(0.999)).astype(np.float32)
+    first_rej = np.arange(B) % (K + 1)
+    for b in range(B):
+        j = int(first_rej[b])
+        if j < K:
+            q[b, j] = 0.0
+            q[b, j, drafts[b, j]] = 1.0
+            ua[b, j] = 0.5
+    f = clm_gpu.spec_verify_bonus if bonus else clm_gpu.spec_verify
+    toks, num = f(to_torch(tl), to_torch(q), to_torch(drafts), to_torch(ua), to_torch(s["u_resample"]), T)
+    toks, num = toks.cpu().numpy(), num.cpu().numpy()
+    want = np.where(first_rej < K, first_rej + 1, K + (1 if bonus else 0))
+    np.testing.assert_array_equal(num, want)
+    for b in range(B):
+        j = int(first_rej[b])
+        np.testing.assert_array_equal(toks[b, :min(j, K)], drafts[b, :min(j, K)])
+        assert np.all(toks[b, num[b]:] == -1)
+    ex = check_verify(toks, num, tl, q, drafts, ua, s["u_resample"], T, f"planted rejections bonus={bonus}",
+                      bonus=bonus)
+    print(f"planted rejections bonus={bonus}: exempt {ex}/{B}")
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_chained_step(clm_gpu, cfg):
     """append -> attention -> head -> sample/argmax/verify on the GPU, against

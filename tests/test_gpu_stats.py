@@ -6,6 +6,9 @@ draft is accepted with probability sum_x min(p(x), q(x))).
 
 Every stream sees the same small-vocabulary target and draft rows, its own
 drafted tokens (drawn from the draft rows) and uniforms, all seeded.  The
+number of tokens a stream emits follows from the per-position acceptance
+rates (independent positions), which also fixes how often the bonus token
+appears.  The
 counts are compared with the target probabilities (float64 softmax) by a
 chi-square statistic at a 1e-6 tail, so a kernel that drew from the wrong
 distribution (the draft's, an unnormalised residual, a shifted CDF) fails
@@ -68,6 +71,21 @@ def test_spec_verify_keeps_the_target_distribution(clm_gpu, bonus):
     # given draft 0 kept, the second token follows p_1
     sel = num >= 2
     _chi2_ok(np.bincount(toks[sel, 1], minlength=V), p_rows[1], f"second token (bonus={bonus})")
+    # drafts and uniforms are independent across positions, so the stream's
+    # first rejection is at j with probability alpha_0 ... alpha_{j-1} (1 - alpha_j)
+    # and it emits j + 1 tokens; with no rejection it emits K (K + 1 with the bonus)
+    alphas = np.minimum(p_rows[:K], q_rows).sum(axis=1)
+    for j in range(K + 1):
+        pj = float(np.prod(alphas[:j]) * (1.0 - alphas[j] if j < K else 1.0))
+        n_j = K + (1 if bonus else 0) if j == K else j + 1
+        if not bonus and j >= K - 1:       # a rejection at the last draft and no rejection both emit K
+            if j == K:
+                continue
+            pj += float(np.prod(alphas))
+        rate = float((num == n_j).mean())
+        sd = np.sqrt(pj * (1 - pj) / B)
+        print(f"emitted {n_j}: {rate:.4f} against {pj:.4f} (sd {sd:.4f})")
+        assert abs(rate - pj) < 5 * sd + 1e-9, (n_j, rate, pj)
     if bonus:
         # after K accepted drafts the bonus token follows p_K
         allk = num == K + 1
