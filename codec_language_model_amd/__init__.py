@@ -503,11 +503,14 @@ class DecodeLoop:
     kv_cache_append_fp8 (uint8 k_cache [nb, H_kv, D/8, bs, 8], v_cache [nb,
     H_kv, D, bs], float32 scales [nb, H_kv, bs]); q, k_new and v_new are then
     bf16, an attention workspace is required and positions are not taken.
-    mode: "greedy", "sample" or "spec".  Every tensor must stay alive while
+    mode: "greedy", "sample", "spec" or "spec_bonus" (verification with a
+    bonus token: the Kq queries score the last kept token and Kq - 1 drafts,
+    so draft_probs is [n, B, Kq-1, V], draft_tokens and u_accept [n, B,
+    Kq-1], out_tokens [n, B, Kq]).  Every tensor must stay alive while
     the loop exists (this object keeps references); launch() enqueues all
     n_steps steps on torch's current stream."""
 
-    _MODES = {"greedy": 0, "sample": 1, "spec": 2}
+    _MODES = {"greedy": 0, "sample": 1, "spec": 2, "spec_bonus": 3}
 
     def __init__(self, *, k_cache, v_cache, block_table, len_before, kv_len, max_kv_len, k_new, v_new, q, W, o,
                  logits, head_id=None, positions=None, rope_base=1.0e6, mode="greedy", tokens=None,
@@ -562,10 +565,13 @@ class DecodeLoop:
         if mode == "sample":
             _out("temperature", temperature, (n, M), torch.float32)
             _out("uniforms", uniforms, (n, M), torch.float32)
-        if mode == "spec":
-            _out("draft_probs", draft_probs, (n, B, Kq, V), torch.float32)
-            _out("draft_tokens", draft_tokens, (n, B, Kq), torch.int32)
-            _out("u_accept", u_accept, (n, B, Kq), torch.float32)
+        if mode in ("spec", "spec_bonus"):
+            Kd = Kq - 1 if mode == "spec_bonus" else Kq
+            if Kd < 1:
+                raise ValueError("DecodeLoop: spec_bonus needs Kq >= 2 (the last kept token and a draft)")
+            _out("draft_probs", draft_probs, (n, B, Kd, V), torch.float32)
+            _out("draft_tokens", draft_tokens, (n, B, Kd), torch.int32)
+            _out("u_accept", u_accept, (n, B, Kd), torch.float32)
             _out("u_resample", u_resample, (n, B), torch.float32)
             _out("out_tokens", out_tokens, (n, B, Kq), torch.int32)
             _out("num_emitted", num_emitted, (n, B), torch.int32)

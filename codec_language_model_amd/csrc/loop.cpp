@@ -75,13 +75,18 @@ int record_step(const clm_decode_step_desc& d, int s, hipStream_t st) {
   rc = clm_codebook_head(o, d.W, d.G, d.head_id, logits, M, d.H_q * d.D, d.V, d.dt, nullptr, 0, st);
   if (rc != CLM_OK) return rc;
   const int32_t* emitted = nullptr;
-  if (d.mode == 2) {
+  if (d.mode == 2 || d.mode == 3) {
+    // mode 3: the Kq target rows score the last kept token and Kd = Kq - 1 drafts
+    const int Kd = d.mode == 3 ? d.Kq - 1 : d.Kq;
+    const size_t Md = (size_t)d.B * Kd;
     int32_t* num = step_ptr(d.num_emitted, s, (size_t)d.B * sizeof(int32_t));
-    rc = clm_spec_verify(logits, step_ptr(d.draft_probs, s, (size_t)M * d.V * sizeof(float)),
-                         step_ptr(d.draft_tokens, s, (size_t)M * sizeof(int32_t)),
-                         step_ptr(d.u_accept, s, (size_t)M * sizeof(float)),
-                         step_ptr(d.u_resample, s, (size_t)d.B * sizeof(float)), d.spec_temperature, d.B, d.Kq,
-                         d.V, step_ptr(d.out_tokens, s, (size_t)M * sizeof(int32_t)), num, st);
+    const float* dp = step_ptr(d.draft_probs, s, Md * d.V * sizeof(float));
+    const int32_t* dtok = step_ptr(d.draft_tokens, s, Md * sizeof(int32_t));
+    const float* ua = step_ptr(d.u_accept, s, Md * sizeof(float));
+    const float* ur = step_ptr(d.u_resample, s, (size_t)d.B * sizeof(float));
+    int32_t* ot = step_ptr(d.out_tokens, s, (size_t)M * sizeof(int32_t));
+    rc = d.mode == 3 ? clm_spec_verify_bonus(logits, dp, dtok, ua, ur, d.spec_temperature, d.B, Kd, d.V, ot, num, st)
+                     : clm_spec_verify(logits, dp, dtok, ua, ur, d.spec_temperature, d.B, Kd, d.V, ot, num, st);
     emitted = num;
   } else {
     rc = clm_sample_or_argmax(logits, M, d.V, d.V,
@@ -101,9 +106,10 @@ int check_desc(const clm_decode_step_desc& d) {
   if (d.mode == 0 || d.mode == 1) {
     if (!d.tokens) return CLM_ERR_INVALID_ARG;
     if (d.mode == 1 && (!d.temperature || !d.uniforms)) return CLM_ERR_INVALID_ARG;
-  } else if (d.mode == 2) {
+  } else if (d.mode == 2 || d.mode == 3) {
     if (!d.draft_probs || !d.draft_tokens || !d.u_accept || !d.u_resample || !d.out_tokens || !d.num_emitted)
       return CLM_ERR_INVALID_ARG;
+    if (d.mode == 3 && d.Kq < 2) return CLM_ERR_INVALID_ARG;
   } else {
     return CLM_ERR_INVALID_ARG;
   }

@@ -445,17 +445,19 @@ typedef struct clm_decode_step_desc {
   float* logits;                    /* [n_steps][B*Kq, V] */
   void* attn_workspace;             /* clm_decode_attention's workspace, or NULL: the library's */
   size_t attn_workspace_bytes;      /*   static scratch (clm_decode_attention_noalloc) */
-  int mode;                         /* 0 greedy, 1 temperature sampling, 2 speculative verification */
+  int mode;                         /* 0 greedy, 1 temperature sampling, 2 speculative verification,
+                                       3 verification with a bonus token (clm_spec_verify_bonus): the
+                                       Kq queries score the last kept token and Kd = Kq - 1 drafts */
   const float* temperature;         /* mode 1: [n_steps][B*Kq] */
   const float* uniforms;            /* mode 1: [n_steps][B*Kq] */
   int32_t* tokens;                  /* modes 0, 1: [n_steps][B*Kq] */
-  float spec_temperature;           /* mode 2 */
-  const float* draft_probs;         /* mode 2: [n_steps][B, Kq, V] */
-  const int32_t* draft_tokens;      /* mode 2: [n_steps][B, Kq] */
-  const float* u_accept;            /* mode 2: [n_steps][B, Kq] */
-  const float* u_resample;          /* mode 2: [n_steps][B] */
-  int32_t* out_tokens;              /* mode 2: [n_steps][B, Kq] */
-  int32_t* num_emitted;             /* mode 2: [n_steps][B]; the lengths advance by these */
+  float spec_temperature;           /* modes 2, 3 */
+  const float* draft_probs;         /* modes 2, 3: [n_steps][B, Kd, V], Kd = Kq (mode 2) or Kq - 1 */
+  const int32_t* draft_tokens;      /* modes 2, 3: [n_steps][B, Kd] */
+  const float* u_accept;            /* modes 2, 3: [n_steps][B, Kd] */
+  const float* u_resample;          /* modes 2, 3: [n_steps][B] */
+  int32_t* out_tokens;              /* modes 2, 3: [n_steps][B, Kq] */
+  int32_t* num_emitted;             /* modes 2, 3: [n_steps][B]; the lengths advance by these */
   float* k_scale;                   /* FP8 (E4M3) cache: the per-row key and value scales */
   float* v_scale;                   /*   [num_blocks, H_kv, block_size] of clm_kv_cache_append_fp8,
                                        with k_cache / v_cache in its byte layouts; both NULL for a
@@ -473,7 +475,8 @@ typedef struct clm_decode_loop clm_decode_loop;   /* opaque */
  * would validate it, before or during capture; on an error nothing is kept.
  * Checked mode must be off (it synchronises): UNSUPPORTED otherwise.
  * Errors: INVALID_ARG (null desc/loop, n_steps out of range, a null array the
- *   mode needs, mode not 0..2, one FP8 scale array without the other),
+ *   mode needs, mode not 0..3, mode 3 with Kq < 2, one FP8 scale array
+ *   without the other),
  *   UNSUPPORTED (an FP8 cache with dt other than CLM_BF16, with positions or
  *   without attn_workspace), the individual calls' errors, HIP.
  */

@@ -115,6 +115,11 @@ int main() {
   EXPECT(clm_decode_loop_create(nullptr, 4, &loop), INV);
   d.mode = 2;
   EXPECT(clm_decode_loop_create(&d, 4, &loop), INV);
+  d.mode = 3;                                              // bonus verification needs Kq >= 2
+  d.draft_probs = F; d.draft_tokens = I; d.u_accept = F; d.u_resample = F; d.out_tokens = I; d.num_emitted = I;
+  EXPECT(clm_decode_loop_create(&d, 4, &loop), INV);
+  d.draft_probs = nullptr; d.draft_tokens = nullptr; d.u_accept = nullptr; d.u_resample = nullptr;
+  d.out_tokens = nullptr; d.num_emitted = nullptr;
   d.mode = 0;
   d.k_scale = F;                                           // FP8 cache: one scale array alone
   EXPECT(clm_decode_loop_create(&d, 4, &loop), INV);

@@ -297,6 +297,11 @@ def test_decode_loop_host_checks(lib):
     assert create(C.byref(d), 4, C.byref(h)) == INVALID          # sampling needs temperature, uniforms
     d.mode = 2
     assert create(C.byref(d), 4, C.byref(h)) == INVALID          # verification needs the draft arrays
+    d.mode = 3
+    assert create(C.byref(d), 4, C.byref(h)) == INVALID          # bonus verification: the draft arrays ...
+    d.draft_probs = d.draft_tokens = d.u_accept = d.u_resample = d.out_tokens = d.num_emitted = 0x100000
+    assert create(C.byref(d), 4, C.byref(h)) == INVALID          # ... and Kq >= 2 (last token + a draft)
+    d.draft_probs = d.draft_tokens = d.u_accept = d.u_resample = d.out_tokens = d.num_emitted = 0
     d.mode = 7
     assert create(C.byref(d), 4, C.byref(h)) == INVALID
     d.mode = 0

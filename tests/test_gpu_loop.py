@@ -38,7 +38,7 @@ def _pages(n, bs):
     return (np.asarray(n, np.int64) + bs - 1) // bs
 
 
-def _loop_case(clm_gpu, cfg, B_live, B_cap, n_steps, rope=False, use_ws=True, replay=False):
+def _loop_case(clm_gpu, cfg, B_live, B_cap, n_steps, rope=False, use_ws=True, replay=False, bonus=False):
     import torch
     x = synth.make_inputs(cfg, B=B_live)
     c = x.cfg
@@ -75,6 +75,10 @@ def _loop_case(clm_gpu, cfg, B_live, B_cap, n_steps, rope=False, use_ws=True, re
     spec_np = None
     if c.mode == "spec":
         spec_np = [x.spec_inputs(s) for s in range(n_steps)]
+        if bonus:           # Kq queries: the last kept token, then Kq - 1 drafts
+            for sp in spec_np:
+                for k in ("draft_probs", "draft_tokens", "u_accept"):
+                    sp[k] = np.ascontiguousarray(sp[k][:, :Kq - 1])
         g["draft_probs"] = T(np.stack([padded(sp["draft_probs"]) for sp in spec_np]))
         g["draft_tokens"] = T(np.stack([padded(sp["draft_tokens"]) for sp in spec_np]))
         g["u_accept"] = T(np.stack([padded(sp["u_accept"]) for sp in spec_np]))
@@ -96,8 +100,8 @@ def _loop_case(clm_gpu, cfg, B_live, B_cap, n_steps, rope=False, use_ws=True, re
         ws = torch.empty(need_ws + 256, dtype=torch.uint8, device=dev)
         ws = ws[(-ws.data_ptr()) % 256:]
     initial = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in g.items()}
-    loop = clm_gpu.DecodeLoop(max_kv_len=max_kv, mode=c.mode, spec_temperature=c.temperature,
-                              attn_workspace=ws, block_size=bs, rope_base=1.0e6, **g)
+    loop = clm_gpu.DecodeLoop(max_kv_len=max_kv, mode="spec_bonus" if bonus else c.mode,
+                              spec_temperature=c.temperature, attn_workspace=ws, block_size=bs, rope_base=1.0e6, **g)
     loop.launch()
     torch.cuda.synchronize()
 
@@ -123,11 +127,17 @@ def _loop_case(clm_gpu, cfg, B_live, B_cap, n_steps, rope=False, use_ws=True, re
         vs = [np.concatenate([vals[b], vf[b]]) for b in range(B_live)]
         kv_len = (lb + Kq).astype(np.int32)
         sp = spec_np[s] if spec_np else None
-        ref = oracle.decode_step(qf, ks, vs, kv_len, scale, Hk, Wf, x.head_id if c.G > 1 else None, bf,
-                                 mode=c.mode,
-                                 temperature=(c.temperature if c.mode == "spec" else
-                                              (temp_np[s, :c.M] if temp_np is not None else None)),
-                                 uniforms=None if uni_np is None else uni_np[s, :c.M], spec=sp)
+        if bonus:           # attention and logits as in any step, then the bonus-token verification
+            ref = oracle.decode_step(qf, ks, vs, kv_len, scale, Hk, Wf, None, bf)
+            ref["out_tokens"], ref["num_emitted"] = oracle.spec_verify(
+                ref["logits"].reshape(B_live, Kq, V), sp["draft_probs"], sp["draft_tokens"], sp["u_accept"],
+                sp["u_resample"], c.temperature, bonus=True)
+        else:
+            ref = oracle.decode_step(qf, ks, vs, kv_len, scale, Hk, Wf, x.head_id if c.G > 1 else None, bf,
+                                     mode=c.mode,
+                                     temperature=(c.temperature if c.mode == "spec" else
+                                                  (temp_np[s, :c.M] if temp_np is not None else None)),
+                                     uniforms=None if uni_np is None else uni_np[s, :c.M], spec=sp)
         sel = np.nonzero(live)[0]
         rows = (sel[:, None] * Kq + np.arange(Kq)[None, :]).reshape(-1)
         o_g = bf16_tensor_to_f32(g["o"][s])[:B_live]
@@ -139,7 +149,8 @@ def _loop_case(clm_gpu, cfg, B_live, B_cap, n_steps, rope=False, use_ws=True, re
             ne = g["num_emitted"][s].cpu().numpy()[:B_live]
             rl = ref["logits"].reshape(B_live, Kq, V)
             check_verify(ot[sel], ne[sel], rl[sel], sp["draft_probs"][sel], sp["draft_tokens"][sel],
-                         sp["u_accept"][sel], sp["u_resample"][sel], c.temperature, f"loop c{cfg} step {s} verify")
+                         sp["u_accept"][sel], sp["u_resample"][sel], c.temperature, f"loop c{cfg} step {s} verify",
+                         bonus=bonus)
             add = ref["num_emitted"].astype(np.int64)
             for b in sel:
                 if ne[b] != add[b] or not np.array_equal(ot[b], ref["out_tokens"][b]):
@@ -206,6 +217,13 @@ def test_loop_greedy_rope_replay(clm_gpu):
 def test_loop_speculative(clm_gpu):
     """32 streams x 6-query blocks, 4 steps; lengths advance by the tokens kept."""
     _loop_case(clm_gpu, 4, 32, 32, 4)
+
+
+def test_loop_speculative_bonus_token(clm_gpu):
+    """The same blocks with a bonus token: the 6 queries score the last kept
+    token and 5 drafts, and a stream that keeps all 5 drafts emits a sixth
+    token from the last target row; 4 steps, lengths advance by 1..6."""
+    _loop_case(clm_gpu, 4, 32, 32, 4, bonus=True)
 
 
 def test_loop_sampling_padded_bucket_static_scratch(clm_gpu):
