@@ -332,17 +332,22 @@ def test_codebook_head_isolated(clm_gpu, cfg):
 def test_codebook_head_ragged_rows(clm_gpu):
     """Row counts that are not multiples of 16, 64 or 128, vocabularies that
     are not multiples of the entry tile, several row chunks per head, one head
-    holding most rows, and d from 128 up."""
+    holding most rows, heads that get no rows at all (the eight-head limit
+    with only the last one used), and d from 128 up."""
     rng = np.random.default_rng(5)
     cases = [(1, 4096, 1, 256), (17, 1000, 1, 256), (70, 4096, 3, 256), (130, 4160, 2, 256),
              (129, 1000, 1, 128), (300, 4160, 1, 384), (260, 20000, 1, 256),
-             (300, 4096, 2, 256)]
+             (300, 4096, 2, 256), (50, 4096, 4, 256), (200, 1000, 8, 128)]
     for M, V, G, d in cases:
         h = synth.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32))
         W = synth.f32_to_bf16_bits((rng.standard_normal((G, V, d)) * 0.05).astype(np.float32))
         hid = rng.integers(0, G, size=M).astype(np.int32)
         if G == 2 and M == 300:
             hid[:220] = 1                       # one head takes 220 of the rows
+        if G == 4:
+            hid = np.where(hid < 2, 0, 3).astype(np.int32)      # heads 1 and 2 get no rows
+        if G == 8:
+            hid[:] = 7                          # all rows on the last of eight heads
         logits = clm_gpu.codebook_head(to_torch(h, bf16=True), to_torch(W, bf16=True),
                                        to_torch(hid) if G > 1 else None)
         ref = oracle.codebook_head(synth.bf16_bits_to_f32(h), synth.bf16_bits_to_f32(W), hid)
@@ -415,6 +420,19 @@ def test_sampler_closed_forms(clm_gpu):
     y[0, 3000:] = 0.0
     t0 = clm_gpu.sample_or_argmax(to_torch(y), to_torch(np.ones(1, np.float32)), to_torch(np.zeros(1, np.float32)))
     assert int(t0.cpu()[0]) == 3000
+    # the largest uniform below 1 takes the last token of positive weight:
+    # equal logits (last index), zero weight past index 499, a vocabulary
+    # mask at 300, and a row of two passes with zero weight past 20000
+    top = np.float32(1.0) - np.float32(2.0 ** -24)
+    z = np.zeros((3, 1000), np.float32)
+    z[1, 500:] = -1e30
+    tz = clm_gpu.sample_or_argmax(to_torch(z), to_torch(np.full(3, 0.7, np.float32)), to_torch(np.full(3, top)),
+                                  vocab_valid=to_torch(np.array([1000, 1000, 300], np.int32))).cpu().numpy()
+    assert tz.tolist() == [999, 499, 299]
+    w = np.zeros((1, 30000), np.float32)
+    w[0, 20001:] = -1e30
+    tw = clm_gpu.sample_or_argmax(to_torch(w), to_torch(np.ones(1, np.float32)), to_torch(np.full(1, top)))
+    assert int(tw.cpu()[0]) == 20000
 
 
 @pytest.mark.parametrize("V", [16385, 50000, 100003])
