@@ -218,6 +218,27 @@ def test_decode_attention_max_streams(clm_gpu):
     check_close(bf16_tensor_to_f32(o), ref, "attention, 4096 streams")
 
 
+@pytest.mark.parametrize("Kq", [1, 6])
+def test_decode_attention_split_boundaries(clm_gpu, Kq):
+    """Lengths on and next to multiples of the split and of the 16-token tile:
+    12 streams with a bound of 129 keys take 64-token splits under both rules
+    (one query: the vector kernel; 6-query blocks: the matrix-core kernel), so
+    streams end one before, on and one after the first and second split
+    boundaries, where the last split is full, short or a single key."""
+    rng = np.random.default_rng(64 + Kq)
+    Hq, Hk, D, bs = 16, 8, 128, 16
+    lens = [max(Kq, 1), 15, 16, 17, 63, 64, 65, 127, 128, 129, 32, 48 if Kq == 1 else 70]
+    kv_len, bt, kc, vc, q, keys, vals = _random_pool_case(rng, lens, Kq, Hq, Hk, D, bs)
+    scale = 1.0 / math.sqrt(D)
+    rows = 2 if Kq == 1 else 12                 # query rows per KV head, as the kernels pad them
+    assert clm_gpu.decode_attention_workspace_size(12, Kq, Hq, Hk, D, 129) == 12 * Hk * 3 * rows * (2 + D) * 4, \
+        "partials for 3 splits of 64 tokens per stream"
+    o = clm_gpu.decode_attention(to_torch(q, bf16=True), to_torch(kc, bf16=True), to_torch(vc, bf16=True),
+                                 to_torch(bt), to_torch(kv_len), 129, scale=scale)
+    ref = oracle.decode_attention(synth.bf16_bits_to_f32(q), keys, vals, kv_len, scale, Hk)
+    check_close(bf16_tensor_to_f32(o), ref, f"attention at split boundaries, Kq={Kq}")
+
+
 def test_decode_attention_long_context(clm_gpu):
     """One stream of 100,000 keys next to one of a single key: 98 splits of
     1024 tokens for the long stream, so the merge pass combines more splits
