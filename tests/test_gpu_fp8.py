@@ -227,3 +227,35 @@ def test_fp8_block_sizes(clm_gpu, cfg, bs, D):
         vals.append(V)
     ref = oracle.decode_attention(synth.bf16_bits_to_f32(x.q), keys, vals, x.kv_len, scale, c.H_kv)
     check_close(bf16_tensor_to_f32(o), ref, f"fp8 attention c{cfg} block size {bs} D {D}")
+
+
+@pytest.mark.parametrize("Kq", [1, 6])
+def test_fp8_attention_split_boundaries(clm_gpu, Kq):
+    """The FP8 kernel with lengths on and next to the 64-token split and the
+    16-token tile boundaries (12 streams, a bound of 129 keys), one query and
+    6-query blocks, random codes and scales, against the oracle on the
+    dequantized rows."""
+    rng = np.random.default_rng(640 + Kq)
+    Hq, Hk, D, bs = 16, 8, 128, 16
+    kv_len = np.array([max(Kq, 1), 15, 16, 17, 63, 64, 65, 127, 128, 129, 32, 48 if Kq == 1 else 70], np.int32)
+    B = kv_len.size
+    pages = (kv_len + bs - 1) // bs
+    nb = int(pages.sum()) + 2
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.zeros((B, int(pages.max())), np.int32)
+    o_ = 0
+    for b in range(B):
+        bt[b, :pages[b]] = perm[o_:o_ + pages[b]]
+        o_ += pages[b]
+    kc, vc, ks, vs = _random_fp8_pool(rng, nb, Hk, D, bs)
+    q_bits = synth.f32_to_bf16_bits(rng.standard_normal((B, Kq, Hq, D)).astype(np.float32))
+    scale = 1.0 / math.sqrt(D)
+    o = clm_gpu.decode_attention_fp8(to_torch(q_bits, bf16=True), dev(kc), dev(vc), dev(ks), dev(vs), dev(bt),
+                                     dev(kv_len), 129, scale=scale)
+    keys, vals = [], []
+    for b in range(B):
+        K, V = _stream_rows(kc, vc, ks, vs, bt, b, int(kv_len[b]), bs)
+        keys.append(K)
+        vals.append(V)
+    ref = oracle.decode_attention(synth.bf16_bits_to_f32(q_bits), keys, vals, kv_len, scale, Hk)
+    check_close(bf16_tensor_to_f32(o), ref, f"fp8 attention at split boundaries, Kq={Kq}")
