@@ -259,3 +259,42 @@ def test_fp8_attention_split_boundaries(clm_gpu, Kq):
         vals.append(V)
     ref = oracle.decode_attention(synth.bf16_bits_to_f32(q_bits), keys, vals, kv_len, scale, Hk)
     check_close(bf16_tensor_to_f32(o), ref, f"fp8 attention at split boundaries, Kq={Kq}")
+
+
+def test_fp8_append_special_rows(clm_gpu):
+    """Rows the quantizer treats specially, bit-exact against the oracle's
+    codes and scales: all +0 (scale 1), all -0 and mixed signed zeros (sign
+    bits kept), a single nonzero entry, rows whose scale is 1 so small entries
+    land on the subnormal codes, magnitudes near the ends of the bf16 range,
+    and a row of bf16 subnormals (its scale is an fp32 subnormal)."""
+    B, T, H, D, bs = 1, 10, 1, 128, 16
+    rng = np.random.default_rng(8)
+    rows = np.zeros((T, D), np.float32)
+    rows[1] = -0.0
+    rows[2, ::2] = -0.0
+    rows[3, 17] = 1.0
+    rows[4] = rng.uniform(-0.02, 0.02, D)
+    rows[4, 5] = 448.0                                   # scale 1: the rest quantize on the subnormal steps
+    rows[5] = rng.standard_normal(D) * 1e30
+    rows[6] = rng.standard_normal(D) * 1e-30
+    rows[7] = rng.standard_normal(D) * 2e-39             # bf16 subnormals
+    rows[8] = rng.standard_normal(D)
+    rows[8, 0] = -3.0e38                                 # near the largest bf16
+    rows[9] = np.linspace(-448.0, 448.0, D)
+    bits = synth.f32_to_bf16_bits(rows).reshape(B, T, H, D)
+    vals = synth.bf16_bits_to_f32(bits)
+    nb = 1
+    bt = np.zeros((B, 1), np.int32)
+    lb = np.zeros(B, np.int32)
+    kc = np.zeros((nb, H, D // 8, bs, 8), np.uint8)
+    vc = np.zeros((nb, H, D, bs), np.uint8)
+    ks = np.zeros((nb, H, bs), np.float32)
+    vs = np.zeros((nb, H, bs), np.float32)
+    dk, dv, dks, dvs = dev(kc), dev(vc), dev(ks), dev(vs)
+    clm_gpu.kv_cache_append_fp8(to_torch(bits, bf16=True), to_torch(bits, bf16=True), dk, dv, dks, dvs, dev(bt),
+                                dev(lb), block_size=bs)
+    rk, rv, rks, rvs = fp8.fp8_kv_cache_append(kc, vc, ks, vs, bt, lb, vals, vals, bs)
+    for name, got, want in (("key codes", dk, rk), ("value codes", dv, rv)):
+        np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=name)
+    for name, got, want in (("key scales", dks, rks), ("value scales", dvs, rvs)):
+        np.testing.assert_array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32), err_msg=name)
