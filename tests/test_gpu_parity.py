@@ -928,3 +928,64 @@ def test_codebook_head_rows_independent_of_batch(clm_gpu):
         np.testing.assert_array_equal(grouped[rows].view(np.uint32), one.view(np.uint32), err_msg=f"stage {g}")
     check_close(grouped, oracle.codebook_head(synth.bf16_bits_to_f32(h), synth.bf16_bits_to_f32(W), hid),
                 "grouped head 256 rows")
+
+
+@pytest.mark.parametrize("Kq", [1, 6])
+def test_decode_attention_closed_forms(clm_gpu, Kq):
+    """Results fixed by the definition alone, on both kernels and across
+    split merges (the 3000- and 1000-key streams span several splits):
+    - a stream whose keys are all equal attends uniformly: each query's output
+      is the plain mean of the values it sees (causal: query j of a block
+      averages exactly kv_len - (Kq-1-j) rows; the 17- and 2-key streams make
+      one row more or less show);
+    - a query equal to 30/sqrt(D) times one visible key (a score of about 30
+      for that key against a spread of about 3 for the others) returns that
+      key's value row;
+    - scores with a spread of about 100 (q and K entries of N(0, 10)) against
+      the oracle."""
+    rng = np.random.default_rng(777 + Kq)
+    Hq, Hk, D, bs = 16, 8, 128, 16
+    G = Hq // Hk
+    lens = [3000, 1000, 17, max(Kq, 2), 2500, 64]
+    kv_len, bt, kc, vc, q, keys, vals = _random_pool_case(rng, lens, Kq, Hq, Hk, D, bs)
+    B = len(lens)
+    # streams 0-3: every key row equal (per KV head)
+    for b in (0, 1, 2, 3):
+        n = int(kv_len[b])
+        row = synth.f32_to_bf16_bits(rng.standard_normal((Hk, D)).astype(np.float32))
+        for pos in range(n):
+            kc[bt[b, pos // bs], :, pos % bs, :] = row
+    # stream 4: each query row is 30 x the key at position t (visible to every query of the block)
+    t_dom = 1234
+    qf = synth.bf16_bits_to_f32(q)
+    kf = synth.bf16_bits_to_f32(kc)
+    for j in range(Kq):
+        for h in range(Hq):
+            qf[4, j, h] = 30.0 * kf[bt[4, t_dom // bs], h // G, t_dom % bs] / np.sqrt(D)
+    # stream 5: large scores
+    qf[5] *= 10.0
+    q = synth.f32_to_bf16_bits(qf)
+    qf = synth.bf16_bits_to_f32(q)
+    blk5 = bt[5, :(64 + bs - 1) // bs]
+    kc[blk5] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(kc[blk5]) * 10.0)
+    scale = 1.0 / math.sqrt(D)
+    o = clm_gpu.decode_attention(to_torch(q, bf16=True), to_torch(kc, bf16=True), to_torch(vc, bf16=True),
+                                 to_torch(bt), to_torch(kv_len), int(kv_len.max()), scale=scale)
+    of = bf16_tensor_to_f32(o)
+    vf = synth.bf16_bits_to_f32(vc)
+    for b in (0, 1, 2, 3):
+        for j in range(Kq):
+            n_j = int(kv_len[b]) - (Kq - 1 - j)
+            pos = np.arange(n_j)
+            mean = vf[bt[b, pos // bs], :, :, pos % bs].astype(np.float64).mean(axis=0)    # [Hk, D]
+            want = np.repeat(mean, G, axis=0)                                               # [Hq, D]
+            # exact up to fp32 sums and the bf16 output rounding
+            check_close(of[b, j], want, f"equal keys: stream {b} query {j} averages its {n_j} rows",
+                        atol=2e-3, rtol=8e-3)
+    v_dom = vf[bt[4, t_dom // bs], :, :, t_dom % bs]                                        # [Hk, D]
+    for j in range(Kq):
+        check_close(of[4, j], np.repeat(v_dom, G, axis=0), f"dominant key: query {j}")
+    keys5 = [synth.bf16_bits_to_f32(kc)[bt[5, np.arange(64) // bs], :, np.arange(64) % bs, :]]
+    vals5 = [vf[bt[5, np.arange(64) // bs], :, :, np.arange(64) % bs]]
+    ref5 = oracle.decode_attention(qf[5:6], keys5, vals5, kv_len[5:6], scale, Hk)
+    check_close(of[5:6], ref5, "scores of magnitude ~100")
