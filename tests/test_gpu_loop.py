@@ -219,6 +219,13 @@ def test_loop_speculative(clm_gpu):
     _loop_case(clm_gpu, 4, 32, 32, 4)
 
 
+def test_loop_speculative_rope(clm_gpu):
+    """The 6-query blocks with rotary embedding at logical positions, 3 steps:
+    the positions advance by the tokens kept, like the lengths, so the next
+    block's queries and keys are rotated where its tokens really sit."""
+    _loop_case(clm_gpu, 4, 32, 32, 3, rope=True)
+
+
 def test_loop_speculative_bonus_token(clm_gpu):
     """The same blocks with a bonus token: the 6 queries score the last kept
     token and 5 drafts, and a stream that keeps all 5 drafts emits a sixth
