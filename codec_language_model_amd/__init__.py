@@ -89,6 +89,14 @@ def _out(name, t, shape, dtype):
     return t
 
 
+def _rows(call, B, **arrays):
+    """Per-stream device arrays must have B rows: a shorter one would be read
+    past its end by the kernels."""
+    for name, t in arrays.items():
+        if t is not None and t.shape[0] != B:
+            raise ValueError(f"{call}: {name} has {t.shape[0]} rows for {B} streams")
+
+
 def _ptr(t):
     return C.c_void_p(0 if t is None else t.data_ptr())
 
@@ -189,6 +197,7 @@ def kv_cache_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_
             or tuple(v_cache.shape) != (nb, H, D, block_size) or tuple(k_scale.shape) != (nb, H, block_size) \
             or tuple(v_scale.shape) != (nb, H, block_size):
         raise ValueError("kv_cache_append_fp8: shape mismatch")
+    _rows("kv_cache_append_fp8", B, block_table=block_table, len_before=len_before)
     _check("clm_kv_cache_append_fp8", lib.clm_kv_cache_append_fp8(
         _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
         block_table.shape[1], _ptr(len_before), B, T, H, D, block_size, nb, _stream()))
@@ -213,6 +222,7 @@ def decode_attention(q, k_cache, v_cache, block_table, kv_len, max_kv_len, scale
     nb, H_kv = k_cache.shape[0], k_cache.shape[1]
     if tuple(k_cache.shape) != (nb, H_kv, block_size, D) or tuple(v_cache.shape) != (nb, H_kv, D, block_size):
         raise ValueError("decode_attention: cache shape mismatch")
+    _rows("decode_attention", B, block_table=block_table, kv_len=kv_len)
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -248,6 +258,7 @@ def decode_attention_noalloc(q, k_cache, v_cache, block_table, kv_len, max_kv_le
     nb, H_kv = k_cache.shape[0], k_cache.shape[1]
     if tuple(k_cache.shape) != (nb, H_kv, block_size, D) or tuple(v_cache.shape) != (nb, H_kv, D, block_size):
         raise ValueError("decode_attention_noalloc: cache shape mismatch")
+    _rows("decode_attention_noalloc", B, block_table=block_table, kv_len=kv_len)
     if out is None:
         raise ValueError("decode_attention_noalloc: the caller provides `out` (nothing is allocated here)")
     _out("out", out, q.shape, q.dtype)
@@ -277,6 +288,7 @@ def decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, kv_
     if tuple(k_cache.shape) != (nb, H_kv, D // 8, bs, 8) or tuple(v_cache.shape) != (nb, H_kv, D, bs) \
             or tuple(k_scale.shape) != (nb, H_kv, bs) or tuple(v_scale.shape) != (nb, H_kv, bs):
         raise ValueError("decode_attention_fp8: shape mismatch")
+    _rows("decode_attention_fp8", B, block_table=block_table, kv_len=kv_len)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -291,7 +303,7 @@ def decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, kv_
     _check("clm_decode_attention_fp8", lib.clm_decode_attention_fp8(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
         block_table.shape[1], _ptr(kv_len), int(max_kv_len), _ptr(out), B, Kq, H_q, H_kv, D, bs, nb,
-        C.c_float(scale), _ptr(workspace), workspace.numel(), _stream()))
+        C.c_float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
     return out
 
 
@@ -334,6 +346,7 @@ def codebook_head(h, W, head_id=None, out=None, workspace=None):
         raise ValueError("codebook_head: shape mismatch")
     if head_id is not None:
         _cuda("head_id", head_id, torch.int32, 1)
+        _rows("codebook_head", M, head_id=head_id)
     if out is None:
         out = torch.empty((M, V), dtype=torch.float32, device=h.device)
     else:
@@ -371,6 +384,7 @@ def codebook_head_mlp(h, W1, W2, head_id=None, act=None, out=None, workspace=Non
         raise ValueError("codebook_head_mlp: shape mismatch")
     if head_id is not None:
         _cuda("head_id", head_id, torch.int32, 1)
+        _rows("codebook_head_mlp", M, head_id=head_id)
     if act is None:
         act = torch.empty((M, F), dtype=torch.bfloat16, device=h.device)
     else:
@@ -400,6 +414,8 @@ def sample_or_argmax(logits, temperature=None, uniforms=None, vocab_valid=None, 
                         ("vocab_valid", vocab_valid, torch.int32)):
         if t is not None:
             _cuda(name, t, dt, 1)
+            if t.shape[0] != M:
+                raise ValueError(f"{name} must have {M} entries (one per row), got {t.shape[0]}")
     if out is None:
         out = torch.empty(M, dtype=torch.int32, device=logits.device)
     else:
@@ -423,7 +439,8 @@ def spec_verify(target_logits, draft_probs, draft_tokens, u_accept, u_resample, 
     _cuda("u_accept", u_accept, torch.float32, 2)
     _cuda("u_resample", u_resample, torch.float32, 1)
     B, K, V = target_logits.shape
-    if tuple(draft_probs.shape) != (B, K, V) or tuple(draft_tokens.shape) != (B, K):
+    if tuple(draft_probs.shape) != (B, K, V) or tuple(draft_tokens.shape) != (B, K) \
+            or tuple(u_accept.shape) != (B, K) or tuple(u_resample.shape) != (B,):
         raise ValueError("spec_verify: shape mismatch")
     if out_tokens is None:
         out_tokens = torch.empty((B, K), dtype=torch.int32, device=target_logits.device)
@@ -452,7 +469,8 @@ def spec_verify_bonus(target_logits, draft_probs, draft_tokens, u_accept, u_resa
     _cuda("u_accept", u_accept, torch.float32, 2)
     _cuda("u_resample", u_resample, torch.float32, 1)
     B, K, V = draft_probs.shape
-    if tuple(target_logits.shape) != (B, K + 1, V) or tuple(draft_tokens.shape) != (B, K):
+    if tuple(target_logits.shape) != (B, K + 1, V) or tuple(draft_tokens.shape) != (B, K) \
+            or tuple(u_accept.shape) != (B, K) or tuple(u_resample.shape) != (B,):
         raise ValueError("spec_verify_bonus: shape mismatch")
     if out_tokens is None:
         out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=target_logits.device)

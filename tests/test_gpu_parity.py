@@ -989,3 +989,44 @@ def test_decode_attention_closed_forms(clm_gpu, Kq):
     vals5 = [vf[bt[5, np.arange(64) // bs], :, :, np.arange(64) % bs]]
     ref5 = oracle.decode_attention(qf[5:6], keys5, vals5, kv_len[5:6], scale, Hk)
     check_close(of[5:6], ref5, "scores of magnitude ~100")
+
+
+def test_binding_rejects_short_per_row_arrays(clm_gpu):
+    """The binding refuses per-stream and per-row arrays shorter than the
+    batch before any launch (a kernel would read past their ends)."""
+    import torch
+    dev = torch.device("cuda")
+    B, Kq, Hq, Hk, D, bs, nb, V = 4, 2, 16, 8, 128, 16, 8, 64
+    q = torch.zeros((B, Kq, Hq, D), dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros((nb, Hk, bs, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros((nb, Hk, D, bs), dtype=torch.bfloat16, device=dev)
+    bt = torch.zeros((B, 2), dtype=torch.int32, device=dev)
+    kl = torch.full((B,), 4, dtype=torch.int32, device=dev)
+    short = torch.zeros(B - 1, dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        clm_gpu.decode_attention(q, kc, vc, bt, short, 16)
+    with pytest.raises(ValueError):
+        clm_gpu.decode_attention(q, kc, vc, bt[:B - 1], kl, 16)
+    k8 = torch.zeros((nb, Hk, D // 8, bs, 8), dtype=torch.uint8, device=dev)
+    v8 = torch.zeros((nb, Hk, D, bs), dtype=torch.uint8, device=dev)
+    sc = torch.ones((nb, Hk, bs), dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError):
+        clm_gpu.decode_attention_fp8(q, k8, v8, sc, sc, bt, short, 16)
+    kn = torch.zeros((B, Kq, Hk, D), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        clm_gpu.kv_cache_append_fp8(kn, kn, k8, v8, sc, sc, bt, short)
+    logits = torch.zeros((B, V), dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError):
+        clm_gpu.sample_or_argmax(logits, torch.ones(B - 1, device=dev), torch.ones(B - 1, device=dev))
+    with pytest.raises(ValueError):
+        clm_gpu.sample_or_argmax(logits, vocab_valid=short)
+    tl = torch.zeros((B, Kq, V), dtype=torch.float32, device=dev)
+    dt = torch.zeros((B, Kq), dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        clm_gpu.spec_verify(tl, tl, dt, torch.zeros((B, Kq - 1), device=dev), torch.zeros(B, device=dev), 0.7)
+    with pytest.raises(ValueError):
+        clm_gpu.spec_verify(tl, tl, dt, torch.zeros((B, Kq), device=dev), torch.zeros(B - 1, device=dev), 0.7)
+    h = torch.zeros((B, Hq * D), dtype=torch.bfloat16, device=dev)
+    W = torch.zeros((2, V, Hq * D), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        clm_gpu.codebook_head(h, W, short)
