@@ -478,9 +478,6 @@ def main():
             import dataclasses
             cfg = dataclasses.replace(cfg, block_size=args.block_size)
         graph = args.graph == "on"
-        if graph and args.head != "linear":
-            print("--graph on runs the decode loop of the linear head", file=sys.stderr)
-            sys.exit(2)
         if args.kv == "fp8" and args.append == "rope":
             print("--append rope has no FP8 form (the rotary append writes bf16 or fp32 rows)", file=sys.stderr)
             sys.exit(2)
@@ -628,6 +625,8 @@ def main():
                       max_kv_len=max_kv, k_new=rep(k_new), v_new=rep(v_new), q=rep(q), W=W, head_id=head_id,
                       o=torch.empty_like(rep(q)), logits=lg_all, mode=c.mode, attn_workspace=ws,
                       block_size=c.block_size)
+            if mlp is not None:
+                lp.update(W=mlp[0], W2=mlp[1], act=mlp[2])
             if rope_pos is not None:
                 lp.update(positions=rope_pos, rope_base=1.0e6)
             if c.mode == "spec":

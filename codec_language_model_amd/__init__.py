@@ -521,6 +521,9 @@ class DecodeLoop:
     kv_cache_append_fp8 (uint8 k_cache [nb, H_kv, D/8, bs, 8], v_cache [nb,
     H_kv, D, bs], float32 scales [nb, H_kv, bs]); q, k_new and v_new are then
     bf16, an attention workspace is required and positions are not taken.
+    With W2 the head has two layers (codebook_head_mlp): W holds the first
+    layer [G, F, H_q*D] and W2 the second [G, V, F], bf16; act [B*Kq, F] bf16
+    is the activation scratch (allocated when None).
     mode: "greedy", "sample", "spec" or "spec_bonus" (verification with a
     bonus token: the Kq queries score the last kept token and Kq - 1 drafts,
     so draft_probs is [n, B, Kq-1, V], draft_tokens and u_accept [n, B,
@@ -534,7 +537,7 @@ class DecodeLoop:
                  logits, head_id=None, positions=None, rope_base=1.0e6, mode="greedy", tokens=None,
                  temperature=None, uniforms=None, spec_temperature=0.0, draft_probs=None, draft_tokens=None,
                  u_accept=None, u_resample=None, out_tokens=None, num_emitted=None, attn_workspace=None,
-                 block_size=16, k_scale=None, v_scale=None):
+                 block_size=16, k_scale=None, v_scale=None, W2=None, act=None):
         torch = _torch()
         self._lib = load()
         self._h = None
@@ -569,10 +572,26 @@ class DecodeLoop:
             _out("positions", positions, (B, Kq), torch.int32)
         Ws = [W[g] for g in range(W.shape[0])] if isinstance(W, torch.Tensor) and W.dim() == 3 else list(W)
         G = len(Ws)
-        V = Ws[0].shape[0]
-        for i, w in enumerate(Ws):
-            _out(f"W[{i}]", w, (V, H_q * D), dt)
         M = B * Kq
+        W2s, F = None, 0
+        if W2 is not None:
+            if dt != torch.bfloat16:
+                raise ValueError("DecodeLoop: the two-layer head takes bf16")
+            W2s = [W2[g] for g in range(W2.shape[0])] if isinstance(W2, torch.Tensor) and W2.dim() == 3 \
+                else list(W2)
+            if len(W2s) != G:
+                raise ValueError("DecodeLoop: W and W2 need one matrix per stage each")
+            F, V = Ws[0].shape[0], W2s[0].shape[0]
+            for i, (a, b2) in enumerate(zip(Ws, W2s)):
+                _out(f"W[{i}]", a, (F, H_q * D), dt)
+                _out(f"W2[{i}]", b2, (V, F), dt)
+            if act is None:
+                act = torch.empty((M, F), dtype=torch.bfloat16, device=q.device)
+            _out("act", act, (M, F), torch.bfloat16)
+        else:
+            V = Ws[0].shape[0]
+            for i, w in enumerate(Ws):
+                _out(f"W[{i}]", w, (V, H_q * D), dt)
         _out("logits", logits, (n, M, V), torch.float32)
         if head_id is not None:
             _out("head_id", head_id, (M,), torch.int32)
@@ -596,9 +615,10 @@ class DecodeLoop:
         if attn_workspace is not None:
             _cuda("attn_workspace", attn_workspace, torch.uint8, 1)
         self._warr = (C.c_void_p * G)(*[w.data_ptr() for w in Ws])
+        self._w2arr = None if W2s is None else (C.c_void_p * G)(*[w.data_ptr() for w in W2s])
         self._keep = [k_cache, v_cache, block_table, len_before, kv_len, positions, k_new, v_new, q, Ws, head_id,
                       o, logits, tokens, temperature, uniforms, draft_probs, draft_tokens, u_accept, u_resample,
-                      out_tokens, num_emitted, attn_workspace, k_scale, v_scale]
+                      out_tokens, num_emitted, attn_workspace, k_scale, v_scale, W2s, act]
         p = lambda t: 0 if t is None else t.data_ptr()
         d = _lib.DecodeStepDesc(
             B=B, Kq=Kq, H_q=H_q, H_kv=H_kv, D=D, block_size=block_size, num_blocks=nb,
@@ -610,7 +630,8 @@ class DecodeLoop:
             mode=self._MODES[mode], temperature=p(temperature), uniforms=p(uniforms), tokens=p(tokens),
             spec_temperature=float(spec_temperature), draft_probs=p(draft_probs), draft_tokens=p(draft_tokens),
             u_accept=p(u_accept), u_resample=p(u_resample), out_tokens=p(out_tokens), num_emitted=p(num_emitted),
-            k_scale=p(k_scale), v_scale=p(v_scale))
+            k_scale=p(k_scale), v_scale=p(v_scale),
+            W2=None if W2s is None else C.cast(self._w2arr, C.c_void_p).value, F=F, act=p(act))
         h = C.c_void_p()
         _check("clm_decode_loop_create", self._lib.clm_decode_loop_create(C.byref(d), n, C.byref(h)))
         self._h = h

@@ -64,7 +64,7 @@ class DecodeStepDesc(C.Structure):
         ("mode", _i), ("temperature", _vp), ("uniforms", _vp), ("tokens", _vp),
         ("spec_temperature", _f), ("draft_probs", _vp), ("draft_tokens", _vp), ("u_accept", _vp),
         ("u_resample", _vp), ("out_tokens", _vp), ("num_emitted", _vp),
-        ("k_scale", _vp), ("v_scale", _vp),
+        ("k_scale", _vp), ("v_scale", _vp), ("W2", _vp), ("F", _i), ("act", _vp),
     ]
 
 

@@ -72,7 +72,9 @@ int record_step(const clm_decode_step_desc& d, int s, hipStream_t st) {
                                       scale, d.dt, st);
   if (rc != CLM_OK) return rc;
   float* logits = step_ptr(d.logits, s, (size_t)M * d.V * sizeof(float));
-  rc = clm_codebook_head(o, d.W, d.G, d.head_id, logits, M, d.H_q * d.D, d.V, d.dt, nullptr, 0, st);
+  rc = d.W2 ? clm_codebook_head_mlp(o, d.W, d.W2, d.G, d.head_id, d.act, logits, M, d.H_q * d.D, d.F, d.V, d.dt,
+                                     nullptr, 0, st)
+            : clm_codebook_head(o, d.W, d.G, d.head_id, logits, M, d.H_q * d.D, d.V, d.dt, nullptr, 0, st);
   if (rc != CLM_OK) return rc;
   const int32_t* emitted = nullptr;
   if (d.mode == 2 || d.mode == 3) {
@@ -114,6 +116,8 @@ int check_desc(const clm_decode_step_desc& d) {
     return CLM_ERR_INVALID_ARG;
   }
   if (!d.k_scale != !d.v_scale) return CLM_ERR_INVALID_ARG;
+  if (d.W2 && (!d.act || d.F < 1)) return CLM_ERR_INVALID_ARG;
+  if (d.W2 && d.dt != CLM_BF16) return CLM_ERR_UNSUPPORTED;
   if (d.k_scale && (d.dt != CLM_BF16 || d.positions || !d.attn_workspace)) return CLM_ERR_UNSUPPORTED;
   return CLM_OK;
 }

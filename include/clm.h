@@ -415,7 +415,8 @@ int clm_advance_lengths(int32_t* len_before, int32_t* kv_len, int32_t* positions
  * One decode step per loop iteration, as the calls above would run it:
  *   append (rotary at logical positions when positions != NULL; the
  *   quantizing append when k_scale != NULL) -> attention (score scale
- *   1/sqrt(D); over the FP8 cache when k_scale != NULL) -> head -> token
+ *   1/sqrt(D); over the FP8 cache when k_scale != NULL) -> head (two
+ *   layers with Mish when W2 != NULL) -> token
  *   choice (greedy, sampling or speculative verification) ->
  *   clm_advance_lengths.
  * Step s (0 <= s < n_steps) reads and writes slice s of each per-step array
@@ -464,6 +465,12 @@ typedef struct clm_decode_step_desc {
                                        cache of element type dt.  FP8 needs dt = CLM_BF16 and a
                                        caller attn_workspace; positions must be NULL (UNSUPPORTED
                                        otherwise: there is no rotary FP8 append) */
+  const void* const* W2;            /* two-layer head (clm_codebook_head_mlp): host array of G
+                                       device pointers, each [V, F]; W then holds the first layer,
+                                       each [F, H_q*D].  NULL: the one-layer head */
+  int F;                            /*   two-layer head: the widened size */
+  void* act;                        /*   two-layer head: [B*Kq, F] bf16 activation scratch, reused
+                                       by every step; bf16 only (UNSUPPORTED otherwise) */
 } clm_decode_step_desc;
 
 typedef struct clm_decode_loop clm_decode_loop;   /* opaque */
@@ -476,9 +483,10 @@ typedef struct clm_decode_loop clm_decode_loop;   /* opaque */
  * Checked mode must be off (it synchronises): UNSUPPORTED otherwise.
  * Errors: INVALID_ARG (null desc/loop, n_steps out of range, a null array the
  *   mode needs, mode not 0..3, mode 3 with Kq < 2, one FP8 scale array
- *   without the other),
+ *   without the other, a two-layer head without act or with F < 1),
  *   UNSUPPORTED (an FP8 cache with dt other than CLM_BF16, with positions or
- *   without attn_workspace), the individual calls' errors, HIP.
+ *   without attn_workspace; a two-layer head with dt other than CLM_BF16),
+ *   the individual calls' errors, HIP.
  */
 int clm_decode_loop_create(const clm_decode_step_desc* desc, int n_steps, clm_decode_loop** loop);
 

@@ -128,6 +128,11 @@ int main() {
   d.attn_workspace = P; d.attn_workspace_bytes = 1 << 20;
   EXPECT(clm_decode_loop_create(&d, 4, &loop), HIP);       // FP8 loop: no device either
   d.k_scale = d.v_scale = nullptr; d.attn_workspace = nullptr; d.attn_workspace_bytes = 0;
+  d.W2 = Ws; d.F = 4096;                                   // two-layer head without its activation scratch
+  EXPECT(clm_decode_loop_create(&d, 4, &loop), INV);
+  d.act = P; d.dt = CLM_F32;                               // two-layer head takes bf16 only
+  EXPECT(clm_decode_loop_create(&d, 4, &loop), UNS);
+  d.W2 = nullptr; d.F = 0; d.act = nullptr; d.dt = CLM_BF16;
   EXPECT(clm_decode_loop_create(&d, 4, &loop), HIP);       // no device: capture cannot start
   EXPECT((int)(loop == nullptr), 1);
   EXPECT(clm_decode_loop_launch(nullptr, S), INV);

@@ -315,6 +315,11 @@ def test_decode_loop_host_checks(lib):
     d.positions, d.dt = 0, 0
     assert create(C.byref(d), 4, C.byref(h)) == UNSUPPORTED      # bf16 queries only
     d.dt, d.k_scale, d.v_scale, d.attn_workspace, d.attn_workspace_bytes = 1, 0, 0, 0, 0
+    d.W2, d.F = 0x100000, 4096                                   # two-layer head: the activation scratch ...
+    assert create(C.byref(d), 4, C.byref(h)) == INVALID
+    d.act, d.dt = 0x100000, 0
+    assert create(C.byref(d), 4, C.byref(h)) == UNSUPPORTED      # ... and bf16
+    d.W2, d.F, d.act, d.dt = 0, 0, 0, 1
     prev = lib.clm_set_checked(1)
     try:
         assert create(C.byref(d), 4, C.byref(h)) == UNSUPPORTED  # checked mode synchronises

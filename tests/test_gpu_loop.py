@@ -38,7 +38,8 @@ def _pages(n, bs):
     return (np.asarray(n, np.int64) + bs - 1) // bs
 
 
-def _loop_case(clm_gpu, cfg, B_live, B_cap, n_steps, rope=False, use_ws=True, replay=False, bonus=False):
+def _loop_case(clm_gpu, cfg, B_live, B_cap, n_steps, rope=False, use_ws=True, replay=False, bonus=False,
+               mlp=False):
     import torch
     x = synth.make_inputs(cfg, B=B_live)
     c = x.cfg
@@ -68,6 +69,15 @@ def _loop_case(clm_gpu, cfg, B_live, B_cap, n_steps, rope=False, use_ws=True, re
     g = dict(k_cache=k_cache, v_cache=v_cache, block_table=T(bt), len_before=T(lb0), kv_len=T(lb0 + Kq),
              k_new=T(k_new, bf), v_new=T(v_new, bf), q=T(q_all, bf), W=T(x.W, bf),
              head_id=None if head_id is None else T(head_id))
+    mlp_w = None
+    if mlp:             # TontaubeV1's two-layer head: d -> 4096 -> Mish -> V per stage, N(0, 0.02) weights
+        assert c.mode == "greedy" and bf
+        wr = np.random.default_rng(4096 + cfg)
+        F = 4096
+        W1 = synth.f32_to_bf16_bits((wr.standard_normal((c.G, F, c.d_model)) * 0.02).astype(np.float32))
+        W2 = synth.f32_to_bf16_bits((wr.standard_normal((c.G, V, F)) * 0.02).astype(np.float32))
+        mlp_w = (f32(W1), f32(W2))
+        g["W"], g["W2"] = T(W1, True), T(W2, True)
     g["o"] = torch.empty_like(g["q"])
     g["logits"] = torch.empty((n_steps, M_cap, V), dtype=torch.float32, device=dev)
     if rope:
@@ -127,7 +137,12 @@ def _loop_case(clm_gpu, cfg, B_live, B_cap, n_steps, rope=False, use_ws=True, re
         vs = [np.concatenate([vals[b], vf[b]]) for b in range(B_live)]
         kv_len = (lb + Kq).astype(np.int32)
         sp = spec_np[s] if spec_np else None
-        if bonus:           # attention and logits as in any step, then the bonus-token verification
+        if mlp:             # attention as in any step, then the two-layer head and the argmax
+            ref = oracle.decode_step(qf, ks, vs, kv_len, scale, Hk, Wf, x.head_id if c.G > 1 else None, bf)
+            _, lg = oracle.codebook_head_mlp(ref["h"], mlp_w[0], mlp_w[1], x.head_id if c.G > 1 else None)
+            ref["logits"] = lg.astype(np.float32)
+            ref["tokens"] = oracle.sample_or_argmax(ref["logits"])
+        elif bonus:         # attention and logits as in any step, then the bonus-token verification
             ref = oracle.decode_step(qf, ks, vs, kv_len, scale, Hk, Wf, None, bf)
             ref["out_tokens"], ref["num_emitted"] = oracle.spec_verify(
                 ref["logits"].reshape(B_live, Kq, V), sp["draft_probs"], sp["draft_tokens"], sp["u_accept"],
@@ -239,6 +254,13 @@ def test_loop_sampling_padded_bucket_static_scratch(clm_gpu):
     sizes = [16, 64, 256]
     assert clm_gpu.pick_bucket(sizes, 12) == 0
     _loop_case(clm_gpu, 2, 12, sizes[clm_gpu.pick_bucket(sizes, 12)], 3, use_ws=False)
+
+
+def test_loop_two_layer_head(clm_gpu):
+    """TontaubeV1's two-layer Mish head in the loop: 64 streams over three
+    stage heads, 3 steps, greedy; the activation scratch is reused by every
+    step."""
+    _loop_case(clm_gpu, 3, 64, 64, 3, mlp=True)
 
 
 def test_loop_grouped_heads_and_fp32(clm_gpu):
