@@ -478,9 +478,6 @@ def main():
             import dataclasses
             cfg = dataclasses.replace(cfg, block_size=args.block_size)
         graph = args.graph == "on"
-        if args.kv == "fp8" and args.append == "rope":
-            print("--append rope has no FP8 form (the rotary append writes bf16 or fp32 rows)", file=sys.stderr)
-            sys.exit(2)
         t_gen = time.perf_counter()
         x = synth.make_inputs(cfg)
         c = x.cfg
@@ -575,7 +572,10 @@ def main():
             rep_i[0] += 1
             if ev is not None:
                 ev[0].record()
-            if f8 is not None:
+            if f8 is not None and rope_pos is not None:
+                clm.rope_kv_cache_append_fp8(q, k_new, v_new, *kvs, bt, len_before, rope_pos, 1.0e6,
+                                             block_size=c.block_size)
+            elif f8 is not None:
                 clm.kv_cache_append_fp8(k_new, v_new, *kvs, bt, len_before, block_size=c.block_size)
             elif rope_pos is None:
                 clm.kv_cache_append(k_new, v_new, kvs[0], kvs[1], bt, len_before, block_size=c.block_size)

@@ -25,7 +25,7 @@ __all__ = [
     "decode_attention_fp8", "decode_attention_workspace_size", "decode_attention_noalloc",
     "codebook_head", "codebook_head_mlp", "codebook_head_workspace_size", "codebook_head_mlp_workspace_size",
     "sample_or_argmax", "spec_verify", "spec_verify_bonus",
-    "Workspace", "set_checked", "advance_lengths", "DecodeLoop", "pick_bucket",
+    "rope_kv_cache_append_fp8", "Workspace", "set_checked", "advance_lengths", "DecodeLoop", "pick_bucket",
 ]
 
 
@@ -201,6 +201,38 @@ def kv_cache_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_
     _check("clm_kv_cache_append_fp8", lib.clm_kv_cache_append_fp8(
         _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
         block_table.shape[1], _ptr(len_before), B, T, H, D, block_size, nb, _stream()))
+
+
+def rope_kv_cache_append_fp8(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, len_before,
+                             positions, rope_base, block_size=16):
+    """kv_cache_append_fp8 with the rotary embedding of rope_kv_cache_append:
+    keys rotated (fp32) then quantized, q [B,T,H_q,D] bf16 rotated in place,
+    values quantized unrotated.  positions [B,T] int32."""
+    torch = _torch()
+    lib = load()
+    _cuda("q", q, torch.bfloat16, 4)
+    _cuda("k_new", k_new, torch.bfloat16, 4)
+    _cuda("v_new", v_new, torch.bfloat16, 4)
+    _cuda("k_cache", k_cache, torch.uint8, 5)
+    _cuda("v_cache", v_cache, torch.uint8, 4)
+    _cuda("k_scale", k_scale, torch.float32, 3)
+    _cuda("v_scale", v_scale, torch.float32, 3)
+    _cuda("block_table", block_table, torch.int32, 2)
+    _cuda("len_before", len_before, torch.int32, 1)
+    _cuda("positions", positions, torch.int32, 2)
+    B, T, H, D = k_new.shape
+    H_q = q.shape[2]
+    nb = k_cache.shape[0]
+    if tuple(q.shape) != (B, T, H_q, D) or tuple(v_new.shape) != (B, T, H, D) \
+            or tuple(k_cache.shape) != (nb, H, D // 8, block_size, 8) or tuple(v_cache.shape) != (nb, H, D, block_size) \
+            or tuple(k_scale.shape) != (nb, H, block_size) or tuple(v_scale.shape) != (nb, H, block_size) \
+            or tuple(positions.shape) != (B, T):
+        raise ValueError("rope_kv_cache_append_fp8: shape mismatch")
+    _rows("rope_kv_cache_append_fp8", B, block_table=block_table, len_before=len_before)
+    _check("clm_rope_kv_cache_append_fp8", lib.clm_rope_kv_cache_append_fp8(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), block_table.shape[1], _ptr(len_before), _ptr(positions), C.c_float(rope_base), B, T,
+        H_q, H, D, block_size, nb, _stream()))
 
 
 def decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len) -> int:
@@ -520,7 +552,8 @@ class DecodeLoop:
     With k_scale / v_scale the cache is FP8 (E4M3) as for
     kv_cache_append_fp8 (uint8 k_cache [nb, H_kv, D/8, bs, 8], v_cache [nb,
     H_kv, D, bs], float32 scales [nb, H_kv, bs]); q, k_new and v_new are then
-    bf16, an attention workspace is required and positions are not taken.
+    bf16 and an attention workspace is required (with positions, the steps
+    append by rope_kv_cache_append_fp8).
     With W2 the head has two layers (codebook_head_mlp): W holds the first
     layer [G, F, H_q*D] and W2 the second [G, V, F], bf16; act [B*Kq, F] bf16
     is the activation scratch (allocated when None).

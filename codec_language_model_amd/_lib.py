@@ -38,6 +38,8 @@ SIGNATURES = {
     "clm_decode_attention_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
                                           _f, _i, _vp]),
     "clm_kv_cache_append_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "clm_rope_kv_cache_append_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _f, _i, _i, _i, _i,
+                                          _i, _i, _i, _vp]),
     "clm_decode_attention_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
                                       _f, _vp, _sz, _vp]),
     "clm_codebook_head_workspace_size": (_sz, [_i, _i, _i, _i, _i]),

@@ -231,6 +231,41 @@ int clm_kv_cache_append_fp8(const void* k_new, const void* v_new, void* k_cache,
   return hip_status(clm::launch_fp8_kv_append(a, stream));
 }
 
+int clm_rope_kv_cache_append_fp8(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 float* k_scale, float* v_scale, const int32_t* block_table, int max_blocks,
+                                 const int32_t* len_before, const int32_t* positions, float rope_base, int B,
+                                 int T_new, int H_q, int H_kv, int D, int block_size, int num_blocks,
+                                 hipStream_t stream) {
+  if (!q || !positions) return CLM_ERR_INVALID_ARG;
+  if (H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return CLM_ERR_INVALID_ARG;
+  if (!std::isfinite(rope_base) || !(rope_base > 1.f)) return CLM_ERR_INVALID_ARG;
+  if (!aligned(q, 16)) return CLM_ERR_INVALID_ARG;
+  if (!k_new || !v_new || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !len_before)
+    return CLM_ERR_INVALID_ARG;
+  if (B < 1 || T_new < 1 || D < 1 || max_blocks < 1 || num_blocks < 1 || block_size < 1)
+    return CLM_ERR_INVALID_ARG;
+  if ((D != 64 && D != 128) || !bs_ok(block_size)) return CLM_ERR_UNSUPPORTED;
+  if ((long)T_new > (long)max_blocks * block_size) return CLM_ERR_CAPACITY;
+  if ((long)B * H_kv > (1L << 31) - 1) return CLM_ERR_UNSUPPORTED;
+  if (checked()) {
+    const long lim = (long)max_blocks * block_size - T_new;
+    int st = run_checks(stream, [&](int* bad) {
+      hipError_t e = clm::launch_check_lengths(len_before, B, 0, (int)(lim > 0x7fffffff ? 0x7fffffff : lim), bad, stream);
+      if (e != hipSuccess) return e;
+      return clm::launch_check_block_table(block_table, len_before, B, max_blocks, T_new, block_size,
+                                           num_blocks, bad, stream);
+    });
+    if (st != CLM_OK) return st;
+  }
+  clm::Fp8AppendArgs a{k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, len_before,
+                       max_blocks, B, T_new, H_kv, D, block_size, num_blocks};
+  a.q = q;
+  a.positions = positions;
+  a.rope_base = rope_base;
+  a.H_q = H_q;
+  return hip_status(clm::launch_fp8_kv_append(a, stream));
+}
+
 int clm_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
                              const float* v_scale, const int32_t* block_table, int max_blocks,
                              const int32_t* kv_len, int max_kv_len, void* o, int B, int Kq, int H_q, int H_kv,

@@ -46,6 +46,11 @@ struct Fp8AppendArgs {
   const int32_t* block_table;
   const int32_t* len_before;
   int max_blocks, B, T_new, H_kv, D, block_size, num_blocks;
+  // rotary embedding at logical positions (q == nullptr: none)
+  void* q = nullptr;                  // [B, T_new, H_q, D] bf16, rotated in place
+  const int32_t* positions = nullptr; // [B, T_new]
+  float rope_base = 0.f;
+  int H_q = 0;
 };
 hipError_t launch_fp8_kv_append(const Fp8AppendArgs& a, hipStream_t s);
 

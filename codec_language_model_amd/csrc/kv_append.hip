@@ -175,11 +175,43 @@ struct Fp8AppendP {
   AppendP a;
   float* k_scale;     // [num_blocks, H_kv, bs]
   float* v_scale;
+  uint16_t* q;        // ROPE: [B, T_new, H_q, D] bf16, rotated in place
+  const int32_t* positions;
+  int H_q, G;
+  double log_base;
 };
+
+// cos and sin of pair i's angle at logical position p, with the very
+// expressions of rope_append_kernel (fp64, then fp32).
+template <int D>
+__device__ __forceinline__ void rope_cs(int p, int i, double log_base, float& c, float& s) {
+  const double th = exp(-2.0 * (double)i / (double)D * log_base);
+  const double ang = (double)p * th;
+  c = (float)cos(ang);
+  s = (float)sin(ang);
+}
+
+// The pair partner of the value this lane holds in slot k: lane l holds
+// dimensions l + 64k, so at D = 128 the pair (i, i + 64) sits in one lane and
+// at D = 64 the pair (i, i + 32) sits in lanes i and i + 32.
+template <int D>
+__device__ __forceinline__ void rope_row(float (&x)[D / 64], int lane, float c, float s) {
+  if constexpr (D == 128) {
+    const float x0 = x[0], x1 = x[1];
+    x[0] = x0 * c - x1 * s;
+    x[1] = x0 * s + x1 * c;
+  } else {
+    const float other = __shfl_xor(x[0], 32, 64);
+    x[0] = lane < 32 ? x[0] * c - other * s : other * s + x[0] * c;
+  }
+}
 
 // One workgroup of 2 waves per (stream, KV head): wave 0 quantizes and writes
 // the key row of each new token, wave 1 the value row (transposed block).
-template <int D>
+// ROPE: wave 0 rotates the key row (fp32, from its bf16 values) before
+// quantizing it, and wave 1 rotates the G query rows of this KV head in
+// place after writing the value row.
+template <int D, bool ROPE>
 __global__ __launch_bounds__(128) void fp8_append_kernel(Fp8AppendP F) {
   const AppendP& P = F.a;
   const int b = blockIdx.x / P.H_kv;
@@ -198,7 +230,26 @@ __global__ __launch_bounds__(128) void fp8_append_kernel(Fp8AppendP F) {
     uint32_t code[D / 64];
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) x[i] = bf16_to_f32(row[lane + 64 * i]);
+    float rc = 1.f, rs = 0.f;
+    if constexpr (ROPE) {
+      rope_cs<D>(F.positions[b * P.T_new + t], lane % (D / 2), F.log_base, rc, rs);
+      if (w == 0) rope_row<D>(x, lane, rc, rs);
+    }
     const float scale = quantize_row<D>(x, code);
+    if constexpr (ROPE) {
+      if (w == 1) {
+        // the G query heads of this KV head, in place (rope_append_kernel's arithmetic)
+        for (int gi = 0; gi < F.G; ++gi) {
+          uint16_t* qrow = F.q + ((size_t)(b * P.T_new + t) * F.H_q + h * F.G + gi) * D;
+          if (lane < D / 2) {
+            const int i = lane;
+            const float x0 = bf16_to_f32(qrow[i]), x1 = bf16_to_f32(qrow[i + D / 2]);
+            qrow[i] = f32_to_bf16(x0 * rc - x1 * rs);
+            qrow[i + D / 2] = f32_to_bf16(x0 * rs + x1 * rc);
+          }
+        }
+      }
+    }
     const int pos = lb + t;
     if (pos < 0) continue;
     const int page = pos / P.bs;
@@ -279,9 +330,17 @@ hipError_t launch_fp8_kv_append(const Fp8AppendArgs& a, hipStream_t s) {
                 a.max_blocks, a.T_new, a.H_kv, a.block_size, a.num_blocks};
   F.k_scale = a.k_scale;
   F.v_scale = a.v_scale;
+  F.q = static_cast<uint16_t*>(a.q);
+  F.positions = a.positions;
+  F.H_q = a.H_q;
+  F.G = a.q ? a.H_q / a.H_kv : 0;
+  F.log_base = a.q ? log((double)a.rope_base) : 0.0;
   const dim3 grid(a.B * a.H_kv), block(128);
-  if (a.D == 128) hipLaunchKernelGGL((fp8_append_kernel<128>), grid, block, 0, s, F);
-  else if (a.D == 64) hipLaunchKernelGGL((fp8_append_kernel<64>), grid, block, 0, s, F);
+  const bool rope = a.q != nullptr;
+  if (a.D == 128 && rope) hipLaunchKernelGGL((fp8_append_kernel<128, true>), grid, block, 0, s, F);
+  else if (a.D == 128) hipLaunchKernelGGL((fp8_append_kernel<128, false>), grid, block, 0, s, F);
+  else if (a.D == 64 && rope) hipLaunchKernelGGL((fp8_append_kernel<64, true>), grid, block, 0, s, F);
+  else if (a.D == 64) hipLaunchKernelGGL((fp8_append_kernel<64, false>), grid, block, 0, s, F);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

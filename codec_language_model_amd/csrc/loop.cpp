@@ -45,7 +45,11 @@ int record_step(const clm_decode_step_desc& d, int s, hipStream_t st) {
   const void* vn = step_ptr(d.v_new, s, kv_step);
   const bool f8 = d.k_scale != nullptr;
   int rc;
-  if (f8)
+  if (f8 && d.positions)
+    rc = clm_rope_kv_cache_append_fp8(q, kn, vn, d.k_cache, d.v_cache, d.k_scale, d.v_scale, d.block_table,
+                                      d.max_blocks, d.len_before, d.positions, d.rope_base, d.B, d.Kq, d.H_q,
+                                      d.H_kv, d.D, d.block_size, d.num_blocks, st);
+  else if (f8)
     rc = clm_kv_cache_append_fp8(kn, vn, d.k_cache, d.v_cache, d.k_scale, d.v_scale, d.block_table, d.max_blocks,
                                  d.len_before, d.B, d.Kq, d.H_kv, d.D, d.block_size, d.num_blocks, st);
   else if (d.positions)
@@ -118,7 +122,7 @@ int check_desc(const clm_decode_step_desc& d) {
   if (!d.k_scale != !d.v_scale) return CLM_ERR_INVALID_ARG;
   if (d.W2 && (!d.act || d.F < 1)) return CLM_ERR_INVALID_ARG;
   if (d.W2 && d.dt != CLM_BF16) return CLM_ERR_UNSUPPORTED;
-  if (d.k_scale && (d.dt != CLM_BF16 || d.positions || !d.attn_workspace)) return CLM_ERR_UNSUPPORTED;
+  if (d.k_scale && (d.dt != CLM_BF16 || !d.attn_workspace)) return CLM_ERR_UNSUPPORTED;
   return CLM_OK;
 }
 

@@ -14,6 +14,7 @@
  *                          ragged cache (split-KV flash decoding)
  *   clm_kv_cache_append_fp8, clm_decode_attention_fp8
  *                          the same two calls for an FP8 (E4M3) cache
+ *   clm_rope_kv_cache_append_fp8  the rotary append into the FP8 cache
  *   clm_codebook_head      codebook logit projection, optionally grouped by
  *                          stage (one weight matrix per stage)
  *   clm_codebook_head_mlp  the two-layer (d -> F -> Mish -> V) form of that head
@@ -247,6 +248,23 @@ int clm_kv_cache_append_fp8(const void* k_new, const void* v_new, void* k_cache,
                             int num_blocks, hipStream_t stream);
 
 /*
+ * clm_rope_kv_cache_append for the FP8 cache: the rotary embedding of
+ * clm_rope_kv_cache_append (same angles, fp64, and the same fp32 rotation) is
+ * applied to each new key row, which is then quantized from its fp32 values
+ * as clm_kv_cache_append_fp8 quantizes a row; values are quantized
+ * unrotated; q (bf16) is rotated in place exactly as clm_rope_kv_cache_append
+ * rotates it.  q, k_new, v_new bf16; caches and scales as
+ * clm_kv_cache_append_fp8.  Errors as clm_kv_cache_append_fp8, plus those
+ * clm_rope_kv_cache_append adds (null q or positions, H_q % H_kv != 0,
+ * rope_base not finite or <= 1, q not 16-byte aligned).
+ */
+int clm_rope_kv_cache_append_fp8(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 float* k_scale, float* v_scale, const int32_t* block_table, int max_blocks,
+                                 const int32_t* len_before, const int32_t* positions, float rope_base, int B,
+                                 int T_new, int H_q, int H_kv, int D, int block_size, int num_blocks,
+                                 hipStream_t stream);
+
+/*
  * clm_decode_attention over the FP8 cache: q and o bf16, the same visibility,
  * scale and split plan (workspace: clm_decode_attention_workspace_size).
  * Keys and values are decoded to bf16 exactly in registers; scores are
@@ -414,7 +432,8 @@ int clm_advance_lengths(int32_t* len_before, int32_t* kv_len, int32_t* positions
 /*
  * One decode step per loop iteration, as the calls above would run it:
  *   append (rotary at logical positions when positions != NULL; the
- *   quantizing append when k_scale != NULL) -> attention (score scale
+ *   quantizing append when k_scale != NULL; both: the rotary FP8 append)
+ *   -> attention (score scale
  *   1/sqrt(D); over the FP8 cache when k_scale != NULL) -> head (two
  *   layers with Mish when W2 != NULL) -> token
  *   choice (greedy, sampling or speculative verification) ->
@@ -463,8 +482,8 @@ typedef struct clm_decode_step_desc {
   float* v_scale;                   /*   [num_blocks, H_kv, block_size] of clm_kv_cache_append_fp8,
                                        with k_cache / v_cache in its byte layouts; both NULL for a
                                        cache of element type dt.  FP8 needs dt = CLM_BF16 and a
-                                       caller attn_workspace; positions must be NULL (UNSUPPORTED
-                                       otherwise: there is no rotary FP8 append) */
+                                       caller attn_workspace (UNSUPPORTED otherwise); with positions
+                                       the step appends by clm_rope_kv_cache_append_fp8 */
   const void* const* W2;            /* two-layer head (clm_codebook_head_mlp): host array of G
                                        device pointers, each [V, F]; W then holds the first layer,
                                        each [F, H_q*D].  NULL: the one-layer head */
@@ -484,8 +503,8 @@ typedef struct clm_decode_loop clm_decode_loop;   /* opaque */
  * Errors: INVALID_ARG (null desc/loop, n_steps out of range, a null array the
  *   mode needs, mode not 0..3, mode 3 with Kq < 2, one FP8 scale array
  *   without the other, a two-layer head without act or with F < 1),
- *   UNSUPPORTED (an FP8 cache with dt other than CLM_BF16, with positions or
- *   without attn_workspace; a two-layer head with dt other than CLM_BF16),
+ *   UNSUPPORTED (an FP8 cache with dt other than CLM_BF16 or without
+ *   attn_workspace; a two-layer head with dt other than CLM_BF16),
  *   the individual calls' errors, HIP.
  */
 int clm_decode_loop_create(const clm_decode_step_desc* desc, int n_steps, clm_decode_loop** loop);

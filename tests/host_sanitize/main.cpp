@@ -55,6 +55,10 @@ int main() {
   EXPECT(clm_rope_kv_cache_append(P, P, P, P, P, I, 8, I, I, 1e6f, 4, 1, 16, 8, 128, 16, 64, CLM_BF16, S), HIP);
   EXPECT(clm_kv_cache_append_fp8(P, P, P, P, F, F, I, 8, I, 2, 1, 8, 64, 16, 100, S), HIP);
   EXPECT(clm_kv_cache_append_fp8(P, P, P, P, nullptr, F, I, 8, I, 2, 1, 8, 64, 16, 100, S), INV);
+  EXPECT(clm_rope_kv_cache_append_fp8(P, P, P, P, P, F, F, I, 8, I, I, 1e6f, 2, 1, 16, 8, 64, 16, 100, S), HIP);
+  EXPECT(clm_rope_kv_cache_append_fp8(nullptr, P, P, P, P, F, F, I, 8, I, I, 1e6f, 2, 1, 16, 8, 64, 16, 100, S), INV);
+  EXPECT(clm_rope_kv_cache_append_fp8(P, P, P, P, P, F, F, I, 8, I, I, 1e6f, 2, 1, 12, 8, 64, 16, 100, S), INV);
+  EXPECT(clm_rope_kv_cache_append_fp8(P, P, P, P, P, F, F, I, 8, I, I, 1e6f, 2, 1, 16, 8, 96, 16, 100, S), UNS);
 
   // attention: the workspace query, then the call
   const size_t need = clm_decode_attention_workspace_size(4, 1, 16, 8, 128, 1000);

@@ -236,6 +236,26 @@ def test_rope_append_argument_errors(lib):
     assert call(a11=1000) == CAPACITY                  # T_new > max_blocks * bs
 
 
+def test_rope_fp8_append_argument_errors(lib):
+    f = lib.clm_rope_kv_cache_append_fp8
+    args = [P, P, P, P, P, P, P, P, 8, P, P, C.c_float(1e6), 4, 1, 16, 8, 128, 16, 64, S]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=N) == INVALID                       # q missing
+    assert call(a5=N) == INVALID                       # a scale array missing
+    assert call(a10=N) == INVALID                      # positions missing
+    assert call(a11=C.c_float(0.5)) == INVALID         # base <= 1
+    assert call(a11=C.c_float(float("inf"))) == INVALID
+    assert call(a14=12) == INVALID                     # H_q % H_kv
+    assert call(a0=C.c_void_p(0x100008)) == INVALID    # q not 16-byte aligned
+    assert call(a16=96) == UNSUPPORTED                 # D
+    assert call(a17=24) == UNSUPPORTED                 # block size
+    assert call(a13=1000) == CAPACITY                  # T_new > max_blocks * bs
+
+
 def test_head_sampler_verify_argument_errors(lib):
     Ws = (C.c_void_p * 3)(0x100000, 0x200000, 0x300000)
     head = lib.clm_codebook_head
@@ -310,9 +330,7 @@ def test_decode_loop_host_checks(lib):
     d.v_scale = 0x100000
     assert create(C.byref(d), 4, C.byref(h)) == UNSUPPORTED      # ... and a caller workspace
     d.attn_workspace, d.attn_workspace_bytes = 0x100000, 1 << 20
-    d.positions = 0x100000
-    assert create(C.byref(d), 4, C.byref(h)) == UNSUPPORTED      # no rotary FP8 append
-    d.positions, d.dt = 0, 0
+    d.dt = 0
     assert create(C.byref(d), 4, C.byref(h)) == UNSUPPORTED      # bf16 queries only
     d.dt, d.k_scale, d.v_scale, d.attn_workspace, d.attn_workspace_bytes = 1, 0, 0, 0, 0
     d.W2, d.F = 0x100000, 4096                                   # two-layer head: the activation scratch ...

@@ -298,3 +298,52 @@ def test_fp8_append_special_rows(clm_gpu):
         np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=name)
     for name, got, want in (("key scales", dks, rks), ("value scales", dvs, rvs)):
         np.testing.assert_array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32), err_msg=name)
+
+
+@pytest.mark.parametrize("cfg,offset", [(4, 1000), (5, 123456)])
+def test_fp8_rope_append(clm_gpu, cfg, offset):
+    """The rotary append into the FP8 cache at logical positions len_before +
+    offset + t: the oracle rotates the new keys (fp64), then quantizes them
+    from float32 with its quantizer.  The kernel rotates in fp32, so a key
+    element whose scaled value sits at a rounding boundary may take the
+    neighbouring code; everything else is exact:
+    - key scales within 4 ulp, key codes equal except for at most 1 in 1000,
+      each of those one step from the oracle's (or a zero of the other sign);
+    - value codes and scales bit-exact (values are not rotated);
+    - the rotated queries within the attention tolerance, as the bf16 rotary
+      append is checked; every slot the append does not own unchanged."""
+    x = synth.make_inputs(cfg, B=SMALL_B[cfg])
+    c = x.cfg
+    bs, T = c.block_size, c.Kq
+    kc, vc, ks, vs = fp8_pool(x, include_new=False)
+    pos = (x.len_before[:, None] + offset + np.arange(T)[None, :]).astype(np.int32)
+    q = to_torch(x.q, bf16=True)
+    dk, dv, dks, dvs = dev(kc), dev(vc), dev(ks), dev(vs)
+    clm_gpu.rope_kv_cache_append_fp8(q, to_torch(x.k_new, bf16=True), to_torch(x.v_new, bf16=True), dk, dv, dks,
+                                     dvs, dev(x.block_table), dev(x.len_before), dev(pos), 1.0e6, block_size=bs)
+    f32 = synth.bf16_bits_to_f32
+    q_ref = oracle.rope(f32(x.q), pos[:, :, None], 1.0e6)
+    k_rot = oracle.rope(f32(x.k_new), pos[:, :, None], 1.0e6).astype(np.float32)
+    rk, rv, rks, rvs = fp8.fp8_kv_cache_append(kc, vc, ks, vs, x.block_table, x.len_before, k_rot,
+                                               f32(x.v_new), bs)
+    check_close(bf16_tensor_to_f32(q), q_ref, f"fp8 rope q c{cfg}")
+    np.testing.assert_array_equal(dv.cpu().numpy(), rv, err_msg="value codes")
+    np.testing.assert_array_equal(dvs.cpu().numpy().view(np.uint32), rvs.view(np.uint32), err_msg="value scales")
+    gk, gks = dk.cpu().numpy(), dks.cpu().numpy()
+    # scales: every slot; untouched ones are bit-equal, new ones within 4 ulp
+    np.testing.assert_allclose(gks, rks, rtol=4 * 2.0 ** -23, atol=0)
+    diff = gk != rk
+    n_touched = c.B * T * c.H_kv * c.D
+    assert diff.sum() <= max(1, n_touched // 1000), f"{diff.sum()} key codes differ of {n_touched}"
+    g_mag, r_mag = gk[diff] & 0x7F, rk[diff] & 0x7F
+    same_sign = (gk[diff] & 0x80) == (rk[diff] & 0x80)
+    ok = (same_sign & (np.abs(g_mag.astype(int) - r_mag.astype(int)) == 1)) | ((g_mag == 0) & (r_mag == 0))
+    assert ok.all(), list(zip(gk[diff][~ok][:8], rk[diff][~ok][:8]))
+    # every differing code belongs to a slot this append wrote
+    touched = np.zeros(gk.shape[:2] + gk.shape[3:4], bool)      # [nb, H, bs]
+    for b in range(c.B):
+        for t in range(T):
+            p_ = int(x.len_before[b]) + t
+            touched[int(x.block_table[b, p_ // bs]), :, p_ % bs] = True
+    assert not (diff.any(axis=(2, 4)) & ~touched).any(), "a slot the append does not own changed"
+    print(f"fp8 rope append c{cfg}: {int(diff.sum())} of {n_touched} key codes one step from the oracle's")

@@ -303,7 +303,7 @@ def _fp8_stream_rows(kc, vc, ks, vs, bt, b, n, bs):
     return fp8.dequantize_rows(kcodes, ksc), fp8.dequantize_rows(vcodes, vsc)
 
 
-def _fp8_loop_case(clm_gpu, cfg, B_live, n_steps):
+def _fp8_loop_case(clm_gpu, cfg, B_live, n_steps, rope=False):
     """The loop over an FP8 (E4M3) cache: every step's quantizing append
     against the oracle's quantizer (the whole cache bit for bit at the end),
     attention, logits and tokens against the oracle on the dequantized rows,
@@ -339,8 +339,11 @@ def _fp8_loop_case(clm_gpu, cfg, B_live, n_steps):
     need_ws = clm_gpu.decode_attention_workspace_size(c.B, Kq, Hq, Hk, D, max_kv)
     ws = torch.empty(need_ws + 256, dtype=torch.uint8, device=dev)
     ws = ws[(-ws.data_ptr()) % 256:]
+    offset = 1000
+    if rope:
+        g["positions"] = T((lb0[:, None] + offset + np.arange(Kq)[None, :]).astype(np.int32))
     loop = clm_gpu.DecodeLoop(max_kv_len=max_kv, mode=c.mode, spec_temperature=c.temperature, attn_workspace=ws,
-                              block_size=bs, **g)
+                              block_size=bs, rope_base=1.0e6, **g)
     loop.launch()
     torch.cuda.synchronize()
 
@@ -350,11 +353,16 @@ def _fp8_loop_case(clm_gpu, cfg, B_live, n_steps):
     Wf = f32(x.W)
     for s in range(n_steps):
         kn, vn, qs = steps[s]
-        kc, vc, ks, vs = fp8.fp8_kv_cache_append(kc, vc, ks, vs, bt, lb.astype(np.int32), f32(kn), f32(vn), bs)
+        kf, qf = f32(kn), f32(qs)
+        if rope:            # keys quantized from their fp32 rotation; the rotated queries are stored as bf16
+            pos = lb[:, None] + offset + np.arange(Kq)[None, :]
+            kf = oracle.rope(kf, pos[:, :, None], 1.0e6).astype(np.float32)
+            qf = oracle.round_to_bf16(oracle.rope(qf, pos[:, :, None], 1.0e6)).astype(np.float32)
+        kc, vc, ks, vs = fp8.fp8_kv_cache_append(kc, vc, ks, vs, bt, lb.astype(np.int32), kf, f32(vn), bs)
         kv_len = (lb + Kq).astype(np.int32)
         rows_kv = [_fp8_stream_rows(kc, vc, ks, vs, bt, b, int(kv_len[b]), bs) for b in range(c.B)]
         sp = spec_np[s] if spec_np else None
-        ref = oracle.decode_step(f32(qs), [r[0] for r in rows_kv], [r[1] for r in rows_kv], kv_len, scale, Hk, Wf,
+        ref = oracle.decode_step(qf, [r[0] for r in rows_kv], [r[1] for r in rows_kv], kv_len, scale, Hk, Wf,
                                  None, True, mode=c.mode,
                                  temperature=c.temperature if c.mode == "spec" else None, spec=sp)
         sel = np.nonzero(live)[0]
@@ -375,7 +383,10 @@ def _fp8_loop_case(clm_gpu, cfg, B_live, n_steps):
             add = np.full(c.B, Kq, np.int64)
         lb = lb + add
     assert np.array_equal(g["len_before"].cpu().numpy()[live], lb[live]), "lengths after the loop"
-    if live.all():
+    if rope:
+        assert np.array_equal(g["positions"].cpu().numpy()[live],
+                              (lb[:, None] + offset + np.arange(Kq)[None, :])[live])
+    elif live.all():        # with rotary the keys' codes may sit one step apart at rounding boundaries
         blocks = np.unique(bt)
         np.testing.assert_array_equal(g["k_cache"].cpu().numpy()[blocks], kc[blocks], err_msg="fp8 key codes")
         np.testing.assert_array_equal(g["v_cache"].cpu().numpy()[blocks], vc[blocks], err_msg="fp8 value codes")
@@ -392,3 +403,11 @@ def test_loop_fp8_cache(clm_gpu):
     verification, 3 steps (12 rows)."""
     _fp8_loop_case(clm_gpu, 5, 24, 3)
     _fp8_loop_case(clm_gpu, 4, 32, 3)
+
+
+def test_loop_fp8_cache_rope(clm_gpu):
+    """FP8 cache with rotary positions in the loop (the rotary FP8 append):
+    24 streams of the 256-stream mix, greedy, and the 6-query blocks with
+    verification, 3 steps each; positions advance with the lengths."""
+    _fp8_loop_case(clm_gpu, 5, 24, 3, rope=True)
+    _fp8_loop_case(clm_gpu, 4, 32, 3, rope=True)
