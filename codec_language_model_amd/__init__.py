@@ -15,6 +15,7 @@ Calls (names follow the C ABI):
 from __future__ import annotations
 
 import ctypes as C
+import functools
 import math
 
 from . import _lib
@@ -98,11 +99,20 @@ def _rows(call, B, **arrays):
 
 
 def _ptr(t):
-    return C.c_void_p(0 if t is None else t.data_ptr())
+    # ctypes turns None into NULL and an int into the pointer (argtypes c_void_p)
+    return None if t is None else t.data_ptr()
 
 
 def _stream():
-    return C.c_void_p(_torch().cuda.current_stream().cuda_stream)
+    """The raw HIP stream of torch's current stream on the current device.
+    torch's own accessor of the raw handle costs ~0.1 us against ~3 us for
+    building a Stream object, which matters at small batch where a step is
+    bounded by host time; the public API is the fallback."""
+    torch = _torch()
+    try:
+        return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
+    except AttributeError:
+        return torch.cuda.current_stream().cuda_stream
 
 
 class Workspace:
@@ -235,6 +245,7 @@ def rope_kv_cache_append_fp8(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale
         H_q, H, D, block_size, nb, _stream()))
 
 
+@functools.lru_cache(maxsize=256)
 def decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len) -> int:
     return int(load().clm_decode_attention_workspace_size(B, Kq, H_q, H_kv, D, max_kv_len))
 
@@ -339,10 +350,12 @@ def decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, kv_
     return out
 
 
+@functools.lru_cache(maxsize=256)
 def codebook_head_workspace_size(M, d, V, G, bf16=True) -> int:
     return int(load().clm_codebook_head_workspace_size(M, d, V, G, CLM_BF16 if bf16 else CLM_F32))
 
 
+@functools.lru_cache(maxsize=256)
 def codebook_head_mlp_workspace_size(M, d, F, V, G) -> int:
     return int(load().clm_codebook_head_mlp_workspace_size(M, d, F, V, G))
 
