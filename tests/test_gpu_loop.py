@@ -229,6 +229,14 @@ def test_loop_greedy_rope_replay(clm_gpu):
     _loop_case(clm_gpu, 5, 24, 24, 4, rope=True, replay=True)
 
 
+def test_loop_full_size_256_streams(clm_gpu):
+    """The graph loop at the size the benchmark times it: all 256 streams of
+    the log-uniform 64..8192 mix, 2 steps (1024-token splits, merge pass),
+    every stream's attention, logits and token against the oracle, and the
+    whole cache bit for bit at the end."""
+    _loop_case(clm_gpu, 5, 256, 256, 2)
+
+
 def test_loop_speculative(clm_gpu):
     """32 streams x 6-query blocks, 4 steps; lengths advance by the tokens kept."""
     _loop_case(clm_gpu, 4, 32, 32, 4)
