@@ -64,8 +64,9 @@ def parse():
                     help="skip timing the CPU oracle (cpu_baseline is then null)")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="time only the chosen workload (by default the 256-stream step is followed by "
-                         "short eager runs of the four smaller workloads, reported under other_workloads; "
-                         "profiler runs of one workload pass this flag)")
+                         "short eager runs of the four smaller workloads, reported under other_workloads, "
+                         "and by the one- and 16-stream steps as graph loops, under graph_loop; profiler "
+                         "runs of one workload pass this flag)")
     ap.add_argument("--cpu-streams", type=int, default=0,
                     help="streams in the oracle's timed sample (0 = the whole batch)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -795,6 +796,17 @@ def main():
             keep["attention_hbm_frac"] = o["roofline"]["frac"]
             others[o["config"]["workload"]] = keep
         out["other_workloads"] = others
+        # the launch-bound steps (one and 16 streams) again as the native decode
+        # loop: 16 steps per HIP graph, lengths advancing on the device
+        loops = {}
+        for w in ("c1", "c2"):
+            a = copy.copy(args)
+            a.workload, a.no_cpu_baseline, a.copy_check, a.graph = w, True, False, "on"
+            a.steps, a.warmup = 48, 16
+            torch.cuda.empty_cache()
+            o = run_one(a)
+            loops[o["config"]["workload"]] = {k: o[k] for k in ("value", "unit", "ms_per_step", "steps")}
+        out["graph_loop"] = loops
     print(json.dumps(out), flush=True)
 
 
