@@ -300,8 +300,8 @@ def test_fp8_append_special_rows(clm_gpu):
         np.testing.assert_array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32), err_msg=name)
 
 
-@pytest.mark.parametrize("cfg,offset", [(4, 1000), (5, 123456)])
-def test_fp8_rope_append(clm_gpu, cfg, offset):
+@pytest.mark.parametrize("cfg,offset,bs,D", [(4, 1000, 16, 128), (5, 123456, 16, 128), (4, 77, 32, 64)])
+def test_fp8_rope_append(clm_gpu, cfg, offset, bs, D):
     """The rotary append into the FP8 cache at logical positions len_before +
     offset + t: the oracle rotates the new keys (fp64), then quantizes them
     from float32 with its quantizer.  The kernel rotates in fp32, so a key
@@ -311,10 +311,13 @@ def test_fp8_rope_append(clm_gpu, cfg, offset):
       each of those one step from the oracle's (or a zero of the other sign);
     - value codes and scales bit-exact (values are not rotated);
     - the rotated queries within the attention tolerance, as the bf16 rotary
-      append is checked; every slot the append does not own unchanged."""
-    x = synth.make_inputs(cfg, B=SMALL_B[cfg])
+      append is checked; every slot the append does not own unchanged.
+    Head width 64 (32-slot pages) takes the kernel's other pairing: the two
+    members of a rotation pair sit in lanes i and i + 32."""
+    import dataclasses
+    x = synth.make_inputs(dataclasses.replace(synth.get_config(cfg), block_size=bs, D=D), B=SMALL_B[cfg])
     c = x.cfg
-    bs, T = c.block_size, c.Kq
+    T = c.Kq
     kc, vc, ks, vs = fp8_pool(x, include_new=False)
     pos = (x.len_before[:, None] + offset + np.arange(T)[None, :]).astype(np.int32)
     q = to_torch(x.q, bf16=True)
