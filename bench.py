@@ -320,12 +320,13 @@ def host_info():
     return info
 
 
-def cpu_baseline(x, n_streams, min_seconds, threads=None):
+def cpu_baseline(x, n_streams, min_seconds, threads=None, keep_ref=False):
     """The oracle, as it stands, on n_streams streams spread over the length
     distribution (all of them when n_streams is 0 or >= B): attention, head
     and token choice per stream, repeated until min_seconds have passed.
     threads: BLAS/OpenMP thread limit for the run (None: the library default,
-    all cores)."""
+    all cores).  keep_ref: also return the last repetition's outputs and the
+    streams they cover, under "_ref"."""
     import contextlib
 
     import numpy as np
@@ -351,8 +352,8 @@ def cpu_baseline(x, n_streams, min_seconds, threads=None):
         t0 = time.perf_counter()
         reps = 0
         while reps == 0 or time.perf_counter() - t0 < min_seconds:
-            oracle.decode_step(q, keys, vals, x.kv_len, scale, c.H_kv, W, x.head_id if c.G > 1 else None,
-                               c.dtype == "bf16", streams=streams)
+            ref = oracle.decode_step(q, keys, vals, x.kv_len, scale, c.H_kv, W, x.head_id if c.G > 1 else None,
+                                     c.dtype == "bf16", streams=streams)
             reps += 1
         dt = time.perf_counter() - t0
         used = os.cpu_count()
@@ -363,9 +364,44 @@ def cpu_baseline(x, n_streams, min_seconds, threads=None):
     rows = len(streams) * c.Kq * reps
     what = "the whole batch" if len(streams) == c.B else \
         f"{len(streams)} of {c.B} streams (spread over the KV-length order)"
-    return {"value": round(rows / dt, 3), "unit": "stream-steps/s", "cores": used, "kind": "oracle",
-            "sample": f"{what}, {int(sum(x.kv_len[b] for b in streams))} cached tokens, full head, "
-                      f"{reps} repetitions: {dt:.1f} s"}
+    out = {"value": round(rows / dt, 3), "unit": "stream-steps/s", "cores": used, "kind": "oracle",
+           "sample": f"{what}, {int(sum(x.kv_len[b] for b in streams))} cached tokens, full head, "
+                     f"{reps} repetitions: {dt:.1f} s"}
+    if keep_ref:
+        out["_ref"] = (streams, ref)
+    return out
+
+
+def parity_of_step(c, streams, ref, o, logits, tokens):
+    """The timed step's own outputs against the oracle's for the same inputs
+    (the CPU baseline's last repetition): attention outputs and logits by the
+    |gpu - oracle| <= 2e-2 + 2e-2 |oracle| bar, greedy tokens equal except
+    where the oracle's top-2 logit gap is under 1e-3 (then the GPU's token
+    must be within 1e-3 of the oracle's max)."""
+    import numpy as np
+    rows = np.array([b * c.Kq + j for b in streams for j in range(c.Kq)])
+    o_g = o.float().cpu().numpy()[streams].astype(np.float64)
+    l_g = logits.cpu().numpy()[rows].astype(np.float64)
+    t_g = tokens.cpu().numpy()[rows]
+    o_r = np.asarray(ref["o"])[streams]
+    l_r = np.asarray(ref["logits"], np.float64)[rows]
+
+    def bar(g, r):
+        err = np.abs(g - r)
+        return float(err.max()), float((err / (2e-2 + 2e-2 * np.abs(r))).max())
+    eo, so = bar(o_g, o_r)
+    el, sl = bar(l_g, l_r)
+    top2 = np.sort(l_r, axis=1)[:, -2:]
+    gap = top2[:, 1] - top2[:, 0]
+    want = np.argmax(l_r, axis=1)
+    equal = t_g == want
+    near = l_r[np.arange(len(rows)), t_g] >= top2[:, 1] - 1e-3
+    exempt = (~equal) & (gap < 1e-3) & near
+    return {"streams": len(streams), "rows": int(len(rows)),
+            "attention_max_abs_err": round(eo, 6), "attention_bar_share": round(so, 4),
+            "logits_max_abs_err": round(el, 6), "logits_bar_share": round(sl, 4),
+            "tokens_equal": int(equal.sum()), "tokens_exempt": int(exempt.sum()),
+            "pass": bool(so <= 1.0 and sl <= 1.0 and (equal | exempt).all())}
 
 
 def cpu_baseline_table(reps=3):
@@ -693,14 +729,21 @@ def main():
             del src, dst
 
         cpu = None
+        parity = None
         if not args.no_cpu_baseline:
             log("[bench] timing the CPU oracle on all cores, then on one ...")
-            cpu = cpu_baseline(x, args.cpu_streams, args.cpu_seconds)
+            cpu = cpu_baseline(x, args.cpu_streams, args.cpu_seconds, keep_ref=True)
+            streams_ref, ref = cpu.pop("_ref")
             one = cpu_baseline(x, args.cpu_streams, args.cpu_seconds, threads=1)
             cpu["single_core"] = {"value": one["value"], "cores": one["cores"], "sample": one["sample"]}
             cpu["host"] = host_info()
             log(f"[bench] cpu oracle: {cpu['value']:.2f} {cpu['unit']} on {cpu['cores']} threads, "
                 f"{one['value']:.2f} on {one['cores']} ({cpu['host']})")
+            # the timed step's outputs against the oracle's on the same inputs (the
+            # plain greedy step only: the other modes change what the step computes)
+            if f8 is None and rope_pos is None and mlp is None and not graph and c.mode == "greedy":
+                parity = parity_of_step(c, streams_ref, ref, o, reps[0][2], tokens)
+                log(f"[bench] parity against the oracle: {parity}")
 
         head_flops = 2.0 * c.M * c.d_model * c.V if mlp is None else 2.0 * c.M * mlp[3] * (c.d_model + c.V)
         head_roof = None
@@ -763,6 +806,7 @@ def main():
             "hbm_copy": None if copy is None else {"copy_GBs": round(copy, 1),
                                                    "attention_frac_of_copy": round(achieved / copy, 4)},
             "cpu_baseline": cpu,
+            "parity": parity,
         }
         if bf:
             out["codebook_head_mfma_frac"] = round(head_flops / (per_us[2] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
